@@ -1,0 +1,328 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+Each test ties an oracle function to something other than itself: values
+derived by hand (tests/golden/), closed forms stated on the pages, brute force
+over all subsets on tiny inputs, invariants, and special cases that reduce to
+library routines (torch softmax / SiLU, NumPy sorting).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+LN = {"ln3": math.log(3.0), "ln2": math.log(2.0)}
+
+
+def _ev(expr):
+    """Evaluate a hand-derived fixture expression (numbers, + - * / ( ), ln2, ln3)."""
+    if isinstance(expr, (int, float)):
+        return float(expr)
+    allowed = set("0123456789.+-*/() ")
+    names = expr
+    for k in LN:
+        names = names.replace(k, "")
+    assert set(names) <= allowed, expr
+    return float(eval(expr, {"__builtins__": {}}, LN))  # noqa: S307 - restricted alphabet
+
+
+def _arr(nested):
+    return np.vectorize(_ev, otypes=[np.float64])(np.array(nested, dtype=object))
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand_layer(rng, T, D, E, K, F, Fs, gated=True):
+    x = rng.standard_normal((T, D))
+    r = rng.standard_normal((T, D))
+    wr = rng.standard_normal((E, D)) / math.sqrt(D)
+    banks = O.Banks(rng.standard_normal((E, F, D)) / math.sqrt(D),
+                    rng.standard_normal((E, F, D)) / math.sqrt(D),
+                    rng.standard_normal((E, D, F)) / math.sqrt(F),
+                    rng.standard_normal((Fs, D)) / math.sqrt(D) if Fs else None,
+                    rng.standard_normal((Fs, D)) / math.sqrt(D) if Fs else None,
+                    rng.standard_normal((D, Fs)) / math.sqrt(Fs) if Fs else None,
+                    rng.standard_normal(D) / math.sqrt(D) if (Fs and gated) else None)
+    return x, r, wr, banks
+
+
+# ------------------------------------------------------------- golden fixtures
+def test_golden_softmax_layer_by_hand():
+    g = _load("softmax_layer_hand.json")
+    x, r = _arr(g["x"]), _arr(g["residual"])
+    banks = O.Banks(_arr(g["gate"]), _arr(g["up"]), _arr(g["down"]), _arr(g["shared_gate"]),
+                    _arr(g["shared_up"]), _arr(g["shared_down"]), _arr(g["shared_gate_vec"]))
+    res = O.layer_forward(x, r, _arr(g["router"]), banks, "softmax", g["shape"]["K"])
+    np.testing.assert_array_equal(res.route.ids, np.array(g["expected_ids"]))
+    np.testing.assert_allclose(res.route.weights, _arr(g["expected_weights"]), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(res.out, _arr(g["expected_out"]), rtol=0, atol=1e-12)
+    # the per-token loop formulation reproduces the same hand values
+    loop = O.layer_forward_loop(x, r, _arr(g["router"]), banks, "softmax", g["shape"]["K"])
+    np.testing.assert_allclose(loop, _arr(g["expected_out"]), rtol=0, atol=1e-12)
+
+
+def test_golden_sigmoid_group_by_hand():
+    g = _load("sigmoid_group_hand.json")
+    sh = g["shape"]
+    z = O.router_logits(_arr(g["x"]), _arr(g["router"]))
+    rt = O.sigmoid_group_topk(z, _arr(g["expert_bias"]), sh["K"], sh["n_group"], sh["topk_group"],
+                              sh["routed_scaling"])
+    np.testing.assert_array_equal(rt.ids, np.array(g["expected_ids"]))
+    np.testing.assert_allclose(rt.weights, _arr(g["expected_weights"]), rtol=0, atol=1e-14)
+    # negative control: ranking groups by their single best score picks another group
+    sel = O.sigmoid(z) + _arr(g["expert_bias"])[None]
+    top1 = sel.reshape(2, sh["n_group"], -1).max(axis=-1)
+    kept = int(np.argmax(top1[0]))
+    members = np.arange(kept * 2, kept * 2 + 2)
+    alt = members[np.argsort(-sel[0, members], kind="stable")][: sh["K"]]
+    assert list(alt) == g["top1_group_rule_ids_token0"] != list(rt.ids[0])
+
+
+def test_golden_u4_dequant_by_hand():
+    g = _load("u4_affine_g64_hand.json")
+    codes = np.array([g["codes_row0_bytes"][0]] * 32 + [g["codes_row0_bytes"][1]] * 32, dtype=np.uint8)[None]
+    w = O.dequant_u4_g64(codes, np.array([g["scale_bits_row0"]], dtype=np.uint16),
+                         np.array([g["min_bits_row0"]], dtype=np.uint16))
+    assert w.shape == (1, 128)
+    np.testing.assert_array_equal(w[0, :64].reshape(32, 2), np.tile(g["expected_row0_group0_pair"], (32, 1)))
+    np.testing.assert_array_equal(w[0, 64:].reshape(32, 2), np.tile(g["expected_row0_group1_pair"], (32, 1)))
+
+
+def test_golden_permute_by_hand():
+    g = _load("permute_hand.json")
+    p = O.permute(np.array(g["ids"]), g["n_experts"])
+    np.testing.assert_array_equal(p.offsets, g["expected_offsets"])
+    np.testing.assert_array_equal(p.active, g["expected_active"])
+    assert p.n_active == len(g["expected_active"])
+    np.testing.assert_array_equal(p.sorted_pairs, g["expected_sorted_pairs"])
+
+
+def test_bf16_widening_exact():
+    # bit patterns with known values: 1.0, -2.0, 0.5, smallest subnormal, max finite
+    bits = np.array([0x3F80, 0xC000, 0x3F00, 0x0001, 0x7F7F], dtype=np.uint16)
+    v = O.bf16_bits_to_f64(bits)
+    assert v[0] == 1.0 and v[1] == -2.0 and v[2] == 0.5
+    assert v[3] == 2.0 ** -133
+    assert v[4] == (2 - 2 ** -7) * 2.0 ** 127
+    t = torch.tensor([1.0, -2.0, 0.5, 3.140625], dtype=torch.bfloat16)
+    np.testing.assert_array_equal(O.bf16_bits_to_f64(t.view(torch.int16).numpy()), t.double().numpy())
+
+
+# ------------------------------------------------------------- routing invariants
+@pytest.mark.parametrize("E,K", [(16, 4), (256, 8), (256, 4), (8, 8)])
+def test_renorm_sums_to_one_and_selected_softmax_form(E, K):
+    rng = np.random.default_rng(E * 10 + K)
+    z = rng.standard_normal((64, E)) * 2.0
+    rt = O.softmax_topk(z, K)
+    np.testing.assert_allclose(rt.weights.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    # the global denominator cancels: alpha = exp(z_i) / sum_{j in I} exp(z_j)
+    zs = np.take_along_axis(z, rt.ids.astype(np.int64), axis=1)
+    closed = np.exp(zs) / np.exp(zs).sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(rt.weights, closed, rtol=1e-12, atol=0)
+    # the 2^-14 clamp never binds for softmax: the top-K mass is >= K/E
+    assert (np.sort(rt.score, axis=1)[:, ::-1][:, :K].sum(axis=1) >= K / E - 1e-15).all()
+
+
+def test_softmax_matches_library_routine():
+    rng = np.random.default_rng(7)
+    z = rng.standard_normal((32, 256)) * 3
+    np.testing.assert_allclose(O.softmax(z), torch.softmax(torch.from_numpy(z), dim=1).numpy(), rtol=1e-13, atol=0)
+
+
+def _is_topk(score, S, K):
+    """Defining property of the top-K set with ties to the lower index."""
+    rest = [j for j in range(score.size) if j not in S]
+    return len(S) == K and all((score[i] > score[j]) or (score[i] == score[j] and i < j)
+                               for i in S for j in rest)
+
+
+@pytest.mark.parametrize("tied", [False, True])
+def test_topk_brute_force_tiny(tied):
+    rng = np.random.default_rng(11 + tied)
+    E, K = 16, 4
+    for trial in range(40):
+        z = rng.integers(-2, 3, E).astype(np.float64) if tied else rng.standard_normal(E)
+        rt = O.softmax_topk(z[None], K)
+        winners = [S for S in itertools.combinations(range(E), K) if _is_topk(rt.score[0], S, K)]
+        assert len(winners) == 1
+        assert sorted(rt.ids[0].tolist()) == list(winners[0])
+        # slot order: descending score, ties -> lower index
+        ids = rt.ids[0]
+        for a, b in zip(ids[:-1], ids[1:]):
+            assert rt.score[0, a] > rt.score[0, b] or (rt.score[0, a] == rt.score[0, b] and a < b)
+        # ranking by probability equals ranking by logit
+        assert list(ids) == list(np.lexsort((np.arange(E), -z))[:K])
+
+
+def test_all_tie_softmax():
+    rt = O.softmax_topk(np.zeros((3, 256)), 8)
+    np.testing.assert_array_equal(rt.ids, np.tile(np.arange(8), (3, 1)))
+    np.testing.assert_array_equal(rt.weights, np.full((3, 8), 1 / 8))
+    assert rt.flags.all()
+
+
+def _brute_group(z, b, K, G, tg, scale):
+    E = z.size
+    gs = E // G
+    s = 1 / (1 + np.exp(-z))
+    sel = s + b
+    # "sum of the two best" by brute force over all pairs of distinct members
+    gscore = np.array([max(sel[i] + sel[j] for i, j in itertools.combinations(range(g * gs, (g + 1) * gs), 2))
+                       for g in range(G)])
+    kept = [Gs for Gs in itertools.combinations(range(G), tg) if _is_topk(gscore, Gs, tg)]
+    assert len(kept) == 1
+    cand = [e for g in kept[0] for e in range(g * gs, (g + 1) * gs)]
+    masked = np.where(np.isin(np.arange(E), cand), sel, -np.inf)
+    S = [S for S in itertools.combinations(cand, K) if _is_topk(masked, S, K)]
+    assert len(S) == 1
+    w = scale * s[list(S[0])] / max(s[list(S[0])].sum(), 2.0 ** -14)
+    return set(S[0]), dict(zip(S[0], w))
+
+
+@pytest.mark.parametrize("E,G,tg,K", [(16, 4, 2, 4), (16, 8, 3, 3), (12, 3, 1, 2), (16, 4, 4, 5)])
+def test_group_topk_brute_force(E, G, tg, K):
+    rng = np.random.default_rng(E + G + tg + K)
+    for trial in range(25):
+        z = rng.standard_normal(E) if trial % 3 else rng.integers(-1, 2, E).astype(float)
+        b = rng.standard_normal(E) * 0.3 if trial % 2 else np.zeros(E)
+        rt = O.sigmoid_group_topk(z[None], b, K, G, tg, 2.5)
+        S, w = _brute_group(z, b, K, G, tg, 2.5)
+        assert set(rt.ids[0].tolist()) == S
+        for slot, e in enumerate(rt.ids[0]):
+            assert abs(rt.weights[0, slot] - w[int(e)]) < 1e-13
+        np.testing.assert_allclose(rt.weights.sum(), 2.5, rtol=1e-13)
+
+
+def test_group_rule_degenerates_to_plain_topk():
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal((50, 128))
+    b = rng.standard_normal(128) * 0.3
+    sel = 1 / (1 + np.exp(-z)) + b
+    plain = np.stack([np.lexsort((np.arange(128), -row))[:8] for row in sel])
+    for G, tg in [(8, 8), (1, 1)]:
+        rt = O.sigmoid_group_topk(z, b, 8, G, tg, 2.5)
+        np.testing.assert_array_equal(rt.ids, plain)
+
+
+def test_bias_selects_but_does_not_weight():
+    rng = np.random.default_rng(5)
+    z = rng.standard_normal((40, 128))
+    b = rng.standard_normal(128) * 0.3
+    base = O.sigmoid_group_topk(z, b, 8, 8, 4, 2.5)
+    shifted = O.sigmoid_group_topk(z, b + 0.75, 8, 8, 4, 2.5)
+    np.testing.assert_array_equal(base.ids, shifted.ids)
+    np.testing.assert_allclose(base.weights, shifted.weights, rtol=0, atol=0)
+    # a +10 bias forces expert 77 into every token; its weight uses the raw score only
+    b2 = b.copy()
+    b2[77] += 10
+    forced = O.sigmoid_group_topk(z, b2, 8, 8, 4, 2.5)
+    s = 1 / (1 + np.exp(-z))
+    for t in range(z.shape[0]):
+        ids = forced.ids[t]
+        assert ids[0] == 77
+        np.testing.assert_allclose(forced.weights[t], 2.5 * s[t, ids] / s[t, ids].sum(), rtol=1e-13)
+        # negative control: weighting by the biased score would differ
+        assert not np.allclose(forced.weights[t], 2.5 * (s[t, ids] + b2[ids]) / (s[t, ids] + b2[ids]).sum())
+
+
+def test_all_tie_sigmoid_group():
+    rt = O.sigmoid_group_topk(np.zeros((2, 128)), np.zeros(128), 8, 8, 4, 2.5)
+    np.testing.assert_array_equal(rt.ids, np.tile(np.arange(8), (2, 1)))
+    np.testing.assert_array_equal(rt.weights, np.full((2, 8), 2.5 / 8))
+
+
+def test_sigmoid_clamp_binds_only_when_scores_vanish():
+    z = np.full((1, 16), -30.0)
+    z[0, :4] += np.array([0.5, 0.25, 0.125, 0.0])
+    rt = O.sigmoid_group_topk(z, None, 4, 4, 2, 2.5)
+    s = 1 / (1 + np.exp(-z[0, rt.ids[0]]))
+    assert s.sum() < 2.0 ** -14
+    assert rt.weights.sum() < 2.5 * 1e-6  # the floor keeps the weights tiny instead of renormalising to 2.5
+    np.testing.assert_allclose(rt.weights[0] / rt.weights[0].sum(), s / s.sum(), rtol=1e-12)
+
+
+# ------------------------------------------------------------- permute
+def test_permute_brute_force():
+    rng = np.random.default_rng(9)
+    for T, E, K in [(1, 8, 2), (7, 16, 4), (33, 64, 8), (100, 5, 5)]:
+        ids = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+        p = O.permute(ids, E)
+        buckets = {e: [] for e in range(E)}
+        for t in range(T):
+            for k in range(K):
+                buckets[int(ids[t, k])].append(t * K + k)
+        flat = [q for e in range(E) for q in buckets[e]]
+        assert p.sorted_pairs.tolist() == flat
+        assert p.offsets[-1] == T * K and sorted(flat) == list(range(T * K))
+        assert p.offsets.tolist() == [0] + list(np.cumsum([len(buckets[e]) for e in range(E)]))
+        assert p.active.tolist() == [e for e in range(E) if buckets[e]]
+
+
+# ------------------------------------------------------------- textbook reductions
+def _torch_swiglu(x, wg, wu, wd):
+    xt = torch.from_numpy(x)
+    h = torch.nn.functional.silu(xt @ torch.from_numpy(wg).T) * (xt @ torch.from_numpy(wu).T)
+    return (h @ torch.from_numpy(wd).T).numpy()
+
+
+def test_single_expert_is_plain_swiglu_ffn():
+    rng = np.random.default_rng(21)
+    x, r, wr, banks = _rand_layer(rng, 6, 32, 1, 1, 16, 0)
+    res = O.layer_forward(x, r, wr, banks, "softmax", 1)
+    np.testing.assert_array_equal(res.route.weights, np.ones((6, 1)))
+    ffn = _torch_swiglu(x, banks.gate[0], banks.up[0], banks.down[0])
+    np.testing.assert_allclose(res.out, r + ffn, rtol=1e-12, atol=1e-12)
+
+
+def test_k_equals_e_is_dense_softmax_mixture():
+    rng = np.random.default_rng(22)
+    T, D, E, F = 5, 24, 6, 8
+    x, r, wr, banks = _rand_layer(rng, T, D, E, E, F, 0)
+    res = O.layer_forward(x, r, wr, banks, "softmax", E)
+    p = torch.softmax(torch.from_numpy(x @ wr.T), dim=1).numpy()
+    dense = sum(p[:, e:e + 1] * _torch_swiglu(x, banks.gate[e], banks.up[e], banks.down[e]) for e in range(E))
+    np.testing.assert_allclose(res.y_moe, dense, rtol=1e-11, atol=1e-12)
+
+
+def test_zero_gate_vector_halves_shared_expert():
+    rng = np.random.default_rng(23)
+    x, r, wr, banks = _rand_layer(rng, 4, 16, 4, 2, 8, 8)
+    banks.shared_gate_vec = np.zeros(16)
+    ys = O.shared_expert(x, banks)
+    np.testing.assert_allclose(ys, 0.5 * _torch_swiglu(x, banks.shared_gate, banks.shared_up, banks.shared_down),
+                               rtol=1e-13, atol=1e-16)
+    # sigmoid(0) = 1/2 exactly: the gated output is exactly half the ungated one
+    banks.shared_gate_vec = None
+    np.testing.assert_array_equal(ys, 0.5 * O.shared_expert(x, banks))
+
+
+def test_grouped_and_loop_formulations_agree():
+    rng = np.random.default_rng(24)
+    x, r, wr, banks = _rand_layer(rng, 9, 64, 16, 4, 32, 32)
+    for fam, kw in [("softmax", {}), ("sigmoid_group",
+                                       dict(bias=rng.standard_normal(16) * 0.3, n_group=4, topk_group=2,
+                                            routed_scaling=2.5))]:
+        a = O.layer_forward(x, r, wr, banks, fam, 4, **kw).out
+        b = O.layer_forward_loop(x, r, wr, banks, fam, 4, **kw)
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_token_subset_and_given_ids_consistent():
+    rng = np.random.default_rng(25)
+    x, r, wr, banks = _rand_layer(rng, 12, 32, 8, 2, 16, 16)
+    full = O.layer_forward(x, r, wr, banks, "softmax", 2)
+    sub = np.array([3, 0, 11])
+    part = O.layer_forward(x, r, wr, banks, "softmax", 2, tokens=sub)
+    np.testing.assert_allclose(part.out, full.out[sub], rtol=0, atol=1e-14)
+    again = O.layer_forward(x, r, wr, banks, "softmax", 2, ids=full.route.ids)
+    np.testing.assert_allclose(again.out, full.out, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(O.softmax_weights_for(full.z, full.route.ids), full.route.weights, rtol=1e-15)
