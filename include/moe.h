@@ -1,0 +1,190 @@
+/*
+ * moe.h - C ABI of a gfx950 (MI355X) library computing the forward pass of
+ * one sparse mixture-of-experts layer.
+ *
+ * The operation (sources cited per entry point below):
+ *   Treebeard, "How Treebeard routes Qwen3.6 MoE tokens":
+ *     "Routing math"              z = W_router^T x, p = softmax(z), I = TopK(p, K),
+ *                                 alpha = p_I / max(sum p_I, 2^-14)
+ *     "Routed expert computation" e_i = W_down_i^T (SiLU(W_gate_i^T x) * W_up_i^T x),
+ *                                 y_routed = sum_i alpha_i e_i
+ *     "Shared expert computation" y_shared = sigmoid(w_shared^T x) * shared SwiGLU(x),
+ *                                 r_next = r + (y_routed + y_shared)
+ *     "Treebeard's execution optimization" / "Intel SYCL path": routing artefacts
+ *                                 are final before expert execution; pairs are
+ *                                 counted per expert, offset, listed and packed,
+ *                                 and results written back to their token and slot.
+ *   edge0, "MoE Routing and Experts":
+ *     "Routing families"          softmax top-k, and sigmoid group top-k with
+ *                                 expert_bias, n_group, topk_group, routed_scaling
+ *     tier table                  "4-bit affine, group 64" weights.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; matrices are
+ *     row-major with the input (reduction) dimension contiguous.  The library
+ *     never allocates device memory, never synchronises the host, never prints
+ *     and never aborts; it returns a moe_status.
+ *   - All argument checks run on the host before any launch.  A failed check
+ *     returns an error code and launches nothing.  n_tokens == 0 returns MOE_OK
+ *     with no launch.  After launching, a launch failure reported by the HIP
+ *     runtime returns MOE_ERR_HIP; moe_last_error() gives a message.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Scratch memory is the caller's `ws` of `ws_bytes` bytes (size it with
+ *     moe_workspace_size).  Calls that share a workspace must be ordered on
+ *     one stream.  The workspace needs no initialisation.
+ *   - Results are deterministic: the same inputs give bitwise-identical
+ *     outputs run to run (fixed reduction orders, no floating-point atomics).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* moe_stream_t; /* identical to hipStream_t */
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1,  /* null pointer, bad size or family parameter */
+    MOE_ERR_UNSUPPORTED = 2,       /* shape or dtype mix this library does not build */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOE_ERR_HIP = 4                /* the HIP runtime reported a failure */
+} moe_status;
+
+typedef enum {
+    MOE_F32 = 0,            /* float32 */
+    MOE_BF16 = 1,           /* bfloat16 */
+    MOE_U4_AFFINE_G64 = 2   /* 4-bit codes (two per byte, even element in the low
+                               nibble) + bf16 scale and bf16 min per 64 consecutive
+                               input elements: w = scale * q + min */
+} moe_dtype;
+
+typedef enum {
+    MOE_ROUTE_SOFTMAX_TOPK = 0,      /* edge0 "Softmax top-k"; Treebeard "Routing math" */
+    MOE_ROUTE_SIGMOID_GROUP_TOPK = 1 /* edge0 "Sigmoid group top-k" */
+} moe_route_family;
+
+/* Layer description.  Field names follow the GGUF keys quoted on the
+ * Treebeard page ("Source map"): d_model = embedding_length, n_experts =
+ * expert_count, top_k = expert_used_count, d_ff = expert_feed_forward_length,
+ * d_ff_shared = expert_shared_feed_forward_length. */
+typedef struct {
+    int32_t n_tokens;       /* T >= 0 */
+    int32_t d_model;        /* D */
+    int32_t n_experts;      /* E, multiple of 16, <= 1024 */
+    int32_t top_k;          /* K, 1 <= K <= min(E, 32) */
+    int32_t d_ff;           /* F, routed expert intermediate width */
+    int32_t d_ff_shared;    /* F_s, shared expert width; 0 = no shared expert */
+    moe_route_family family;
+    int32_t n_group;        /* sigmoid family: groups of E/n_group contiguous experts */
+    int32_t topk_group;     /* sigmoid family: groups kept per token */
+    float routed_scaling;   /* sigmoid family: factor on the renormalised weights */
+    moe_dtype act_dtype;    /* x: MOE_F32 or MOE_BF16 */
+    moe_dtype router_dtype; /* router and shared gate vector: same as act_dtype */
+    moe_dtype expert_dtype; /* routed and shared banks: MOE_F32 (with F32 activations),
+                               MOE_BF16 or MOE_U4_AFFINE_G64 (with BF16 activations) */
+} moe_config;
+
+/* One weight matrix or bank.  For MOE_F32/MOE_BF16 only `w` is used
+ * ([rows, in] per expert).  For MOE_U4_AFFINE_G64: w = codes uint8
+ * [rows, in/2], scale and min = bf16 [rows, in/64]. */
+typedef struct {
+    const void* w;
+    const void* scale;
+    const void* min;
+} moe_matrix;
+
+typedef struct {
+    const void* router;          /* [E, D] router_dtype (z = x W^T) */
+    const float* expert_bias;    /* [E] fp32, sigmoid family selection bias; NULL = zeros */
+    moe_matrix gate;             /* [E, F, D] */
+    moe_matrix up;               /* [E, F, D] */
+    moe_matrix down;             /* [E, D, F] */
+    moe_matrix shared_gate;      /* [F_s, D] (ignored when d_ff_shared == 0) */
+    moe_matrix shared_up;        /* [F_s, D] */
+    moe_matrix shared_down;      /* [D, F_s] */
+    const void* shared_gate_vec; /* [D] router_dtype; NULL => shared gate s_t = 1 */
+} moe_weights;
+
+/* Bytes of workspace every entry point below needs for `cfg` (the largest
+ * need of any of them; 256-byte aligned regions).  Returns MOE_OK or
+ * MOE_ERR_INVALID_ARGUMENT / MOE_ERR_UNSUPPORTED for a config no entry
+ * point accepts. */
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Routing (Treebeard "Routing math"; edge0 "Routing families").
+ * x [T, D] act_dtype; router [E, D] router_dtype; expert_bias [E] fp32 or NULL.
+ * Outputs topk_ids [T, K] int32 (slots in descending selection score, ties
+ * to the lower expert index) and topk_weights [T, K] fp32 (softmax family:
+ * renormalised probabilities with the 2^-14 floor; sigmoid family:
+ * routed_scaling * raw sigmoid scores renormalised with the same floor,
+ * bias excluded).  Logits are computed in fp32 from exact products. */
+moe_status moe_route(const moe_config* cfg, const void* x, const void* router,
+                     const float* expert_bias, int32_t* topk_ids, float* topk_weights,
+                     void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Permute (Treebeard "Intel SYCL path", steps 1-3): counts the T*K
+ * (token, slot) pairs per expert and writes
+ *   expert_offsets [E+1] int32   exclusive prefix sum of the counts,
+ *   active_experts [E] int32     experts with count > 0, ascending (first n_active used),
+ *   n_active       [1] int32,
+ *   sorted_pairs   [T*K] int32   flat pair ids t*K + k grouped by expert,
+ *                                ascending inside each expert (stable).
+ * Ids outside [0, E) are not counted and get no row. */
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids,
+                       int32_t* expert_offsets, int32_t* active_experts, int32_t* n_active,
+                       int32_t* sorted_pairs, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Routed experts (Treebeard "Routed expert computation"; edge0 "Experts"):
+ * for every pair p = t*K + k of expert e = topk_ids[t, k],
+ *   slot_out[p, :] = topk_weights[p] * W_down[e]^T (SiLU(W_gate[e]^T x_t) * W_up[e]^T x_t)
+ * slot_out [T, K, D] fp32.  Inputs are the permute outputs above (only the
+ * first n_active entries of active_experts are read) and the flat weights
+ * [T*K] fp32.  Only active experts' weights are read, each once per tile of
+ * up to 16 (small T) or 64 (large T) of its pairs.  The SwiGLU intermediate
+ * is rounded to bf16 for bf16/u4 weights and kept fp32 for fp32 weights. */
+moe_status moe_experts(const moe_config* cfg, const void* x, const moe_weights* weights,
+                       const int32_t* expert_offsets, const int32_t* active_experts,
+                       const int32_t* n_active, const int32_t* sorted_pairs,
+                       const float* topk_weights, float* slot_out,
+                       void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Shared expert (Treebeard "Shared expert computation"):
+ *   shared_out[t, :] = s_t * W_sd^T (SiLU(W_sg^T x_t) * W_su^T x_t),
+ *   s_t = sigmoid(shared_gate_vec . x_t), or 1 when shared_gate_vec is NULL.
+ * shared_out [T, D] fp32.  Requires d_ff_shared > 0. */
+moe_status moe_shared_expert(const moe_config* cfg, const void* x, const moe_weights* weights,
+                             float* shared_out, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Combine (Treebeard "Shared expert computation", last block):
+ *   out[t, :] = residual[t, :] + (sum_{k=0..K-1} slot_out[t, k, :] + shared_out[t, :])
+ * with the slots summed in ascending k in fp32.  shared_out may be NULL
+ * (treated as zeros); out may alias residual. */
+moe_status moe_combine(const moe_config* cfg, const float* slot_out, const float* shared_out,
+                       const float* residual, float* out, moe_stream_t stream);
+
+/* The whole layer: route -> permute -> experts, the shared expert on
+ * aux_stream when it is non-NULL (forked from and joined back into
+ * `stream` with library-owned events; otherwise on `stream`), then combine.
+ * residual [T, D] fp32; out [T, D] fp32 (may alias residual).  topk_ids_out
+ * [T, K] and topk_weights_out [T, K] receive the routing when non-NULL.
+ * Internally the routed slot rows are staged in bf16 for bf16/u4 weights. */
+moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, const void* x,
+                             const float* residual, float* out, int32_t* topk_ids_out,
+                             float* topk_weights_out, void* ws, size_t ws_bytes,
+                             moe_stream_t stream, moe_stream_t aux_stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status status);
+
+/* Message describing the last failure on the calling host thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

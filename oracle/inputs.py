@@ -38,14 +38,13 @@ def widen_matrix(m, index=None) -> np.ndarray:
 
 
 class _LazyBank:
+    """Widens one expert's matrix on demand (no cache: each expert is used once per call)."""
+
     def __init__(self, m):
         self.m = m
-        self.cache = {}
 
     def __call__(self, e):
-        if e not in self.cache:
-            self.cache[e] = widen_matrix(self.m, e)
-        return self.cache[e]
+        return widen_matrix(self.m, e)
 
 
 def banks_from(weights, lazy: bool = False) -> Banks:

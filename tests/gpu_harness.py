@@ -1,0 +1,155 @@
+"""Helpers for the GPU parity tests: run the HIP library through its C ABI
+and compare with the fp64 oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import dataclasses
+import itertools
+from typing import Optional
+
+import numpy as np
+import torch
+
+from oracle import moe_oracle as O
+from oracle.inputs import banks_from, widen_tensor
+from synth import WORKLOADS, LayerSpec, make_tokens, make_weights
+from top_routing_grouped_amd import moe
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "u4": 2e-2}  # normwise per-token relative error gate on y_moe
+WEIGHT_RTOL = 1e-5
+
+
+def spec_of(name: str, **kw) -> LayerSpec:
+    return dataclasses.replace(WORKLOADS[name], **kw)
+
+
+@dataclasses.dataclass
+class Case:
+    spec: LayerSpec
+    w: object  # synth LayerWeights on the GPU
+    x: torch.Tensor
+    r: torch.Tensor
+    # oracle-side fp64 views
+    x64: np.ndarray
+    r64: np.ndarray
+    wr64: np.ndarray
+    bias64: Optional[np.ndarray]
+    banks: O.Banks
+
+    def oracle_route(self, tokens=None):
+        xs = self.x64 if tokens is None else self.x64[tokens]
+        z = O.router_logits(xs, self.wr64)
+        s = self.spec
+        return z, O.route(z, s.family, s.top_k, self.bias64, s.n_group, s.topk_group, s.routed_scaling)
+
+    def oracle_layer(self, tokens=None, ids=None):
+        s = self.spec
+        return O.layer_forward(self.x64, self.r64, self.wr64, self.banks, s.family, s.top_k, self.bias64,
+                               s.n_group, s.topk_group, s.routed_scaling, tokens=tokens, ids=ids)
+
+
+_WEIGHT_CACHE = {}
+
+
+def make_case(spec: LayerSpec, device="cuda", token_seed=None, cache_key=None) -> Case:
+    key = cache_key or (spec.name, spec.d_model, spec.n_experts, spec.d_ff, spec.d_ff_shared, spec.expert_dtype,
+                        spec.top_k, spec.skew_var)
+    if key not in _WEIGHT_CACHE:
+        _WEIGHT_CACHE.clear()  # keep one layer's weights resident at a time
+        _WEIGHT_CACHE[key] = make_weights(spec, device)
+    w = _WEIGHT_CACHE[key]
+    x, r = make_tokens(spec, device, seed=token_seed)
+    lazy = spec.n_experts * spec.d_ff * spec.d_model > (1 << 24)
+    return Case(spec, w, x, r, widen_tensor(x), widen_tensor(r), widen_tensor(w.router),
+                None if w.expert_bias is None else widen_tensor(w.expert_bias), banks_from(w, lazy=lazy))
+
+
+def normwise_err(got: np.ndarray, ref: np.ndarray) -> float:
+    den = np.abs(ref).max(axis=1)
+    den = np.where(den > 0, den, 1.0)
+    return float((np.abs(got - ref).max(axis=1) / den).max())
+
+
+def run_route(case: Case):
+    s = case.spec
+    cfg = moe.config_from_spec(s)
+    ws = moe.alloc_workspace(cfg)
+    ids = torch.full((s.n_tokens, s.top_k), -7, dtype=torch.int32, device="cuda")
+    wts = torch.full((s.n_tokens, s.top_k), -7.0, dtype=torch.float32, device="cuda")
+    moe.route(cfg, case.x, case.w.router, case.w.expert_bias, ids, wts, ws)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), wts.cpu().numpy()
+
+
+def _valid_topk(score, chosen, k, cand=None, eps=O.TIE_EPS):
+    """chosen is a valid top-k of score (restricted to cand) up to eps."""
+    idx = np.arange(score.size) if cand is None else np.asarray(cand)
+    if not set(chosen) <= set(idx.tolist()) or len(set(chosen)) != k:
+        return False
+    srt = np.sort(score[idx])[::-1]
+    kth = srt[k - 1]
+    nxt = srt[k] if k < idx.size else -np.inf
+    rest = [e for e in idx if e not in set(chosen)]
+    return all(score[e] >= kth - eps for e in chosen) and all(score[e] <= nxt + eps for e in rest)
+
+
+def valid_selection(spec: LayerSpec, z_row: np.ndarray, bias, chosen) -> bool:
+    """Whether a selection is one of the near-tied valid answers for a flagged token."""
+    if spec.family == "softmax":
+        return _valid_topk(O.softmax(z_row[None])[0], list(chosen), spec.top_k)
+    E, G, TG = spec.n_experts, spec.n_group, spec.topk_group
+    gs = E // G
+    sel = O.sigmoid(z_row) + (0 if bias is None else bias)
+    gsc = O.group_scores(sel[None], G)[0]
+    for S in itertools.combinations(range(G), TG):
+        if not _valid_topk(gsc, list(S), TG):
+            continue
+        cand = [e for g in S for e in range(g * gs, (g + 1) * gs)]
+        if _valid_topk(sel, list(chosen), spec.top_k, cand):
+            return True
+    return False
+
+
+def check_route(case: Case, ids, wts, z, rt):
+    """ids bit-exact on unflagged tokens; flagged tokens must be a valid
+    near-tie answer; weights within 1e-5 relative on unflagged tokens."""
+    ok = ~rt.flags
+    mism = np.flatnonzero(ok & (ids != rt.ids).any(axis=1))
+    assert mism.size == 0, f"{mism.size} unflagged tokens differ, first {mism[:5]}: {ids[mism[:2]]} vs {rt.ids[mism[:2]]}"
+    for t in np.flatnonzero(rt.flags & (ids != rt.ids).any(axis=1)):
+        assert valid_selection(case.spec, z[t], case.bias64, ids[t]), f"token {t}: invalid near-tie selection {ids[t]}"
+    rel = np.abs(wts[ok] - rt.weights[ok]) / np.abs(rt.weights[ok])
+    assert rel.size == 0 or rel.max() <= WEIGHT_RTOL, f"weights rel err {rel.max():.3e}"
+    return int(rt.flags.sum())
+
+
+def run_layer(case: Case, aux: bool = True, out_alias: bool = False):
+    s = case.spec
+    cfg = moe.config_from_spec(s)
+    ws = moe.alloc_workspace(cfg)
+    ids = torch.empty((s.n_tokens, s.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((s.n_tokens, s.top_k), dtype=torch.float32, device="cuda")
+    r = case.r.clone()
+    out = r if out_alias else torch.empty_like(r)
+    stream = torch.cuda.Stream()
+    aux_stream = torch.cuda.Stream() if aux else None
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        moe.layer_forward(cfg, moe.weights_struct(case.w), case.x, r, out, ids, wts, ws, stream=stream,
+                          aux_stream=aux_stream)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), ids.cpu().numpy(), wts.cpu().numpy()
+
+
+def check_layer(case: Case, out: np.ndarray, ids: np.ndarray, tokens=None):
+    """Gate: per-token normwise error of y_moe = out - r against the oracle
+    (re-run with the GPU's ids for tokens whose near-tied ids differ)."""
+    s = case.spec
+    toks = np.arange(s.n_tokens) if tokens is None else np.asarray(tokens)
+    ref = case.oracle_layer(tokens=toks, ids=ids)
+    y = out[toks].astype(np.float64) - case.r64[toks]
+    err = normwise_err(y, ref.y_moe)
+    err_out = normwise_err(out[toks].astype(np.float64), ref.out)
+    tol = TOL[s.expert_dtype]
+    assert err <= tol, f"y_moe normwise error {err:.3e} > {tol}"
+    assert err_out <= tol
+    return err

@@ -1,0 +1,239 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Small shapes run every token through the oracle and span several GEMM tiles
+with a ragged tail; the full workload shapes compare every token's routing
+and permutation, and the layer output on a sample of tokens."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from tests.gpu_harness import (TOL, check_layer, check_route, make_case, normwise_err, run_layer, run_route,
+                               spec_of)
+from top_routing_grouped_amd import moe
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # name: (base workload, overrides)
+    "small_f32": ("tiny_f32", dict(d_model=64, n_experts=32, top_k=4, d_ff=32, d_ff_shared=48)),
+    "small_bf16": ("qwen_decode", dict(d_model=256, n_experts=32, top_k=4, d_ff=128, d_ff_shared=128)),
+    "small_bf16_noshared": ("qwen_decode", dict(d_model=256, n_experts=48, top_k=6, d_ff=256, d_ff_shared=0)),
+    "small_sigmoid": ("sigmoid_group", dict(d_model=256, n_experts=32, n_group=4, topk_group=2, top_k=4,
+                                            d_ff=128, d_ff_shared=128)),
+    "small_u4": ("qwen_u4", dict(d_model=256, n_experts=32, top_k=4, d_ff=128, d_ff_shared=128)),
+}
+SMALL_T = [1, 37, 301, 700]
+
+FULL = [("tiny_f32", 4), ("qwen_decode", 1), ("qwen_decode", 8), ("qwen_decode", 32),
+        ("qwen_prefill_skew", 4096), ("sigmoid_group", 2048), ("qwen_u4", 1), ("qwen_u4", 64), ("qwen_u4", 512)]
+SAMPLE = 48  # tokens compared through the oracle's expert math at large T
+
+
+def _small(name, T):
+    base, kw = SMALL[name]
+    return make_case(spec_of(base, n_tokens=T, **kw))
+
+
+def _sample(T, seed=0):
+    if T <= 64:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, SAMPLE - 2, replace=False)]))
+
+
+# ------------------------------------------------------------------ routing
+@pytest.mark.parametrize("T", SMALL_T)
+@pytest.mark.parametrize("name", list(SMALL))
+def test_route_small(name, T):
+    case = _small(name, T)
+    ids, wts = run_route(case)
+    z, rt = case.oracle_route()
+    check_route(case, ids, wts, z, rt)
+
+
+@pytest.mark.parametrize("name,T", FULL)
+def test_route_full(name, T):
+    case = make_case(spec_of(name, n_tokens=T))
+    ids, wts = run_route(case)
+    z, rt = case.oracle_route()
+    flagged = check_route(case, ids, wts, z, rt)
+    print(f"{name} T={T}: {flagged} near-tie tokens flagged")
+
+
+@pytest.mark.parametrize("family", ["softmax", "sigmoid_group"])
+def test_route_all_ties_lowest_index(family):
+    base = "qwen_decode" if family == "softmax" else "sigmoid_group"
+    spec = spec_of(base, n_tokens=5, d_model=256, n_experts=64, top_k=8, d_ff=128, d_ff_shared=128,
+                   **({} if family == "softmax" else dict(n_group=8, topk_group=4)))
+    case = make_case(spec, cache_key=("ties", family))
+    case.w.router.zero_()
+    if case.w.expert_bias is not None:
+        case.w.expert_bias.zero_()
+    ids, wts = run_route(case)
+    assert (ids == np.arange(8)[None]).all()
+    want = 1 / 8 if family == "softmax" else 2.5 / 8
+    np.testing.assert_allclose(wts, want, rtol=1e-6)
+
+
+# ------------------------------------------------------------------ permute
+def _run_permute(E, K, ids_np):
+    T = ids_np.shape[0]
+    cfg = moe.make_config(T, 256, E, K, 128, 0)
+    ids = torch.from_numpy(ids_np.astype(np.int32)).cuda()
+    off = torch.full((E + 1,), -1, dtype=torch.int32, device="cuda")
+    act = torch.full((E,), -1, dtype=torch.int32, device="cuda")
+    na = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    sp = torch.full((T * K,), -1, dtype=torch.int32, device="cuda")
+    moe.permute(cfg, ids, off, act, na, sp)
+    torch.cuda.synchronize()
+    return off.cpu().numpy(), act.cpu().numpy(), int(na.item()), sp.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,E,K,mode", [(1, 256, 8, "rand"), (8, 256, 8, "rand"), (4096, 256, 8, "rand"),
+                                        (4096, 256, 8, "zipf"), (2048, 128, 8, "hot"), (33, 1024, 1, "rand"),
+                                        (1000, 16, 16, "rand"), (5000, 512, 3, "zipf")])
+def test_permute_bit_exact(T, E, K, mode):
+    rng = np.random.default_rng(T + E + K)
+    if mode == "rand":
+        ids = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+    elif mode == "hot":
+        ids = np.tile(np.arange(K), (T, 1))
+    else:
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p /= p.sum()
+        ids = np.stack([rng.choice(E, K, replace=False, p=p) for _ in range(T)])
+    off, act, na, sp = _run_permute(E, K, ids)
+    ref = O.permute(ids, E)
+    np.testing.assert_array_equal(off, ref.offsets)
+    assert na == ref.n_active
+    np.testing.assert_array_equal(act[:na], ref.active)
+    np.testing.assert_array_equal(sp, ref.sorted_pairs)
+
+
+def test_permute_drops_out_of_range_ids():
+    rng = np.random.default_rng(3)
+    T, E, K = 50, 64, 4
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+    ids[3, 1] = -5
+    ids[7, 0] = E + 3
+    off, act, na, sp = _run_permute(E, K, ids)
+    keep = (ids.ravel() >= 0) & (ids.ravel() < E)
+    assert off[E] == keep.sum()
+    counts = np.bincount(ids.ravel()[keep], minlength=E)
+    np.testing.assert_array_equal(np.diff(off), counts)
+    order = np.flatnonzero(keep)[np.argsort(ids.ravel()[keep], kind="stable")]
+    np.testing.assert_array_equal(sp[:keep.sum()], order)
+
+
+# ------------------------------------------------------------------ experts / shared / combine
+def _experts_vs_oracle(case, tokens):
+    s = case.spec
+    z, rt = case.oracle_route()
+    cfg = moe.config_from_spec(s)
+    ws = moe.alloc_workspace(cfg)
+    perm = O.permute(rt.ids, s.n_experts)
+    t32 = lambda a: torch.from_numpy(np.ascontiguousarray(a).astype(np.int32)).cuda()  # noqa: E731
+    off, act, sp = t32(perm.offsets), t32(np.pad(perm.active, (0, s.n_experts - perm.n_active))), \
+        t32(perm.sorted_pairs)
+    na = t32(np.array([perm.n_active]))
+    wflat = torch.from_numpy(rt.weights.astype(np.float32).ravel()).cuda()
+    slot = torch.full((s.n_tokens, s.top_k, s.d_model), float("nan"), device="cuda")
+    moe.experts(cfg, case.x, moe.weights_struct(case.w), off, act, na, sp, wflat, slot, ws)
+    torch.cuda.synchronize()
+    got = slot.cpu().numpy()[tokens]
+    # oracle slots with the same (fp32-rounded) weights the GPU received
+    alpha = rt.weights.astype(np.float32).astype(np.float64)
+    ref = O.routed_slots(case.x64, rt.ids, alpha, case.banks, tokens=tokens)
+    assert np.isfinite(got).all()
+    err = normwise_err(got.sum(axis=1), ref.sum(axis=1))
+    tol = TOL[s.expert_dtype]
+    assert err <= tol, f"routed sum error {err:.3e}"
+    # each slot row individually (normwise against that slot's own scale)
+    err_slot = normwise_err(got.reshape(-1, s.d_model), ref.reshape(-1, s.d_model))
+    assert err_slot <= tol, f"slot error {err_slot:.3e}"
+    return err
+
+
+@pytest.mark.parametrize("T", SMALL_T)
+@pytest.mark.parametrize("name", list(SMALL))
+def test_experts_small(name, T):
+    case = _small(name, T)
+    _experts_vs_oracle(case, np.arange(T))
+
+
+@pytest.mark.parametrize("name,T", FULL)
+def test_experts_full(name, T):
+    case = make_case(spec_of(name, n_tokens=T))
+    err = _experts_vs_oracle(case, _sample(T))
+    print(f"{name} T={T}: routed normwise error {err:.2e}")
+
+
+@pytest.mark.parametrize("name,T", [("small_f32", 37), ("small_bf16", 301), ("small_sigmoid", 5), ("small_u4", 700),
+                                    ("qwen_decode", 8), ("qwen_u4", 512)])
+def test_shared_expert(name, T):
+    case = _small(name, T) if name in SMALL else make_case(spec_of(name, n_tokens=T))
+    s = case.spec
+    cfg = moe.config_from_spec(s)
+    ws = moe.alloc_workspace(cfg)
+    out = torch.full((T, s.d_model), float("nan"), device="cuda")
+    moe.shared_expert(cfg, case.x, moe.weights_struct(case.w), out, ws)
+    torch.cuda.synchronize()
+    ref = O.shared_expert(case.x64, case.banks)
+    err = normwise_err(out.cpu().numpy().astype(np.float64), ref)
+    assert err <= TOL[s.expert_dtype], err
+
+
+def test_combine_matches_oracle():
+    rng = np.random.default_rng(5)
+    T, K, D = 37, 8, 2048
+    cfg = moe.make_config(T, D, 256, K, 512, 512)
+    slots = rng.standard_normal((T, K, D)).astype(np.float32)
+    sh = rng.standard_normal((T, D)).astype(np.float32)
+    r = rng.standard_normal((T, D)).astype(np.float32)
+    out = torch.empty(T, D, device="cuda")
+    moe.combine(cfg, torch.from_numpy(slots).cuda(), torch.from_numpy(sh).cuda(), torch.from_numpy(r).cuda(), out)
+    torch.cuda.synchronize()
+    ref = O.combine(r.astype(np.float64), slots.astype(np.float64), sh.astype(np.float64))
+    np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=0, atol=1e-5)
+    # shared NULL and in-place (out aliases residual)
+    rr = torch.from_numpy(r).cuda()
+    moe.combine(cfg, torch.from_numpy(slots).cuda(), None, rr, rr)
+    torch.cuda.synchronize()
+    ref0 = O.combine(r.astype(np.float64), slots.astype(np.float64), np.zeros((T, D)))
+    np.testing.assert_allclose(rr.cpu().numpy(), ref0, rtol=0, atol=1e-5)
+
+
+# ------------------------------------------------------------------ whole layer
+@pytest.mark.parametrize("T", SMALL_T)
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_small(name, T):
+    case = _small(name, T)
+    out, ids, wts = run_layer(case)
+    z, rt = case.oracle_route()
+    check_route(case, ids, wts, z, rt)
+    check_layer(case, out, ids)
+
+
+@pytest.mark.parametrize("name,T", FULL)
+def test_layer_full(name, T):
+    case = make_case(spec_of(name, n_tokens=T))
+    out, ids, wts = run_layer(case)
+    z, rt = case.oracle_route()
+    check_route(case, ids, wts, z, rt)
+    err = check_layer(case, out, ids, tokens=_sample(T))
+    print(f"{name} T={T}: y_moe normwise error {err:.2e} (gate {TOL[case.spec.expert_dtype]})")
+
+
+@pytest.mark.parametrize("name,T", [("small_bf16", 301), ("small_u4", 37), ("small_f32", 700), ("qwen_decode", 8),
+                                    ("qwen_prefill_skew", 4096)])
+def test_layer_deterministic_and_stream_independent(name, T):
+    case = _small(name, T) if name in SMALL else make_case(spec_of(name, n_tokens=T))
+    a = run_layer(case, aux=True)
+    b = run_layer(case, aux=True)
+    c = run_layer(case, aux=False)
+    d = run_layer(case, aux=True, out_alias=True)
+    for other in (b, c, d):
+        for u, v in zip(a, other):
+            assert np.array_equal(u.view(np.uint32) if u.dtype == np.float32 else u,
+                                  v.view(np.uint32) if v.dtype == np.float32 else v)

@@ -1,0 +1,382 @@
+// C ABI of the MoE layer library: argument checks, workspace carving, launch
+// sequencing and the two-stream fork/join of the shared expert.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "moe_kernels.h"
+
+namespace moe {
+size_t permute_smem_bytes(int E);
+}
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+#define HIP_TRY(expr)                                                                         \
+    do {                                                                                      \
+        hipError_t e_ = (expr);                                                               \
+        if (e_ != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+int wkind_of(moe_dtype d) {
+    return d == MOE_F32 ? moe::kWF32 : d == MOE_BF16 ? moe::kWBF16 : moe::kWU4;
+}
+
+// K elements per chunk a wave consumes: fp32 16, bf16/u4 128.
+int kspan_of(moe_dtype expert) { return expert == MOE_F32 ? 16 : 128; }
+
+// tokens per routed GEMM tile: 16 when experts average fewer than 64 pairs.
+int routed_tf(const moe_config& c) {
+    return (int64_t)c.n_tokens * c.top_k >= (int64_t)64 * c.n_experts ? 4 : 1;
+}
+int dense_tf(const moe_config& c) { return c.n_tokens >= 64 ? 4 : 1; }
+
+int64_t max_tiles(int64_t n_pairs, int E, int tile_rows) {
+    const int64_t act = std::min<int64_t>(E, n_pairs);
+    return (n_pairs + act * (tile_rows - 1)) / tile_rows;
+}
+
+struct Layout {
+    size_t logits, gate_logit, ids, wts, offsets, active, n_active, n_tiles, pairs, tiles, h, slots, hs, ys, total;
+};
+
+Layout layout(const moe_config& c) {
+    const size_t T = c.n_tokens, E = c.n_experts, K = c.top_k, D = c.d_model, F = c.d_ff, Fs = c.d_ff_shared;
+    const size_t TK = T * K;
+    const size_t hb = c.expert_dtype == MOE_F32 ? 4 : 2;
+    const size_t mt = size_t(max_tiles(TK, int(E), 16 * routed_tf(c)));
+    Layout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o += align256(bytes);
+        return at;
+    };
+    L.logits = take(T * E * 4);
+    L.gate_logit = take(T * 4);
+    L.ids = take(TK * 4);
+    L.wts = take(TK * 4);
+    L.offsets = take((E + 1) * 4);
+    L.active = take(E * 4);
+    L.n_active = take(4);
+    L.n_tiles = take(4);
+    L.pairs = take(TK * 4);
+    L.tiles = take(mt * 16);
+    L.h = take(TK * F * hb);
+    L.slots = take(TK * D * hb);
+    L.hs = take(T * Fs * hb);
+    L.ys = take(T * D * 4);
+    L.total = o;
+    return L;
+}
+
+moe_status check_config(const moe_config* c) {
+    if (!c) return fail(MOE_ERR_INVALID_ARGUMENT, "config is NULL");
+    if (c->n_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "n_tokens < 0");
+    if (c->d_model <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->d_ff <= 0 || c->d_ff_shared < 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "sizes must be positive (d_ff_shared >= 0)");
+    if (c->top_k > c->n_experts) return fail(MOE_ERR_INVALID_ARGUMENT, "top_k > n_experts");
+    if (c->top_k > 32) return fail(MOE_ERR_UNSUPPORTED, "top_k > 32");
+    if (c->n_experts > 1024 || c->n_experts % 16) return fail(MOE_ERR_UNSUPPORTED, "n_experts must be a multiple of 16, <= 1024");
+    if ((int64_t)c->n_tokens * c->top_k > (int64_t(1) << 30)) return fail(MOE_ERR_UNSUPPORTED, "n_tokens * top_k too large");
+    if (c->family != MOE_ROUTE_SOFTMAX_TOPK && c->family != MOE_ROUTE_SIGMOID_GROUP_TOPK)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "unknown routing family");
+    if (c->family == MOE_ROUTE_SIGMOID_GROUP_TOPK) {
+        const int E = c->n_experts, G = c->n_group, TG = c->topk_group;
+        if (G < 1 || G > 64) return fail(MOE_ERR_INVALID_ARGUMENT, "n_group must be in [1, 64]");
+        if (E % G || E / G < 2) return fail(MOE_ERR_INVALID_ARGUMENT, "n_experts must split into n_group groups of >= 2");
+        if (TG < 1 || TG > G) return fail(MOE_ERR_INVALID_ARGUMENT, "topk_group must be in [1, n_group]");
+        if (c->top_k > TG * (E / G)) return fail(MOE_ERR_INVALID_ARGUMENT, "top_k exceeds the experts of the kept groups");
+        if (!(std::isfinite(c->routed_scaling) && c->routed_scaling > 0.f))
+            return fail(MOE_ERR_INVALID_ARGUMENT, "routed_scaling must be finite and > 0");
+    }
+    const bool f32 = c->act_dtype == MOE_F32;
+    if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "act_dtype must be F32 or BF16");
+    if (c->router_dtype != c->act_dtype) return fail(MOE_ERR_UNSUPPORTED, "router_dtype must equal act_dtype");
+    if (f32 ? c->expert_dtype != MOE_F32 : (c->expert_dtype != MOE_BF16 && c->expert_dtype != MOE_U4_AFFINE_G64))
+        return fail(MOE_ERR_UNSUPPORTED, "expert_dtype must be F32 with F32 activations, BF16 or U4_AFFINE_G64 with BF16");
+    const int span = kspan_of(c->expert_dtype);
+    if (c->d_model % span || c->d_ff % span || c->d_ff_shared % span)
+        return fail(MOE_ERR_UNSUPPORTED, "d_model, d_ff, d_ff_shared must be multiples of %d for this dtype", span);
+    return MOE_OK;
+}
+
+moe_status check_ws(const moe_config& c, void* ws, size_t ws_bytes) {
+    const size_t need = layout(c).total;
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (!ws) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    return MOE_OK;
+}
+
+bool matrix_ok(const moe_matrix& m, moe_dtype d) {
+    if (!m.w) return false;
+    if (d == MOE_U4_AFFINE_G64 && (!m.scale || !m.min)) return false;
+    return true;
+}
+
+moe_status check_weights(const moe_config& c, const moe_weights* w, bool routed, bool shared) {
+    if (!w) return fail(MOE_ERR_INVALID_ARGUMENT, "weights is NULL");
+    if (routed && !(matrix_ok(w->gate, c.expert_dtype) && matrix_ok(w->up, c.expert_dtype) &&
+                    matrix_ok(w->down, c.expert_dtype)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "routed gate/up/down bank pointer is NULL");
+    if (shared && c.d_ff_shared > 0 &&
+        !(matrix_ok(w->shared_gate, c.expert_dtype) && matrix_ok(w->shared_up, c.expert_dtype) &&
+          matrix_ok(w->shared_down, c.expert_dtype)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "shared expert matrix pointer is NULL");
+    return MOE_OK;
+}
+
+moe::GemmArgs gemm_args(const moe_matrix& m0, const moe_matrix* m1, int N, int K, int n_banks) {
+    moe::GemmArgs a{};
+    a.w0 = m0.w; a.s0 = m0.scale; a.m0 = m0.min;
+    if (m1) { a.w1 = m1->w; a.s1 = m1->scale; a.m1 = m1->min; }
+    a.N = N; a.K = K; a.n_banks = n_banks;
+    return a;
+}
+
+template <class T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+// ---- stages (arguments already validated)
+moe_status stage_route(const moe_config& c, const Layout& L, void* ws, const void* x, const void* router,
+                       const float* bias, int32_t* ids, float* wts, hipStream_t s) {
+    const int T = c.n_tokens;
+    moe::GemmArgs a{};
+    moe_matrix rm{router, nullptr, nullptr};
+    a = gemm_args(rm, nullptr, c.n_experts, c.d_model, 1);
+    a.act = x; a.n_act_rows = T; a.n_rows = T;
+    a.out = at<float>(ws, L.logits);
+    const int tf = dense_tf(c);
+    HIP_TRY(moe::launch_gemm(moe::kDenseStore, c.router_dtype == MOE_F32 ? moe::kWF32 : moe::kWBF16, false, a,
+                             (T + 16 * tf - 1) / (16 * tf), tf, s));
+    HIP_TRY(moe::launch_route_select(at<float>(ws, L.logits), T, c.n_experts, c.top_k, int(c.family), c.n_group,
+                                     c.topk_group, c.routed_scaling,
+                                     c.family == MOE_ROUTE_SIGMOID_GROUP_TOPK ? bias : nullptr, ids, wts, s));
+    return MOE_OK;
+}
+
+moe_status stage_experts(const moe_config& c, const Layout& L, void* ws, const void* x, const moe_weights& w,
+                         const int32_t* pairs, const int4* tiles, const int32_t* n_tiles, const float* wts,
+                         void* slot_out, bool slot_bf16, hipStream_t s) {
+    const int T = c.n_tokens, K = c.top_k, TK = T * K;
+    const int tf = routed_tf(c);
+    const int grid = int(max_tiles(TK, c.n_experts, 16 * tf));
+    const int wk = wkind_of(c.expert_dtype);
+    const bool hbf = c.expert_dtype != MOE_F32;
+    void* h = at<void>(ws, L.h);
+    moe::GemmArgs a = gemm_args(w.gate, &w.up, c.d_ff, c.d_model, c.n_experts);
+    a.act = x; a.n_act_rows = T;
+    a.tiles = tiles; a.n_tiles = n_tiles; a.pairs = pairs; a.n_pairs = TK; a.topk = K;
+    a.out = h;
+    HIP_TRY(moe::launch_gemm(moe::kRoutedGateUp, wk, hbf, a, grid, tf, s));
+    moe::GemmArgs d = gemm_args(w.down, nullptr, c.d_model, c.d_ff, c.n_experts);
+    d.act = h; d.n_act_rows = TK;
+    d.tiles = tiles; d.n_tiles = n_tiles; d.pairs = pairs; d.n_pairs = TK; d.topk = K;
+    d.out = slot_out; d.row_scale = wts;
+    HIP_TRY(moe::launch_gemm(moe::kRoutedDown, wk, slot_bf16, d, grid, tf, s));
+    return MOE_OK;
+}
+
+moe_status stage_shared(const moe_config& c, const Layout& L, void* ws, const void* x, const moe_weights& w,
+                        float* shared_out, hipStream_t s) {
+    const int T = c.n_tokens;
+    const int tf = dense_tf(c);
+    const int grid = (T + 16 * tf - 1) / (16 * tf);
+    const int wk = wkind_of(c.expert_dtype);
+    const bool hbf = c.expert_dtype != MOE_F32;
+    const float* gl = nullptr;
+    if (w.shared_gate_vec) {
+        HIP_TRY(moe::launch_gate_logit(x, c.act_dtype == MOE_F32, w.shared_gate_vec, T, c.d_model,
+                                       at<float>(ws, L.gate_logit), s));
+        gl = at<float>(ws, L.gate_logit);
+    }
+    void* hs = at<void>(ws, L.hs);
+    moe::GemmArgs a = gemm_args(w.shared_gate, &w.shared_up, c.d_ff_shared, c.d_model, 1);
+    a.act = x; a.n_act_rows = T; a.n_rows = T; a.out = hs;
+    HIP_TRY(moe::launch_gemm(moe::kDenseGateUp, wk, hbf, a, grid, tf, s));
+    moe::GemmArgs d = gemm_args(w.shared_down, nullptr, c.d_model, c.d_ff_shared, 1);
+    d.act = hs; d.n_act_rows = T; d.n_rows = T; d.out = shared_out; d.row_scale = gl;
+    HIP_TRY(moe::launch_gemm(moe::kDenseDown, wk, false, d, grid, tf, s));
+    return MOE_OK;
+}
+
+constexpr int kMaxDev = 64;
+thread_local hipEvent_t g_ev_fork[kMaxDev] = {};
+thread_local hipEvent_t g_ev_join[kMaxDev] = {};
+
+moe_status fork_join_events(hipEvent_t* fork, hipEvent_t* join) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDev) return fail(MOE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    if (!g_ev_fork[dev]) HIP_TRY(hipEventCreateWithFlags(&g_ev_fork[dev], hipEventDisableTiming));
+    if (!g_ev_join[dev]) HIP_TRY(hipEventCreateWithFlags(&g_ev_join[dev], hipEventDisableTiming));
+    *fork = g_ev_fork[dev];
+    *join = g_ev_join[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status st) {
+    switch (st) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+    g_err[0] = 0;
+    if (moe_status st = check_config(cfg)) return st;
+    if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    *bytes = layout(*cfg).total;
+    return MOE_OK;
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const void* router, const float* expert_bias,
+                     int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes, moe_stream_t stream) {
+    g_err[0] = 0;
+    if (moe_status st = check_config(cfg)) return st;
+    if (cfg->n_tokens == 0) return MOE_OK;
+    if (!x || !router || !topk_ids || !topk_weights) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL tensor argument");
+    if (moe_status st = check_ws(*cfg, ws, ws_bytes)) return st;
+    (void)hipGetLastError();
+    return stage_route(*cfg, layout(*cfg), ws, x, router, expert_bias, topk_ids, topk_weights, stream);
+}
+
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* expert_offsets,
+                       int32_t* active_experts, int32_t* n_active, int32_t* sorted_pairs, void* ws, size_t ws_bytes,
+                       moe_stream_t stream) {
+    g_err[0] = 0;
+    (void)ws;
+    (void)ws_bytes;
+    if (moe_status st = check_config(cfg)) return st;
+    if (cfg->n_tokens == 0) return MOE_OK;
+    if (!topk_ids || !expert_offsets || !active_experts || !n_active || !sorted_pairs)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "NULL tensor argument");
+    (void)hipGetLastError();
+    HIP_TRY(moe::launch_permute(topk_ids, cfg->n_tokens * cfg->top_k, cfg->n_experts, expert_offsets, active_experts,
+                                n_active, sorted_pairs, nullptr, nullptr, 16, stream));
+    return MOE_OK;
+}
+
+moe_status moe_experts(const moe_config* cfg, const void* x, const moe_weights* weights,
+                       const int32_t* expert_offsets, const int32_t* active_experts, const int32_t* n_active,
+                       const int32_t* sorted_pairs, const float* topk_weights, float* slot_out, void* ws,
+                       size_t ws_bytes, moe_stream_t stream) {
+    g_err[0] = 0;
+    if (moe_status st = check_config(cfg)) return st;
+    if (cfg->n_tokens == 0) return MOE_OK;
+    if (!x || !expert_offsets || !active_experts || !n_active || !sorted_pairs || !topk_weights || !slot_out)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "NULL tensor argument");
+    if (moe_status st = check_weights(*cfg, weights, true, false)) return st;
+    if (moe_status st = check_ws(*cfg, ws, ws_bytes)) return st;
+    (void)hipGetLastError();
+    const Layout L = layout(*cfg);
+    const int TK = cfg->n_tokens * cfg->top_k;
+    const int tile_rows = 16 * routed_tf(*cfg);
+    int4* tiles = at<int4>(ws, L.tiles);
+    int32_t* nt = at<int32_t>(ws, L.n_tiles);
+    HIP_TRY(moe::launch_build_tiles(expert_offsets, active_experts, n_active, cfg->n_experts, TK, tiles, nt,
+                                    int(max_tiles(TK, cfg->n_experts, tile_rows)), tile_rows, stream));
+    return stage_experts(*cfg, L, ws, x, *weights, sorted_pairs, tiles, nt, topk_weights, slot_out, false, stream);
+}
+
+moe_status moe_shared_expert(const moe_config* cfg, const void* x, const moe_weights* weights, float* shared_out,
+                             void* ws, size_t ws_bytes, moe_stream_t stream) {
+    g_err[0] = 0;
+    if (moe_status st = check_config(cfg)) return st;
+    if (cfg->d_ff_shared == 0) return fail(MOE_ERR_INVALID_ARGUMENT, "d_ff_shared == 0: no shared expert");
+    if (cfg->n_tokens == 0) return MOE_OK;
+    if (!x || !shared_out) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL tensor argument");
+    if (moe_status st = check_weights(*cfg, weights, false, true)) return st;
+    if (moe_status st = check_ws(*cfg, ws, ws_bytes)) return st;
+    (void)hipGetLastError();
+    return stage_shared(*cfg, layout(*cfg), ws, x, *weights, shared_out, stream);
+}
+
+moe_status moe_combine(const moe_config* cfg, const float* slot_out, const float* shared_out, const float* residual,
+                       float* out, moe_stream_t stream) {
+    g_err[0] = 0;
+    if (moe_status st = check_config(cfg)) return st;
+    if (cfg->n_tokens == 0) return MOE_OK;
+    if (!slot_out || !residual || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL tensor argument");
+    (void)hipGetLastError();
+    HIP_TRY(moe::launch_combine(slot_out, false, shared_out, residual, out, cfg->n_tokens, cfg->top_k, cfg->d_model,
+                                stream));
+    return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, const void* x, const float* residual,
+                             float* out, int32_t* topk_ids_out, float* topk_weights_out, void* ws, size_t ws_bytes,
+                             moe_stream_t stream, moe_stream_t aux_stream) {
+    g_err[0] = 0;
+    if (moe_status st = check_config(cfg)) return st;
+    if (cfg->n_tokens == 0) return MOE_OK;
+    if (!x || !residual || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL tensor argument");
+    if (!weights || !weights->router) return fail(MOE_ERR_INVALID_ARGUMENT, "router weights are NULL");
+    if (moe_status st = check_weights(*cfg, weights, true, true)) return st;
+    if (moe_status st = check_ws(*cfg, ws, ws_bytes)) return st;
+    (void)hipGetLastError();
+    const moe_config& c = *cfg;
+    const Layout L = layout(c);
+    const int TK = c.n_tokens * c.top_k;
+    const bool has_shared = c.d_ff_shared > 0;
+    const bool slot_bf16 = c.expert_dtype != MOE_F32;
+    float* ys = has_shared ? at<float>(ws, L.ys) : nullptr;
+
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    const bool fork = has_shared && aux_stream && aux_stream != stream;
+    if (fork) {
+        if (moe_status st = fork_join_events(&ev_fork, &ev_join)) return st;
+        HIP_TRY(hipEventRecord(ev_fork, stream));
+        HIP_TRY(hipStreamWaitEvent(aux_stream, ev_fork, 0));
+        if (moe_status st = stage_shared(c, L, ws, x, *weights, ys, aux_stream)) return st;
+        HIP_TRY(hipEventRecord(ev_join, aux_stream));
+    } else if (has_shared) {
+        if (moe_status st = stage_shared(c, L, ws, x, *weights, ys, stream)) return st;
+    }
+
+    int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+    float* wts = topk_weights_out ? topk_weights_out : at<float>(ws, L.wts);
+    if (moe_status st = stage_route(c, L, ws, x, weights->router, weights->expert_bias, ids, wts, stream)) return st;
+    const int tile_rows = 16 * routed_tf(c);
+    int32_t* pairs = at<int32_t>(ws, L.pairs);
+    int4* tiles = at<int4>(ws, L.tiles);
+    int32_t* nt = at<int32_t>(ws, L.n_tiles);
+    HIP_TRY(moe::launch_permute(ids, TK, c.n_experts, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.active),
+                                at<int32_t>(ws, L.n_active), pairs, tiles, nt, tile_rows, stream));
+    void* slots = at<void>(ws, L.slots);
+    if (moe_status st = stage_experts(c, L, ws, x, *weights, pairs, tiles, nt, wts, slots, slot_bf16, stream))
+        return st;
+    if (fork) HIP_TRY(hipStreamWaitEvent(stream, ev_join, 0));
+    HIP_TRY(moe::launch_combine(slots, slot_bf16, ys, residual, out, c.n_tokens, c.top_k, c.d_model, stream));
+    return MOE_OK;
+}
+
+}  // extern "C"

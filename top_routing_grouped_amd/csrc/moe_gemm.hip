@@ -1,0 +1,335 @@
+// Grouped "weight-rows x token-columns" MFMA kernels for the MoE layer.
+//
+// One kernel template serves every matrix product of the layer:
+//   * router logits           z[t, e]   = W_router[e, :] . x[t, :]
+//   * routed gate/up + SwiGLU h[p, f]   = SiLU(W_gate[e] x_t)_f * (W_up[e] x_t)_f
+//   * routed down x alpha     slot[p,:] = alpha_p * W_down[e] h_p
+//   * shared gate/up, shared down (x sigmoid gate)
+// (Treebeard, "How Treebeard routes Qwen3.6 MoE tokens": "Routing math",
+// "Routed expert computation", "Shared expert computation").
+//
+// Mapping to CDNA4: the weight matrix is the MFMA "A" operand (16 weight rows
+// per wave), the gathered token rows are the "B" operand (16 tokens per
+// fragment), so each weight element a wave loads is used against every token
+// of the tile and the result for one token sits in 4 consecutive feature
+// rows of a lane (one 8/16-byte store).  Both operands are K-contiguous in
+// memory.  Because any permutation of the reduction index applied to both
+// operands leaves a dot product unchanged, lane-group q of a wave loads one
+// contiguous 64-byte run of K (32 bf16 / 4-bit codes, or 4 fp32) and feeds
+// it to 4 consecutive MFMAs, instead of the 16-byte slices the instruction's
+// own K order would ask for.  Weight rows are streamed straight from HBM into
+// registers (read once per tile); a workgroup's waves split K and reduce
+// their partial sums through LDS in a fixed order.
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+// --------------------------------------------------------------- operands
+template <int WK>
+struct WTraits;
+template <>
+struct WTraits<kWF32> {
+    static constexpr int KL = 4;  // K elements per lane per chunk
+};
+template <>
+struct WTraits<kWBF16> {
+    static constexpr int KL = 32;
+};
+template <>
+struct WTraits<kWU4> {
+    static constexpr int KL = 32;
+};
+
+// A chunk of one lane's operand: 4 MFMA-ready fragments.
+template <bool F32>
+struct Frag;
+template <>
+struct Frag<false> {
+    bf16x8 v[4];
+};
+template <>
+struct Frag<true> {
+    float v[4];
+};
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// Weight chunk: row pointer already offset to the row; k = element offset.
+template <int WK>
+__device__ __forceinline__ void load_w(Frag<WK == kWF32>& f, const void* w, const void* sc, const void* mn,
+                                       size_t row, int K, int k) {
+    if constexpr (WK == kWBF16) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(w) + row * K + k);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f.v[j] = as_bf16x8(__builtin_nontemporal_load(p + j));
+    } else if constexpr (WK == kWF32) {
+        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(w) + row * K + k);
+        f.v[0] = v.x; f.v[1] = v.y; f.v[2] = v.z; f.v[3] = v.w;
+    } else {  // 4-bit affine, group 64: 32 codes (16 bytes) inside one group
+        const u32x4 c = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(w) + row * (K / 2) + k / 2));
+        const size_t g = row * (K / 64) + k / 64;
+        const float s = bf16_to_f32(static_cast<const uint16_t*>(sc)[g]);
+        const float m = bf16_to_f32(static_cast<const uint16_t*>(mn)[g]);
+        const uint32_t words[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t packed[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = fmaf(s, float((words[j] >> (8 * i)) & 0xfu), m);
+                const float hi = fmaf(s, float((words[j] >> (8 * i + 4)) & 0xfu), m);
+                packed[i] = pack_bf16x2(lo, hi);
+            }
+            f.v[j] = as_bf16x8(make_uint4(packed[0], packed[1], packed[2], packed[3]));
+        }
+    }
+}
+
+// Activation chunk (bf16 or fp32 rows), zeros for an absent token.
+template <bool F32>
+__device__ __forceinline__ void load_x(Frag<F32>& f, const void* rowp, int k) {
+    if constexpr (F32) {
+        if (rowp) {
+            const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(rowp) + k);
+            f.v[0] = v.x; f.v[1] = v.y; f.v[2] = v.z; f.v[3] = v.w;
+        } else {
+            f.v[0] = f.v[1] = f.v[2] = f.v[3] = 0.f;
+        }
+    } else {
+        if (rowp) {
+            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(rowp) + k);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f.v[j] = as_bf16x8(p[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f.v[j] = as_bf16x8(make_uint4(0, 0, 0, 0));
+        }
+    }
+}
+
+template <bool F32>
+__device__ __forceinline__ void mma_chunk(f32x4& acc, const Frag<F32>& a, const Frag<F32>& b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (F32)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+        else
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[j], b.v[j], acc, 0, 0, 0);
+    }
+}
+
+// --------------------------------------------------------------- kernel
+// MODE: kRoutedGateUp | kRoutedDown | kDenseGateUp | kDenseDown | kDenseStore
+// WK: weight kind; OUTBF: output stored as bf16 (else fp32)
+// TF: 16-token fragments per tile; WN x WKS waves = 4 (rows x K split)
+template <int MODE, int WK, bool OUTBF, int TF, int WN, int WKS>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+    constexpr bool F32 = (WK == kWF32);
+    constexpr bool DUAL = (MODE == kRoutedGateUp || MODE == kDenseGateUp);
+    constexpr bool ROUTED = (MODE == kRoutedGateUp || MODE == kRoutedDown);
+    constexpr int KL = WTraits<WK>::KL;
+    constexpr int SPAN = 4 * KL;
+    constexpr int BM = 16 * TF;
+    constexpr int NM = DUAL ? 2 : 1;
+
+    // ---- tile
+    int e = 0, begin, count;
+    if constexpr (ROUTED) {
+        const int tile = blockIdx.x;
+        if (tile >= *a.n_tiles) return;
+        const int4 t = a.tiles[tile];
+        e = t.x; begin = t.y; count = t.z;
+        if (e < 0 || e >= a.n_banks || begin < 0 || count <= 0 || begin + count > a.n_pairs) return;
+    } else {
+        begin = blockIdx.x * BM;
+        count = min(BM, a.n_rows - begin);
+        if (count <= 0) return;
+    }
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wn = wave % WN;
+    const int wk = wave / WN;
+    const int q = lane >> 4;
+    const int r = lane & 15;
+    const int N = a.N, K = a.K;
+    const int wrow0 = blockIdx.y * (16 * WN) + 16 * wn;
+    const bool rows_ok = wrow0 < N;
+
+    // ---- token rows of this lane (one per 16-token fragment)
+    const void* xrow[TF];
+#pragma unroll
+    for (int j = 0; j < TF; ++j) {
+        const int i = j * 16 + r;
+        const void* p = nullptr;
+        if (i < count) {
+            int arow;
+            if constexpr (MODE == kRoutedGateUp) {
+                const int pair = a.pairs[begin + i];
+                arow = (pair >= 0 && pair < a.n_pairs) ? pair / a.topk : -1;
+            } else {
+                arow = begin + i;
+            }
+            if (arow >= 0 && arow < a.n_act_rows)
+                p = F32 ? static_cast<const void*>(static_cast<const float*>(a.act) + size_t(arow) * K)
+                        : static_cast<const void*>(static_cast<const uint16_t*>(a.act) + size_t(arow) * K);
+        }
+        xrow[j] = p;
+    }
+
+    f32x4 acc[NM][TF];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int j = 0; j < TF; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (rows_ok) {
+        const size_t wrow = size_t(e) * N + wrow0 + r;
+        const int kper = K / WKS;
+        const int kbeg = wk * kper + q * KL;
+        const int nchunks = kper / SPAN;
+#pragma unroll 2
+        for (int c = 0; c < nchunks; ++c) {
+            const int k = kbeg + c * SPAN;
+            Frag<F32> wa[NM];
+            load_w<WK>(wa[0], a.w0, a.s0, a.m0, wrow, K, k);
+            if constexpr (DUAL) load_w<WK>(wa[1], a.w1, a.s1, a.m1, wrow, K, k);
+            Frag<F32> xb[TF];
+#pragma unroll
+            for (int j = 0; j < TF; ++j) load_x<F32>(xb[j], xrow[j], k);
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int j = 0; j < TF; ++j) mma_chunk<F32>(acc[m][j], wa[m], xb[j]);
+        }
+    }
+
+    // ---- split-K reduction through LDS, fixed order wk = 0, 1, 2, ...
+    if constexpr (WKS > 1) {
+        constexpr int NACC = NM * TF * 4;
+        __shared__ float red[(WKS - 1) * WN * NACC * 64];
+        if (wk > 0) {
+            float* dst = red + ((wk - 1) * WN + wn) * NACC * 64;
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int j = 0; j < TF; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dst[((m * TF + j) * 4 + i) * 64 + lane] = acc[m][j][i];
+        }
+        __syncthreads();
+        if (wk > 0) return;
+#pragma unroll
+        for (int s = 1; s < WKS; ++s) {
+            const float* src = red + ((s - 1) * WN + wn) * NACC * 64;
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int j = 0; j < TF; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[m][j][i] += src[((m * TF + j) * 4 + i) * 64 + lane];
+        }
+    }
+    if (!rows_ok) return;
+
+    // ---- epilogue: lane holds rows wrow0 + 4q + (0..3) of token column j*16 + r
+    const int f0 = wrow0 + 4 * q;
+#pragma unroll
+    for (int j = 0; j < TF; ++j) {
+        const int i = j * 16 + r;
+        if (i >= count) continue;
+        float v[4];
+        size_t dest;
+        if constexpr (DUAL) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float g = acc[0][j][t];
+                v[t] = g / (1.0f + __expf(-g)) * acc[1][j][t];
+            }
+            dest = size_t(begin + i);
+        } else if constexpr (MODE == kRoutedDown) {
+            const int pair = a.pairs[begin + i];
+            if (pair < 0 || pair >= a.n_pairs) continue;
+            const float s = a.row_scale[pair];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = s * acc[0][j][t];
+            dest = size_t(pair);
+        } else if constexpr (MODE == kDenseDown) {
+            const float s = a.row_scale ? sigmoidf_(a.row_scale[begin + i]) : 1.0f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = s * acc[0][j][t];
+            dest = size_t(begin + i);
+        } else {  // kDenseStore
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = acc[0][j][t];
+            dest = size_t(begin + i);
+        }
+        if constexpr (OUTBF) {
+            uint2 pk = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + dest * N + f0) = pk;
+        } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + dest * N + f0) =
+                make_float4(v[0], v[1], v[2], v[3]);
+        }
+    }
+}
+
+// --------------------------------------------------------------- launchers
+template <int MODE, int WK, bool OUTBF>
+static hipError_t launch_cfg(const GemmArgs& a, int grid_x, int tf, hipStream_t s) {
+    // small tiles: 16 tokens, 4 waves split K; larger: 64 tokens.
+    const int K = a.K;
+    constexpr int SPAN = 4 * WTraits<WK>::KL;
+    const bool ksplit4 = (K % (4 * SPAN) == 0);
+    const bool ksplit2 = (K % (2 * SPAN) == 0);
+    if (tf == 1) {
+        if (ksplit4) {
+            dim3 g(grid_x, (a.N + 15) / 16);
+            gemm_kernel<MODE, WK, OUTBF, 1, 1, 4><<<g, 256, 0, s>>>(a);
+        } else if (ksplit2) {
+            dim3 g(grid_x, (a.N + 31) / 32);
+            gemm_kernel<MODE, WK, OUTBF, 1, 2, 2><<<g, 256, 0, s>>>(a);
+        } else {
+            dim3 g(grid_x, (a.N + 63) / 64);
+            gemm_kernel<MODE, WK, OUTBF, 1, 4, 1><<<g, 256, 0, s>>>(a);
+        }
+    } else {
+        if (ksplit4) {
+            dim3 g(grid_x, (a.N + 15) / 16);
+            gemm_kernel<MODE, WK, OUTBF, 4, 1, 4><<<g, 256, 0, s>>>(a);
+        } else {
+            dim3 g(grid_x, (a.N + 63) / 64);
+            gemm_kernel<MODE, WK, OUTBF, 4, 4, 1><<<g, 256, 0, s>>>(a);
+        }
+    }
+    return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t dispatch_wk(const GemmArgs& a, int wkind, bool outbf, int grid_x, int tf, hipStream_t s) {
+    if (wkind == kWBF16)
+        return outbf ? launch_cfg<MODE, kWBF16, true>(a, grid_x, tf, s) : launch_cfg<MODE, kWBF16, false>(a, grid_x, tf, s);
+    if (wkind == kWU4)
+        return outbf ? launch_cfg<MODE, kWU4, true>(a, grid_x, tf, s) : launch_cfg<MODE, kWU4, false>(a, grid_x, tf, s);
+    return launch_cfg<MODE, kWF32, false>(a, grid_x, tf, s);
+}
+
+hipError_t launch_gemm(int mode, int wkind, bool outbf, const GemmArgs& a, int grid_x, int tf, hipStream_t s) {
+    if (grid_x <= 0) return hipSuccess;
+    switch (mode) {
+        case kRoutedGateUp: return dispatch_wk<kRoutedGateUp>(a, wkind, outbf, grid_x, tf, s);
+        case kRoutedDown: return dispatch_wk<kRoutedDown>(a, wkind, outbf, grid_x, tf, s);
+        case kDenseGateUp: return dispatch_wk<kDenseGateUp>(a, wkind, outbf, grid_x, tf, s);
+        case kDenseDown: return dispatch_wk<kDenseDown>(a, wkind, outbf, grid_x, tf, s);
+        default:
+            // router logits: bf16 or fp32 weights, fp32 output
+            return dispatch_wk<kDenseStore>(a, wkind == kWF32 ? kWF32 : kWBF16, false, grid_x, tf, s);
+    }
+}
+
+}  // namespace moe
