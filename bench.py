@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Throughput of one sparse-MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one whole layer forward (routing, permute, routed gate/up +
+SwiGLU, routed down x alpha, shared expert, combine + residual) over one
+batch of T tokens, launched as one captured HIP graph of the library's
+moe_layer_forward.  Steps rotate over L layer instances that are distinct
+device copies of the seeded weights, each with its own seeded tokens (so
+the routing differs per instance and no instance's weights stay cached in
+the 256 MB last-level cache).  Inputs are resident in HBM before the timed
+region, which is bracketed by device synchronisation and HIP events.
+
+Prints one JSON line: tokens/s of the Qwen3.6-35B-A3B layer at decode shape
+(T = 8), the roofline of its dominant kernel (routed gate/up GEMM, timed
+alone with HIP events over re-launches of that stage on the same routing),
+the fp64 oracle timed on the host cores on a bounded sample, and the
+T = 4096 skewed prefill layer as a secondary entry.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from synth import WORKLOADS, make_tokens, make_weights  # noqa: E402
+from top_routing_grouped_amd import moe  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "MoE layer tokens/s, Qwen3.6 shape at T=8 and T=4096; % of HBM / MFMA roofline"
+BYTES_PER_PARAM = {"f32": 4.0, "bf16": 2.0, "u4": 0.5 + 4.0 / 64}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def clone_weights(w):
+    import copy
+    c = copy.copy(w)
+    c.router = w.router.clone()
+    c.expert_bias = None if w.expert_bias is None else w.expert_bias.clone()
+    for name in ("gate", "up", "down", "shared_gate", "shared_up", "shared_down"):
+        m = getattr(w, name)
+        if m is not None:
+            mm = copy.copy(m)
+            mm.w = m.w.clone()
+            mm.scale = None if m.scale is None else m.scale.clone()
+            mm.min = None if m.min is None else m.min.clone()
+            setattr(c, name, mm)
+    c.shared_gate_vec = None if w.shared_gate_vec is None else w.shared_gate_vec.clone()
+    return c
+
+
+class Instance:
+    def __init__(self, spec, w, seed):
+        self.spec = spec
+        self.w = w
+        self.ws_struct = moe.weights_struct(w)
+        self.x, self.r = make_tokens(spec, "cuda", seed=seed)
+        self.cfg = moe.config_from_spec(spec)
+        self.ws = moe.alloc_workspace(self.cfg)
+        self.out = torch.empty_like(self.r)
+        self.ids = torch.empty(spec.n_tokens, spec.top_k, dtype=torch.int32, device="cuda")
+        self.wts = torch.empty(spec.n_tokens, spec.top_k, dtype=torch.float32, device="cuda")
+        self.graph = None
+
+    def forward(self, aux):
+        moe.layer_forward(self.cfg, self.ws_struct, self.x, self.r, self.out, self.ids, self.wts, self.ws,
+                          aux_stream=aux)
+
+    def stage(self, stage):
+        moe.layer_stage(self.cfg, self.ws_struct, self.x, self.wts, stage, self.ws)
+
+    def n_active(self):
+        return int(np.unique(self.ids.cpu().numpy()).size)
+
+
+def layer_bytes(spec, n_active):
+    T, D, E, F, Fs = spec.n_tokens, spec.d_model, spec.n_experts, spec.d_ff, spec.d_ff_shared
+    bw = BYTES_PER_PARAM[spec.expert_dtype]
+    br = 4.0 if spec.router_dtype == "f32" else 2.0
+    bx = 4.0 if spec.act_dtype == "f32" else 2.0
+    gate_vec = D * br if spec.shared_gate and Fs else 0
+    return E * D * br + n_active * 3 * D * F * bw + 3 * D * Fs * bw + gate_vec + T * D * bx + 2 * T * D * 4
+
+
+def layer_flops(spec):
+    T, D, E, K, F, Fs = spec.n_tokens, spec.d_model, spec.n_experts, spec.top_k, spec.d_ff, spec.d_ff_shared
+    return 2.0 * T * (E * D + K * 3 * D * F + 3 * D * Fs + (D if spec.shared_gate and Fs else 0))
+
+
+def gateup_bytes(spec, n_active):
+    """Algorithmic bytes of one routed gate/up launch: the active experts' gate
+    and up matrices read once, the token rows read, the bf16 SwiGLU rows written."""
+    T, D, K, F = spec.n_tokens, spec.d_model, spec.top_k, spec.d_ff
+    bw = BYTES_PER_PARAM[spec.expert_dtype]
+    return n_active * 2 * D * F * bw + T * D * 2 + T * K * F * 2
+
+
+def gateup_flops(spec):
+    return 2.0 * spec.n_tokens * spec.top_k * 2 * spec.d_model * spec.d_ff
+
+
+def build_instances(spec, L, log_prefix):
+    t0 = time.time()
+    base = make_weights(spec, "cuda")
+    ws = [base] + [clone_weights(base) for _ in range(L - 1)]
+    torch.cuda.synchronize()
+    tok_seed = 1000 * spec.workload_id + spec.n_tokens
+    insts = [Instance(spec, w, tok_seed + 7919 * i) for i, w in enumerate(ws)]
+    log(f"{log_prefix}: {L} instances built in {time.time() - t0:.1f}s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB on device)")
+    return insts
+
+
+def time_layer(insts, steps, warmup):
+    aux = torch.cuda.Stream()
+    # eager warm-up (creates the library's fork/join events), then capture
+    for inst in insts:
+        inst.forward(aux)
+    torch.cuda.synchronize()
+    ref_out = insts[0].out.clone()
+    cap = torch.cuda.Stream()
+    for inst in insts:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            inst.forward(aux)
+        inst.graph = g
+    torch.cuda.synchronize()
+    # the captured forward must reproduce the eager result bit for bit, replay after replay
+    for _ in range(3):
+        insts[0].out.fill_(float("nan"))
+        insts[0].graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(insts[0].out.view(torch.int32), ref_out.view(torch.int32)):
+            raise RuntimeError("graph replay differs from the eager forward")
+    L = len(insts)
+    for i in range(warmup):
+        insts[i % L].graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        insts[i % L].graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def time_stage(insts, stage, reps):
+    """Average duration of one stage launch, re-launched `reps` times in one
+    captured graph over the instances' real routing; HIP events on the
+    replay stream."""
+    L = len(insts)
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for i in range(reps):
+            insts[i % L].stage(stage)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "top_routing_grouped_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel_key, workload, launch_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this kernel and workload, if it was taken from the current sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        recs = json.load(f)
+    rec = recs.get(f"{kernel_key}/{workload}")
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inst, seconds):
+    """The fp64 oracle (as it stands) on the host cores: full layer over
+    instance 0's tokens, repeated for about `seconds`."""
+    from oracle import moe_oracle as O
+    from oracle.inputs import banks_from, widen_tensor
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    spec = inst.spec
+    host_w = clone_weights_to_host(inst.w)
+    banks = banks_from(host_w, lazy=True)
+    x64, r64 = widen_tensor(inst.x), widen_tensor(inst.r)
+    wr = widen_tensor(host_w.router)
+    bias = None if host_w.expert_bias is None else widen_tensor(host_w.expert_bias)
+    reps, t0 = 0, time.time()
+    while True:
+        O.layer_forward(x64, r64, wr, banks, spec.family, spec.top_k, bias, spec.n_group, spec.topk_group,
+                        spec.routed_scaling)
+        reps += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = time.time() - t0
+    return {"value": reps * spec.n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} full layer forwards of the same workload (T={spec.n_tokens}) in float64 NumPy, "
+                      f"{dt:.1f} s wall clock; weights widened from bf16 per expert inside each call"}
+
+
+def clone_weights_to_host(w):
+    import copy
+    c = copy.copy(w)
+    c.router = w.router.cpu()
+    c.expert_bias = None if w.expert_bias is None else w.expert_bias.cpu()
+    for name in ("gate", "up", "down", "shared_gate", "shared_up", "shared_down"):
+        m = getattr(w, name)
+        if m is not None:
+            mm = copy.copy(m)
+            mm.w = m.w.cpu()
+            mm.scale = None if m.scale is None else m.scale.cpu()
+            mm.min = None if m.min is None else m.min.cpu()
+            setattr(c, name, mm)
+    c.shared_gate_vec = None if w.shared_gate_vec is None else w.shared_gate_vec.cpu()
+    return c
+
+
+def run_workload(name, T, L, steps, warmup, stage_reps):
+    spec = WORKLOADS[name].with_tokens(T)
+    insts = build_instances(spec, L, f"{name} T={T}")
+    ms = time_layer(insts, steps, warmup)
+    n_act = [inst.n_active() for inst in insts]
+    mean_act = float(np.mean(n_act))
+    byts = float(np.mean([layer_bytes(spec, a) for a in n_act]))
+    flops = layer_flops(spec)
+    t = ms / 1e3
+    stage_ms = time_stage(insts, moe.STAGE_GATE_UP, stage_reps)
+    gu_bytes = float(np.mean([gateup_bytes(spec, a) for a in n_act]))
+    gu_flops = gateup_flops(spec)
+    gu_t = stage_ms / 1e3
+    res = {
+        "spec": spec, "insts": insts, "ms_per_step": ms, "tokens_per_s": T / t,
+        "n_active_mean": mean_act, "layer_bytes": byts, "layer_flops": flops,
+        "layer_hbm_frac": byts / t / (HBM_PEAK_GBS * 1e9), "layer_mfma_frac": flops / t / (BF16_PEAK_TFLOPS * 1e12),
+        "gateup_ms": stage_ms, "gateup_bytes": gu_bytes, "gateup_flops": gu_flops,
+        "gateup_gbs": gu_bytes / gu_t / 1e9, "gateup_tflops": gu_flops / gu_t / 1e12,
+    }
+    log(f"{name} T={T}: {ms * 1e3:.1f} us/layer, {T / t:,.0f} tok/s, n_active {mean_act:.1f}, "
+        f"layer {byts / t / 1e9:,.0f} GB/s ({res['layer_hbm_frac']:.1%} HBM), "
+        f"{flops / t / 1e12:.1f} TFLOP/s ({res['layer_mfma_frac']:.1%} MFMA); gate/up {stage_ms * 1e3:.1f} us = "
+        f"{res['gateup_gbs']:,.0f} GB/s, {res['gateup_tflops']:.1f} TFLOP/s")
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--instances", type=int, default=16)
+    ap.add_argument("--stage-reps", type=int, default=64)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    moe.lib()
+
+    dec = run_workload("qwen_decode", 8, args.instances, args.steps, args.warmup, args.stage_reps)
+    spec = dec["spec"]
+    gu_traffic = traffic_record("gateup", "qwen_decode_T8", dec["gateup_bytes"])
+    line = {
+        "metric": METRIC,
+        "value": round(dec["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3.6-35B-A3B MoE layer forward, decode shape",
+                   "n_tokens": 8, "d_model": spec.d_model, "n_experts": spec.n_experts, "top_k": spec.top_k,
+                   "d_ff": spec.d_ff, "d_ff_shared": spec.d_ff_shared, "routing": "softmax top-k, 2^-14 clamp",
+                   "shared_gate": True, "layer_instances": args.instances,
+                   "n_active_mean": round(dec["n_active_mean"], 2),
+                   "layer_algorithmic_bytes": round(dec["layer_bytes"]),
+                   "layer_hbm_frac": round(dec["layer_hbm_frac"], 4)},
+        "roofline": {"kernel": "routed gate/up GEMM + SwiGLU", "bound": "hbm",
+                     "achieved": round(dec["gateup_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec["gateup_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": gu_traffic, "launch_us": round(dec["gateup_ms"] * 1e3, 3),
+                     "algorithmic_bytes": round(dec["gateup_bytes"])},
+    }
+    if not args.no_prefill:
+        pre = run_workload("qwen_prefill_skew", 4096, 4, max(4, args.steps // 40), max(2, args.warmup // 10),
+                           max(8, args.stage_reps // 4))
+        line["secondary"] = {
+            "workload": "Qwen3.6-35B-A3B MoE layer forward, prefill T=4096, skewed routing",
+            "value": round(pre["tokens_per_s"], 1), "unit": "tokens/s",
+            "ms_per_step": round(pre["ms_per_step"], 6), "n_active_mean": round(pre["n_active_mean"], 2),
+            "layer_mfma_frac": round(pre["layer_mfma_frac"], 4), "layer_hbm_frac": round(pre["layer_hbm_frac"], 4),
+            "roofline": {"kernel": "routed gate/up GEMM + SwiGLU", "bound": "mfma",
+                         "achieved": round(pre["gateup_tflops"], 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(pre["gateup_tflops"] / BF16_PEAK_TFLOPS, 4),
+                         "hbm_gbs": round(pre["gateup_gbs"], 1), "launch_us": round(pre["gateup_ms"] * 1e3, 2),
+                         "traffic": traffic_record("gateup", "qwen_prefill_T4096", pre["gateup_bytes"])},
+        }
+        del pre
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(dec["insts"][0], args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -178,6 +178,24 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
                              float* topk_weights_out, void* ws, size_t ws_bytes,
                              moe_stream_t stream, moe_stream_t aux_stream);
 
+/* Stages of moe_layer_forward that moe_layer_stage can re-launch. */
+typedef enum {
+    MOE_STAGE_ROUTER_LOGITS = 0, /* router GEMM: x [T,D] -> fp32 logits in ws */
+    MOE_STAGE_GATE_UP = 1,       /* routed gate/up GEMM + SwiGLU -> h in ws */
+    MOE_STAGE_DOWN = 2           /* routed down GEMM x alpha -> staged slot rows in ws */
+} moe_stage;
+
+/* Measurement aid: re-launches one kernel stage of the last
+ * moe_layer_forward that ran with this cfg, weights, x and ws, reading the
+ * stage's inputs from the workspace (routing, permutation, tile list, h) and
+ * rewriting the same workspace outputs, so the stage can be timed alone on
+ * the real routing of that call.  topk_weights is the buffer the forward
+ * received as topk_weights_out (NULL if it received NULL).  It has no effect
+ * on the caller's out/residual. */
+moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, const void* x,
+                           const float* topk_weights, moe_stage stage, void* ws, size_t ws_bytes,
+                           moe_stream_t stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 

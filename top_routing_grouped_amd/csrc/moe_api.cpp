@@ -156,43 +156,61 @@ template <class T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
 // ---- stages (arguments already validated)
-moe_status stage_route(const moe_config& c, const Layout& L, void* ws, const void* x, const void* router,
-                       const float* bias, int32_t* ids, float* wts, hipStream_t s) {
+moe_status stage_logits(const moe_config& c, const Layout& L, void* ws, const void* x, const void* router,
+                        hipStream_t s) {
     const int T = c.n_tokens;
-    moe::GemmArgs a{};
     moe_matrix rm{router, nullptr, nullptr};
-    a = gemm_args(rm, nullptr, c.n_experts, c.d_model, 1);
+    moe::GemmArgs a = gemm_args(rm, nullptr, c.n_experts, c.d_model, 1);
     a.act = x; a.n_act_rows = T; a.n_rows = T;
     a.out = at<float>(ws, L.logits);
     const int tf = dense_tf(c);
     HIP_TRY(moe::launch_gemm(moe::kDenseStore, c.router_dtype == MOE_F32 ? moe::kWF32 : moe::kWBF16, false, a,
                              (T + 16 * tf - 1) / (16 * tf), tf, s));
+    return MOE_OK;
+}
+
+moe_status stage_route(const moe_config& c, const Layout& L, void* ws, const void* x, const void* router,
+                       const float* bias, int32_t* ids, float* wts, hipStream_t s) {
+    const int T = c.n_tokens;
+    if (moe_status st = stage_logits(c, L, ws, x, router, s)) return st;
     HIP_TRY(moe::launch_route_select(at<float>(ws, L.logits), T, c.n_experts, c.top_k, int(c.family), c.n_group,
                                      c.topk_group, c.routed_scaling,
                                      c.family == MOE_ROUTE_SIGMOID_GROUP_TOPK ? bias : nullptr, ids, wts, s));
     return MOE_OK;
 }
 
-moe_status stage_experts(const moe_config& c, const Layout& L, void* ws, const void* x, const moe_weights& w,
-                         const int32_t* pairs, const int4* tiles, const int32_t* n_tiles, const float* wts,
-                         void* slot_out, bool slot_bf16, hipStream_t s) {
+moe_status stage_gateup(const moe_config& c, const Layout& L, void* ws, const void* x, const moe_weights& w,
+                        const int32_t* pairs, const int4* tiles, const int32_t* n_tiles, hipStream_t s) {
     const int T = c.n_tokens, K = c.top_k, TK = T * K;
     const int tf = routed_tf(c);
     const int grid = int(max_tiles(TK, c.n_experts, 16 * tf));
-    const int wk = wkind_of(c.expert_dtype);
-    const bool hbf = c.expert_dtype != MOE_F32;
-    void* h = at<void>(ws, L.h);
     moe::GemmArgs a = gemm_args(w.gate, &w.up, c.d_ff, c.d_model, c.n_experts);
     a.act = x; a.n_act_rows = T;
     a.tiles = tiles; a.n_tiles = n_tiles; a.pairs = pairs; a.n_pairs = TK; a.topk = K;
-    a.out = h;
-    HIP_TRY(moe::launch_gemm(moe::kRoutedGateUp, wk, hbf, a, grid, tf, s));
+    a.out = at<void>(ws, L.h);
+    HIP_TRY(moe::launch_gemm(moe::kRoutedGateUp, wkind_of(c.expert_dtype), c.expert_dtype != MOE_F32, a, grid, tf, s));
+    return MOE_OK;
+}
+
+moe_status stage_down(const moe_config& c, const Layout& L, void* ws, const moe_weights& w, const int32_t* pairs,
+                      const int4* tiles, const int32_t* n_tiles, const float* wts, void* slot_out, bool slot_bf16,
+                      hipStream_t s) {
+    const int T = c.n_tokens, K = c.top_k, TK = T * K;
+    const int tf = routed_tf(c);
+    const int grid = int(max_tiles(TK, c.n_experts, 16 * tf));
     moe::GemmArgs d = gemm_args(w.down, nullptr, c.d_model, c.d_ff, c.n_experts);
-    d.act = h; d.n_act_rows = TK;
+    d.act = at<void>(ws, L.h); d.n_act_rows = TK;
     d.tiles = tiles; d.n_tiles = n_tiles; d.pairs = pairs; d.n_pairs = TK; d.topk = K;
     d.out = slot_out; d.row_scale = wts;
-    HIP_TRY(moe::launch_gemm(moe::kRoutedDown, wk, slot_bf16, d, grid, tf, s));
+    HIP_TRY(moe::launch_gemm(moe::kRoutedDown, wkind_of(c.expert_dtype), slot_bf16, d, grid, tf, s));
     return MOE_OK;
+}
+
+moe_status stage_experts(const moe_config& c, const Layout& L, void* ws, const void* x, const moe_weights& w,
+                         const int32_t* pairs, const int4* tiles, const int32_t* n_tiles, const float* wts,
+                         void* slot_out, bool slot_bf16, hipStream_t s) {
+    if (moe_status st = stage_gateup(c, L, ws, x, w, pairs, tiles, n_tiles, s)) return st;
+    return stage_down(c, L, ws, w, pairs, tiles, n_tiles, wts, slot_out, slot_bf16, s);
 }
 
 moe_status stage_shared(const moe_config& c, const Layout& L, void* ws, const void* x, const moe_weights& w,
@@ -377,6 +395,31 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
     if (fork) HIP_TRY(hipStreamWaitEvent(stream, ev_join, 0));
     HIP_TRY(moe::launch_combine(slots, slot_bf16, ys, residual, out, c.n_tokens, c.top_k, c.d_model, stream));
     return MOE_OK;
+}
+
+moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, const void* x,
+                           const float* topk_weights, moe_stage stage, void* ws, size_t ws_bytes,
+                           moe_stream_t stream) {
+    g_err[0] = 0;
+    if (moe_status st = check_config(cfg)) return st;
+    if (cfg->n_tokens == 0) return MOE_OK;
+    if (!x || !weights || !weights->router) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (moe_status st = check_weights(*cfg, weights, true, false)) return st;
+    if (moe_status st = check_ws(*cfg, ws, ws_bytes)) return st;
+    (void)hipGetLastError();
+    const moe_config& c = *cfg;
+    const Layout L = layout(c);
+    int32_t* pairs = at<int32_t>(ws, L.pairs);
+    int4* tiles = at<int4>(ws, L.tiles);
+    int32_t* nt = at<int32_t>(ws, L.n_tiles);
+    switch (stage) {
+        case MOE_STAGE_ROUTER_LOGITS: return stage_logits(c, L, ws, x, weights->router, stream);
+        case MOE_STAGE_GATE_UP: return stage_gateup(c, L, ws, x, *weights, pairs, tiles, nt, stream);
+        case MOE_STAGE_DOWN:
+            return stage_down(c, L, ws, *weights, pairs, tiles, nt, topk_weights ? topk_weights : at<float>(ws, L.wts),
+                              at<void>(ws, L.slots), c.expert_dtype != MOE_F32, stream);
+    }
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown stage %d", int(stage));
 }
 
 }  // extern "C"

@@ -29,7 +29,8 @@ _FAM = {"softmax": SOFTMAX_TOPK, "sigmoid_group": SIGMOID_GROUP_TOPK}
 
 # Entry points the header declares (checked by the CPU tests).
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_experts", "moe_shared_expert",
-           "moe_combine", "moe_layer_forward", "moe_status_string", "moe_last_error")
+           "moe_combine", "moe_layer_forward", "moe_layer_stage", "moe_status_string", "moe_last_error")
+STAGE_ROUTER_LOGITS, STAGE_GATE_UP, STAGE_DOWN = 0, 1, 2
 
 
 class MoeConfig(ctypes.Structure):
@@ -77,6 +78,7 @@ def lib() -> ctypes.CDLL:
             "moe_shared_expert": [cfg, P, wts, P, P, S, P],
             "moe_combine": [cfg, P, P, P, P, P],
             "moe_layer_forward": [cfg, wts, P, P, P, P, P, P, S, P, P],
+            "moe_layer_stage": [cfg, wts, P, P, I32, P, S, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -178,3 +180,9 @@ def layer_forward(cfg, wstruct: MoeWeights, x, residual, out, ids_out=None, weig
                                    _ptr(ids_out), _ptr(weights_out), _ptr(ws), 0 if ws is None else ws.numel(),
                                    _stream(stream), None if aux_stream is None else _stream(aux_stream)),
            "moe_layer_forward")
+
+
+def layer_stage(cfg, wstruct: MoeWeights, x, topk_weights, stage: int, ws, stream=None):
+    """Re-launch one kernel stage of the last layer_forward on `ws` (measurement aid)."""
+    _check(lib().moe_layer_stage(ctypes.byref(cfg), ctypes.byref(wstruct), _ptr(x), _ptr(topk_weights), stage,
+                                 _ptr(ws), ws.numel(), _stream(stream)), "moe_layer_stage")
