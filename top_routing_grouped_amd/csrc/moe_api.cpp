@@ -10,10 +10,8 @@
 
 #include "../../include/moe.h"
 #include "moe_kernels.h"
+#include "moe_select.h"
 
-namespace moe {
-size_t permute_smem_bytes(int E);
-}
 
 namespace {
 
@@ -48,6 +46,13 @@ int routed_tf(const moe_config& c) {
 }
 int dense_tf(const moe_config& c) { return c.n_tokens >= 64 ? 4 : 1; }
 
+// Router logits: K split over workgroups for small T (each wave one chunk).
+int router_ksplit(const moe_config& c) {
+    if (c.n_tokens > 64) return 1;
+    const int per = 4 * kspan_of(c.router_dtype == MOE_F32 ? MOE_F32 : MOE_BF16);
+    return std::max(1, std::min(c.d_model / per, 8));
+}
+
 int64_t max_tiles(int64_t n_pairs, int E, int tile_rows) {
     const int64_t act = std::min<int64_t>(E, n_pairs);
     return (n_pairs + act * (tile_rows - 1)) / tile_rows;
@@ -69,7 +74,7 @@ Layout layout(const moe_config& c) {
         o += align256(bytes);
         return at;
     };
-    L.logits = take(T * E * 4);
+    L.logits = take(size_t(router_ksplit(c)) * T * E * 4);
     L.gate_logit = take(T * 4);
     L.ids = take(TK * 4);
     L.wts = take(TK * 4);
@@ -163,19 +168,42 @@ moe_status stage_logits(const moe_config& c, const Layout& L, void* ws, const vo
     moe::GemmArgs a = gemm_args(rm, nullptr, c.n_experts, c.d_model, 1);
     a.act = x; a.n_act_rows = T; a.n_rows = T;
     a.out = at<float>(ws, L.logits);
+    a.ksplit = router_ksplit(c);
     const int tf = dense_tf(c);
     HIP_TRY(moe::launch_gemm(moe::kDenseStore, c.router_dtype == MOE_F32 ? moe::kWF32 : moe::kWBF16, false, a,
                              (T + 16 * tf - 1) / (16 * tf), tf, s));
     return MOE_OK;
 }
 
+moe::SelParams sel_params(const moe_config& c, const Layout& L, void* ws, const float* bias) {
+    moe::SelParams P{};
+    P.logits = at<float>(ws, L.logits);
+    P.ksplit = router_ksplit(c);
+    P.T = c.n_tokens; P.E = c.n_experts; P.K = c.top_k;
+    P.family = int(c.family);
+    P.G = c.n_group; P.TG = c.topk_group; P.scaling = c.routed_scaling;
+    P.bias = c.family == MOE_ROUTE_SIGMOID_GROUP_TOPK ? bias : nullptr;
+    return P;
+}
+
+moe::PermParams perm_params(const moe_config& c, const int32_t* ids, int32_t* offsets, int32_t* active,
+                            int32_t* n_active, int32_t* sorted_pairs, int4* tiles, int32_t* n_tiles, int tile_rows) {
+    moe::PermParams Q{};
+    Q.ids = ids;
+    Q.n_pairs = c.n_tokens * c.top_k;
+    Q.E = c.n_experts;
+    Q.id_bits = moe::id_bits_for(c.n_experts);
+    Q.offsets = offsets; Q.active = active; Q.n_active = n_active; Q.sorted_pairs = sorted_pairs;
+    Q.tiles = tiles; Q.n_tiles = n_tiles;
+    Q.tile_rows = tile_rows;
+    Q.max_tiles = moe::max_tiles_for(Q.n_pairs, c.n_experts, tile_rows);
+    return Q;
+}
+
 moe_status stage_route(const moe_config& c, const Layout& L, void* ws, const void* x, const void* router,
                        const float* bias, int32_t* ids, float* wts, hipStream_t s) {
-    const int T = c.n_tokens;
     if (moe_status st = stage_logits(c, L, ws, x, router, s)) return st;
-    HIP_TRY(moe::launch_route_select(at<float>(ws, L.logits), T, c.n_experts, c.top_k, int(c.family), c.n_group,
-                                     c.topk_group, c.routed_scaling,
-                                     c.family == MOE_ROUTE_SIGMOID_GROUP_TOPK ? bias : nullptr, ids, wts, s));
+    HIP_TRY(moe::launch_route_select(sel_params(c, L, ws, bias), ids, wts, s));
     return MOE_OK;
 }
 
@@ -298,8 +326,9 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* 
     if (!topk_ids || !expert_offsets || !active_experts || !n_active || !sorted_pairs)
         return fail(MOE_ERR_INVALID_ARGUMENT, "NULL tensor argument");
     (void)hipGetLastError();
-    HIP_TRY(moe::launch_permute(topk_ids, cfg->n_tokens * cfg->top_k, cfg->n_experts, expert_offsets, active_experts,
-                                n_active, sorted_pairs, nullptr, nullptr, 16, stream));
+    HIP_TRY(moe::launch_permute(perm_params(*cfg, topk_ids, expert_offsets, active_experts, n_active, sorted_pairs,
+                                            nullptr, nullptr, 16),
+                                stream));
     return MOE_OK;
 }
 
@@ -363,7 +392,6 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
     (void)hipGetLastError();
     const moe_config& c = *cfg;
     const Layout L = layout(c);
-    const int TK = c.n_tokens * c.top_k;
     const bool has_shared = c.d_ff_shared > 0;
     const bool slot_bf16 = c.expert_dtype != MOE_F32;
     float* ys = has_shared ? at<float>(ws, L.ys) : nullptr;
@@ -382,13 +410,19 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
 
     int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
     float* wts = topk_weights_out ? topk_weights_out : at<float>(ws, L.wts);
-    if (moe_status st = stage_route(c, L, ws, x, weights->router, weights->expert_bias, ids, wts, stream)) return st;
     const int tile_rows = 16 * routed_tf(c);
     int32_t* pairs = at<int32_t>(ws, L.pairs);
     int4* tiles = at<int4>(ws, L.tiles);
     int32_t* nt = at<int32_t>(ws, L.n_tiles);
-    HIP_TRY(moe::launch_permute(ids, TK, c.n_experts, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.active),
-                                at<int32_t>(ws, L.n_active), pairs, tiles, nt, tile_rows, stream));
+    const moe::PermParams Q = perm_params(c, ids, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.active),
+                                          at<int32_t>(ws, L.n_active), pairs, tiles, nt, tile_rows);
+    if (moe_status st = stage_logits(c, L, ws, x, weights->router, stream)) return st;
+    if (moe::route_permute_fusable(c.n_tokens, c.n_experts, c.top_k)) {
+        HIP_TRY(moe::launch_route_permute(sel_params(c, L, ws, weights->expert_bias), ids, wts, Q, stream));
+    } else {
+        HIP_TRY(moe::launch_route_select(sel_params(c, L, ws, weights->expert_bias), ids, wts, stream));
+        HIP_TRY(moe::launch_permute(Q, stream));
+    }
     void* slots = at<void>(ws, L.slots);
     if (moe_status st = stage_experts(c, L, ws, x, *weights, pairs, tiles, nt, wts, slots, slot_bf16, stream))
         return st;

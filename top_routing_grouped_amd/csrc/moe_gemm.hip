@@ -14,12 +14,16 @@
 // of the tile and the result for one token sits in 4 consecutive feature
 // rows of a lane (one 8/16-byte store).  Both operands are K-contiguous in
 // memory.  Because any permutation of the reduction index applied to both
-// operands leaves a dot product unchanged, lane-group q of a wave loads one
-// contiguous 64-byte run of K (32 bf16 / 4-bit codes, or 4 fp32) and feeds
-// it to 4 consecutive MFMAs, instead of the 16-byte slices the instruction's
-// own K order would ask for.  Weight rows are streamed straight from HBM into
-// registers (read once per tile); a workgroup's waves split K and reduce
-// their partial sums through LDS in a fixed order.
+// operands leaves a dot product unchanged, the K order inside a chunk of
+// 4 MFMAs is chosen for the load pattern rather than the instruction's own:
+// for bf16, MFMA j of a chunk takes 8-element block (q + 4j) of the chunk in
+// lane-group q, so each 16-byte load instruction of a wave covers 64
+// contiguous bytes of each of its 16 rows; for 4-bit codes (32 weights in 16
+// bytes) and fp32 (4 values in 16 bytes) lane-group q takes one contiguous
+// 16-byte run, which gives the same 64-byte runs per row.  Weight rows are
+// streamed straight from HBM into registers (read once per tile); a
+// workgroup's waves split K and reduce their partial sums through LDS in a
+// fixed order.
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -58,20 +62,30 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// Weight chunk: row pointer already offset to the row; k = element offset.
+// K offset of MFMA j's operand block for lane-group q in the chunk at kc.
+template <int WK>
+__device__ __forceinline__ int kofs(int kc, int q, int j) {
+    if constexpr (WK == kWBF16) return kc + (q + 4 * j) * 8;
+    else return kc + q * WTraits<WK>::KL + j * (WTraits<WK>::KL / 4);
+}
+
+// Weight chunk at chunk base kc for lane-group q (rows: `row` of the bank).
 template <int WK>
 __device__ __forceinline__ void load_w(Frag<WK == kWF32>& f, const void* w, const void* sc, const void* mn,
-                                       size_t row, int K, int k) {
+                                       size_t row, int K, int kc, int q) {
     if constexpr (WK == kWBF16) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(w) + row * K + k);
+        const uint16_t* p = static_cast<const uint16_t*>(w) + row * K;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) f.v[j] = as_bf16x8(__builtin_nontemporal_load(p + j));
+        for (int j = 0; j < 4; ++j) f.v[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(p + kofs<WK>(kc, q, j)));
     } else if constexpr (WK == kWF32) {
+        const int k = kofs<WK>(kc, q, 0);
         const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(w) + row * K + k);
         f.v[0] = v.x; f.v[1] = v.y; f.v[2] = v.z; f.v[3] = v.w;
     } else {  // 4-bit affine, group 64: 32 codes (16 bytes) inside one group
-        const u32x4 c = __builtin_nontemporal_load(
+        const int k = kofs<WK>(kc, q, 0);
+        const u32x4 c = *(
             reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(w) + row * (K / 2) + k / 2));
+
         const size_t g = row * (K / 64) + k / 64;
         const float s = bf16_to_f32(static_cast<const uint16_t*>(sc)[g]);
         const float m = bf16_to_f32(static_cast<const uint16_t*>(mn)[g]);
@@ -90,21 +104,22 @@ __device__ __forceinline__ void load_w(Frag<WK == kWF32>& f, const void* w, cons
     }
 }
 
-// Activation chunk (bf16 or fp32 rows), zeros for an absent token.
-template <bool F32>
-__device__ __forceinline__ void load_x(Frag<F32>& f, const void* rowp, int k) {
-    if constexpr (F32) {
+// Activation chunk (bf16 or fp32 rows) in the weights' K order, zeros for an
+// absent token.
+template <int WK>
+__device__ __forceinline__ void load_x(Frag<WK == kWF32>& f, const void* rowp, int kc, int q) {
+    if constexpr (WK == kWF32) {
         if (rowp) {
-            const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(rowp) + k);
+            const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(rowp) + kofs<WK>(kc, q, 0));
             f.v[0] = v.x; f.v[1] = v.y; f.v[2] = v.z; f.v[3] = v.w;
         } else {
             f.v[0] = f.v[1] = f.v[2] = f.v[3] = 0.f;
         }
     } else {
         if (rowp) {
-            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(rowp) + k);
+            const uint16_t* p = static_cast<const uint16_t*>(rowp);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) f.v[j] = as_bf16x8(p[j]);
+            for (int j = 0; j < 4; ++j) f.v[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(p + kofs<WK>(kc, q, j)));
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) f.v[j] = as_bf16x8(make_uint4(0, 0, 0, 0));
@@ -158,6 +173,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     const int q = lane >> 4;
     const int r = lane & 15;
     const int N = a.N, K = a.K;
+    // dense store may split K over blockIdx.z (partial sums to separate planes)
+    const int ksub = (MODE == kDenseStore) ? K / max(a.ksplit, 1) : K;
+    const int kbase = (MODE == kDenseStore) ? int(blockIdx.z) * ksub : 0;
     const int wrow0 = blockIdx.y * (16 * WN) + 16 * wn;
     const bool rows_ok = wrow0 < N;
 
@@ -190,18 +208,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 
     if (rows_ok) {
         const size_t wrow = size_t(e) * N + wrow0 + r;
-        const int kper = K / WKS;
-        const int kbeg = wk * kper + q * KL;
+        const int kper = ksub / WKS;
+        const int kbeg = kbase + wk * kper;
         const int nchunks = kper / SPAN;
 #pragma unroll 2
         for (int c = 0; c < nchunks; ++c) {
-            const int k = kbeg + c * SPAN;
+            const int kc = kbeg + c * SPAN;
             Frag<F32> wa[NM];
-            load_w<WK>(wa[0], a.w0, a.s0, a.m0, wrow, K, k);
-            if constexpr (DUAL) load_w<WK>(wa[1], a.w1, a.s1, a.m1, wrow, K, k);
+            load_w<WK>(wa[0], a.w0, a.s0, a.m0, wrow, K, kc, q);
+            if constexpr (DUAL) load_w<WK>(wa[1], a.w1, a.s1, a.m1, wrow, K, kc, q);
             Frag<F32> xb[TF];
 #pragma unroll
-            for (int j = 0; j < TF; ++j) load_x<F32>(xb[j], xrow[j], k);
+            for (int j = 0; j < TF; ++j) load_x<WK>(xb[j], xrow[j], kc, q);
 #pragma unroll
             for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -267,7 +285,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         } else {  // kDenseStore
 #pragma unroll
             for (int t = 0; t < 4; ++t) v[t] = acc[0][j][t];
-            dest = size_t(begin + i);
+            dest = size_t(blockIdx.z) * a.n_rows + begin + i;
         }
         if constexpr (OUTBF) {
             uint2 pk = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -282,28 +300,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 // --------------------------------------------------------------- launchers
 template <int MODE, int WK, bool OUTBF>
 static hipError_t launch_cfg(const GemmArgs& a, int grid_x, int tf, hipStream_t s) {
-    // small tiles: 16 tokens, 4 waves split K; larger: 64 tokens.
-    const int K = a.K;
+    // waves split the workgroup's K range 4, 2 or 1 ways (rows 16, 32, 64)
+    const int ks = (MODE == kDenseStore && a.ksplit > 1) ? a.ksplit : 1;
+    const int kwg = a.K / ks;
     constexpr int SPAN = 4 * WTraits<WK>::KL;
-    const bool ksplit4 = (K % (4 * SPAN) == 0);
-    const bool ksplit2 = (K % (2 * SPAN) == 0);
+    const bool ksplit4 = (kwg % (4 * SPAN) == 0);
+    const bool ksplit2 = (kwg % (2 * SPAN) == 0);
     if (tf == 1) {
         if (ksplit4) {
-            dim3 g(grid_x, (a.N + 15) / 16);
+            dim3 g(grid_x, (a.N + 15) / 16, ks);
             gemm_kernel<MODE, WK, OUTBF, 1, 1, 4><<<g, 256, 0, s>>>(a);
         } else if (ksplit2) {
-            dim3 g(grid_x, (a.N + 31) / 32);
+            dim3 g(grid_x, (a.N + 31) / 32, ks);
             gemm_kernel<MODE, WK, OUTBF, 1, 2, 2><<<g, 256, 0, s>>>(a);
         } else {
-            dim3 g(grid_x, (a.N + 63) / 64);
+            dim3 g(grid_x, (a.N + 63) / 64, ks);
             gemm_kernel<MODE, WK, OUTBF, 1, 4, 1><<<g, 256, 0, s>>>(a);
         }
     } else {
         if (ksplit4) {
-            dim3 g(grid_x, (a.N + 15) / 16);
+            dim3 g(grid_x, (a.N + 15) / 16, ks);
             gemm_kernel<MODE, WK, OUTBF, 4, 1, 4><<<g, 256, 0, s>>>(a);
         } else {
-            dim3 g(grid_x, (a.N + 63) / 64);
+            dim3 g(grid_x, (a.N + 63) / 64, ks);
             gemm_kernel<MODE, WK, OUTBF, 4, 4, 1><<<g, 256, 0, s>>>(a);
         }
     }

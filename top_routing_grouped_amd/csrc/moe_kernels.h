@@ -36,22 +36,26 @@ struct GemmArgs {
     const int* pairs;   // routed modes: sorted flat pair ids
     int n_pairs;        // T*K
     int topk;
-    void* out;              // [rows][N] fp32 or bf16
+    void* out;              // [rows][N] fp32 or bf16 (dense store: [ksplit][rows][N])
     const float* row_scale; // routed down: weights[pair]; dense down: gate logits or null
+    int ksplit;             // dense store only: K split across blockIdx.z (partial sums)
 };
 
 hipError_t launch_gemm(int mode, int wkind, bool outbf, const GemmArgs& a, int grid_x, int tf, hipStream_t s);
 
-// routing
-hipError_t launch_route_select(const float* logits, int T, int E, int K, int family, int n_group, int topk_group,
-                               float routed_scaling, const float* bias, int32_t* ids, float* weights,
-                               hipStream_t s);
+// routing (parameter blocks in moe_select.h)
+struct SelParams;
+struct PermParams;
+hipError_t launch_route_select(const SelParams& P, int32_t* ids, float* weights, hipStream_t s);
+bool route_permute_fusable(int T, int E, int K);
+hipError_t launch_route_permute(const SelParams& P, int32_t* ids, float* weights, const PermParams& Q,
+                                hipStream_t s);
 hipError_t launch_gate_logit(const void* x, bool x_f32, const void* wvec, int T, int D, float* out, hipStream_t s);
 
-// permute; tiles may be null.  tile_rows = rows per GEMM tile.
-hipError_t launch_permute(const int32_t* ids, int n_pairs, int E, int32_t* offsets, int32_t* active,
-                          int32_t* n_active, int32_t* sorted_pairs, int4* tiles, int32_t* n_tiles,
-                          int tile_rows, hipStream_t s);
+// permute (tiles may be null)
+hipError_t launch_permute(const PermParams& P, hipStream_t s);
+int id_bits_for(int E);
+int max_tiles_for(int n_pairs, int E, int tile_rows);
 hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* active, const int32_t* n_active, int E,
                               int n_pairs, int4* tiles, int32_t* n_tiles, int max_tiles, int tile_rows,
                               hipStream_t s);

@@ -14,143 +14,30 @@
 //   out = residual + (sum_{k ascending} slot[t, k, :] + shared[t, :]).
 #include "moe_device.h"
 #include "moe_kernels.h"
+#include "moe_select.h"
 
 namespace moe {
 
-constexpr int kPermThreads = 1024;
-constexpr int kPermWaves = kPermThreads / 64;
-
-// Exclusive scan over the 1024 threads of the block.  `sh` holds >= 16 ints.
-__device__ int block_exclusive_scan(int v, int* total, int* sh) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int inc = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += o;
-    }
-    if (lane == 63) sh[wave] = inc;
-    __syncthreads();
-    if (wave == 0) {
-        int w = lane < kPermWaves ? sh[lane] : 0;
-#pragma unroll
-        for (int d = 1; d < kPermWaves; d <<= 1) {
-            const int o = __shfl_up(w, d, 64);
-            if (lane >= d) w += o;
-        }
-        if (lane < kPermWaves) sh[lane] = w;
-    }
-    __syncthreads();
-    const int excl = (wave > 0 ? sh[wave - 1] : 0) + inc - v;
-    *total = sh[kPermWaves - 1];
-    __syncthreads();
-    return excl;
-}
-
-// Writes the GEMM tiles of expert e (rows [begin, begin+cnt)) starting at
-// tile index `start`; returns nothing.  Tiles past max_tiles are dropped.
-__device__ void write_tiles(int4* tiles, int start, int e, int begin, int cnt, int tile_rows, int max_tiles) {
-    for (int j = 0, r = 0; r < cnt; ++j, r += tile_rows) {
-        const int ti = start + j;
-        if (ti >= max_tiles) break;
-        tiles[ti] = make_int4(e, begin + r, min(tile_rows, cnt - r), 0);
-    }
-}
-
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ ids, int n_pairs, int E,
-                                                               int id_bits, int32_t* __restrict__ offsets,
-                                                               int32_t* __restrict__ active,
-                                                               int32_t* __restrict__ n_active,
-                                                               int32_t* __restrict__ sorted_pairs,
-                                                               int4* __restrict__ tiles, int32_t* __restrict__ n_tiles,
-                                                               int tile_rows, int max_tiles) {
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(PermParams P) {
     extern __shared__ int smem[];
-    int* cnt = smem;             // [E]
-    int* base = cnt + E;         // [E]
-    int* cursor = base + E;      // [E]
-    int* sh = cursor + E;        // [32]
-    uint16_t* wcnt = reinterpret_cast<uint16_t*>(sh + 32);  // [16][E]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    for (int e = tid; e < E; e += kPermThreads) {
-        cnt[e] = 0;
-        cursor[e] = 0;
-    }
-    for (int i = tid; i < kPermWaves * E; i += kPermThreads) wcnt[i] = 0;
-    __syncthreads();
-    for (int p = tid; p < n_pairs; p += kPermThreads) {
-        const int e = ids[p];
-        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-    }
-    __syncthreads();
-
-    // offsets, active list and tile list (E <= 1024: one expert per thread)
-    const int c = tid < E ? cnt[tid] : 0;
-    int total;
-    const int off = block_exclusive_scan(c, &total, sh);
-    int n_act;
-    const int apos = block_exclusive_scan(c > 0 ? 1 : 0, &n_act, sh);
-    const int nt = (c + tile_rows - 1) / tile_rows;
-    int tiles_total;
-    const int tstart = block_exclusive_scan(nt, &tiles_total, sh);
-    if (tid < E) {
-        base[tid] = off;
-        offsets[tid] = off;
-        if (c > 0) {
-            active[apos] = tid;
-            if (tiles) write_tiles(tiles, tstart, tid, off, c, tile_rows, max_tiles);
-        }
-    }
-    if (tid == 0) {
-        offsets[E] = total;
-        *n_active = n_act;
-        if (n_tiles) *n_tiles = min(tiles_total, max_tiles);
-    }
-    __syncthreads();
-
-    // stable scatter, 1024 pairs per round
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int r0 = 0; r0 < n_pairs; r0 += kPermThreads) {
-        const int p = r0 + tid;
-        int e = p < n_pairs ? ids[p] : -1;
-        const bool valid = e >= 0 && e < E;
-        if (!valid) e = 0;
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < id_bits; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t bb = __ballot(bit);
-            peers &= bit ? bb : ~bb;
-        }
-        const int rank = __popcll(peers & lt_mask);
-        const int wc = __popcll(peers);
-        if (valid && rank == 0) wcnt[wave * E + e] = uint16_t(wc);
-        __syncthreads();
-        if (valid) {
-            int before = 0;
-            for (int w = 0; w < wave; ++w) before += wcnt[w * E + e];
-            sorted_pairs[base[e] + cursor[e] + before + rank] = p;
-        }
-        __syncthreads();
-        if (valid && rank == 0) {
-            atomicAdd(&cursor[e], wc);
-            wcnt[wave * E + e] = 0;
-        }
-        __syncthreads();
-    }
+    permute_block(P, smem);
 }
 
-size_t permute_smem_bytes(int E) { return size_t(3 * E + 32) * 4 + size_t(kPermWaves) * E * 2; }
+size_t permute_smem_bytes(int E) { return permute_lds_words(E) * 4; }
 
-hipError_t launch_permute(const int32_t* ids, int n_pairs, int E, int32_t* offsets, int32_t* active,
-                          int32_t* n_active, int32_t* sorted_pairs, int4* tiles, int32_t* n_tiles, int tile_rows,
-                          hipStream_t s) {
-    int bits = 0;
+int id_bits_for(int E) {
+    int bits = 1;
     while ((1 << bits) < E) ++bits;
-    if (bits == 0) bits = 1;
+    return bits;
+}
+
+int max_tiles_for(int n_pairs, int E, int tile_rows) {
     const long long act = E < n_pairs ? E : n_pairs;
-    const long long mt = ((long long)n_pairs + act * (tile_rows - 1)) / tile_rows;
-    permute_kernel<<<1, kPermThreads, permute_smem_bytes(E), s>>>(ids, n_pairs, E, bits, offsets, active, n_active,
-                                                                   sorted_pairs, tiles, n_tiles, tile_rows, int(mt));
+    return int(((long long)n_pairs + act * (tile_rows - 1)) / tile_rows);
+}
+
+hipError_t launch_permute(const PermParams& P, hipStream_t s) {
+    permute_kernel<<<1, kPermThreads, permute_smem_bytes(P.E), s>>>(P);
     return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 // Routing kernels: one wave64 per token selects K experts from the fp32
-// router logits.
+// router logits (selection rules in moe_select.h), and for small token
+// counts a single workgroup that also runs the permute.
 //
 // Softmax family (Treebeard, "How Treebeard routes Qwen3.6 MoE tokens",
 // "Routing math"; edge0 "MoE Routing and Experts", "Softmax top-k"):
@@ -14,167 +15,78 @@
 // Selection is K rounds of a wave-wide maximum over 64-bit keys
 // (score bits << 32 | ~index), which breaks ties toward the lower index and
 // leaves slot k holding the k-th best expert.
-#include <math.h>
-
-#include "moe_device.h"
 #include "moe_kernels.h"
+#include "moe_select.h"
 
 namespace moe {
 
-constexpr float kClamp = 0x1p-14f;  // smallest normal fp16
-
+// One wave per token; blocks of 4 tokens.
 template <int NV>
-__global__ __launch_bounds__(256) void route_softmax_kernel(const float* __restrict__ logits, int T, int E, int K,
-                                                            int32_t* __restrict__ ids, float* __restrict__ wts) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const float* z = logits + size_t(t) * E;
-    float v[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const int e = lane + 64 * j;
-        v[j] = e < E ? z[e] : -INFINITY;
-    }
-    float m = v[0];
-#pragma unroll
-    for (int j = 1; j < NV; ++j) m = fmaxf(m, v[j]);
-    m = wave_max(m);
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-        if (lane + 64 * j < E) s += __expf(v[j] - m);
-    s = wave_sum(s);
-
-    uint32_t taken = 0;
-    int my_id = 0;
-    float my_z = -INFINITY;
-    for (int k = 0; k < K; ++k) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int e = lane + 64 * j;
-            if (e < E && !((taken >> j) & 1u)) {
-                const uint64_t key = sel_key(v[j], e);
-                best = key > best ? key : best;
-            }
-        }
-        best = wave_max_u64(best);
-        const int idx = min(max(key_index(best), 0), E - 1);
-        if ((idx & 63) == lane) taken |= 1u << (idx >> 6);
-        if (lane == k) {
-            my_id = idx;
-            my_z = key_score(best);
-        }
-    }
-    const float p = lane < K ? __expf(my_z - m) / s : 0.f;
-    const float denom = fmaxf(wave_sum(p), kClamp);
-    if (lane < K) {
-        ids[size_t(t) * K + lane] = my_id;
-        wts[size_t(t) * K + lane] = p / denom;
+__global__ __launch_bounds__(256) void route_select_kernel(SelParams P, int32_t* __restrict__ ids,
+                                                           float* __restrict__ wts) {
+    __shared__ float sel_s[4][64 * NV];
+    __shared__ float sig_s[4][64 * NV];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= P.T) return;  // no block-wide barrier below
+    int id;
+    float w;
+    select_token<NV>(P, t, sel_s[wave], sig_s[wave], &id, &w);
+    if (lane < P.K) {
+        ids[size_t(t) * P.K + lane] = id;
+        wts[size_t(t) * P.K + lane] = w;
     }
 }
 
-template <int NV>
-__global__ __launch_bounds__(256) void route_sigmoid_group_kernel(const float* __restrict__ logits, int T, int E,
-                                                                  int K, int G, int TG, float scaling,
-                                                                  const float* __restrict__ bias,
-                                                                  int32_t* __restrict__ ids,
-                                                                  float* __restrict__ wts) {
-    __shared__ float sel_s[4][64 * NV];
-    __shared__ float sig_s[4][64 * NV];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int t = blockIdx.x * 4 + wave;
-    const bool live = t < T;  // every wave reaches the barrier below
-    const int gs = E / G;
+// Small T: every token's selection, then the permute, in one 1024-thread
+// workgroup (16 waves take the tokens in turn; the ids stay in LDS).
+constexpr int kFusedMaxE = 256;
+constexpr int kFusedMaxPairs = 2048;
 
-    float sel[NV];
-    if (live) {
-        const float* z = logits + size_t(t) * E;
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int e = lane + 64 * j;
-            if (e < E) {
-                const float s = sigmoidf_(z[e]);
-                sel[j] = s + (bias ? bias[e] : 0.f);
-                sig_s[wave][e] = s;
-                sel_s[wave][e] = sel[j];
-            } else {
-                sel[j] = -INFINITY;
-            }
+__global__ __launch_bounds__(kPermThreads) void route_permute_kernel(SelParams P, int32_t* __restrict__ ids,
+                                                                     float* __restrict__ wts, PermParams Q) {
+    __shared__ float sel_s[kPermWaves][kFusedMaxE];
+    __shared__ float sig_s[kPermWaves][kFusedMaxE];
+    __shared__ int32_t ids_s[kFusedMaxPairs];
+    __shared__ int perm_lds[permute_lds_words(kFusedMaxE)];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int t = wave; t < P.T; t += kPermWaves) {
+        int id;
+        float w;
+        select_token<4>(P, t, sel_s[wave], sig_s[wave], &id, &w);
+        if (lane < P.K) {
+            ids[size_t(t) * P.K + lane] = id;
+            wts[size_t(t) * P.K + lane] = w;
+            ids_s[t * P.K + lane] = id;
         }
     }
     __syncthreads();
-    if (!live) return;
-
-    // group score: sum of the two best selection scores of the group
-    float gscore = -INFINITY;
-    if (lane < G) {
-        float b1 = -INFINITY, b2 = -INFINITY;
-        for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
-            const float x = sel_s[wave][e];
-            if (x > b1) {
-                b2 = b1;
-                b1 = x;
-            } else if (x > b2) {
-                b2 = x;
-            }
-        }
-        gscore = b1 + b2;
-    }
-    uint64_t kept = 0;
-    for (int g = 0; g < TG; ++g) {
-        uint64_t key = (lane < G && !((kept >> lane) & 1ull)) ? sel_key(gscore, lane) : 0;
-        key = wave_max_u64(key);
-        kept |= 1ull << min(max(key_index(key), 0), G - 1);
-    }
-
-    uint32_t taken = 0;
-    int my_id = 0;
-    for (int k = 0; k < K; ++k) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int e = lane + 64 * j;
-            if (e < E && !((taken >> j) & 1u) && ((kept >> (e / gs)) & 1ull)) {
-                const uint64_t key = sel_key(sel[j], e);
-                best = key > best ? key : best;
-            }
-        }
-        best = wave_max_u64(best);
-        const int idx = min(max(key_index(best), 0), E - 1);
-        if ((idx & 63) == lane) taken |= 1u << (idx >> 6);
-        if (lane == k) my_id = idx;
-    }
-    const float s = lane < K ? sig_s[wave][my_id] : 0.f;
-    const float denom = fmaxf(wave_sum(s), kClamp);
-    if (lane < K) {
-        ids[size_t(t) * K + lane] = my_id;
-        wts[size_t(t) * K + lane] = scaling * s / denom;
-    }
+    Q.ids = ids_s;
+    permute_block(Q, perm_lds);
 }
 
 template <int NV>
-static void launch_nv(const float* logits, int T, int E, int K, int family, int G, int TG, float scaling,
-                      const float* bias, int32_t* ids, float* wts, hipStream_t s) {
-    const int blocks = (T + 3) / 4;
-    if (family == 0)
-        route_softmax_kernel<NV><<<blocks, 256, 0, s>>>(logits, T, E, K, ids, wts);
-    else
-        route_sigmoid_group_kernel<NV><<<blocks, 256, 0, s>>>(logits, T, E, K, G, TG, scaling, bias, ids, wts);
+static void launch_nv(const SelParams& P, int32_t* ids, float* wts, hipStream_t s) {
+    route_select_kernel<NV><<<(P.T + 3) / 4, 256, 0, s>>>(P, ids, wts);
 }
 
-hipError_t launch_route_select(const float* logits, int T, int E, int K, int family, int n_group, int topk_group,
-                               float routed_scaling, const float* bias, int32_t* ids, float* weights,
-                               hipStream_t s) {
-    if (T <= 0) return hipSuccess;
-    const int nv = (E + 63) / 64;
-    if (nv <= 1) launch_nv<1>(logits, T, E, K, family, n_group, topk_group, routed_scaling, bias, ids, weights, s);
-    else if (nv <= 2) launch_nv<2>(logits, T, E, K, family, n_group, topk_group, routed_scaling, bias, ids, weights, s);
-    else if (nv <= 4) launch_nv<4>(logits, T, E, K, family, n_group, topk_group, routed_scaling, bias, ids, weights, s);
-    else if (nv <= 8) launch_nv<8>(logits, T, E, K, family, n_group, topk_group, routed_scaling, bias, ids, weights, s);
-    else launch_nv<16>(logits, T, E, K, family, n_group, topk_group, routed_scaling, bias, ids, weights, s);
+hipError_t launch_route_select(const SelParams& P, int32_t* ids, float* weights, hipStream_t s) {
+    if (P.T <= 0) return hipSuccess;
+    const int nv = (P.E + 63) / 64;
+    if (nv <= 1) launch_nv<1>(P, ids, weights, s);
+    else if (nv <= 2) launch_nv<2>(P, ids, weights, s);
+    else if (nv <= 4) launch_nv<4>(P, ids, weights, s);
+    else if (nv <= 8) launch_nv<8>(P, ids, weights, s);
+    else launch_nv<16>(P, ids, weights, s);
+    return hipGetLastError();
+}
+
+bool route_permute_fusable(int T, int E, int K) { return E <= kFusedMaxE && T * K <= kFusedMaxPairs && T <= 64; }
+
+hipError_t launch_route_permute(const SelParams& P, int32_t* ids, float* weights, const PermParams& Q,
+                                hipStream_t s) {
+    if (P.T <= 0) return hipSuccess;
+    route_permute_kernel<<<1, kPermThreads, 0, s>>>(P, ids, weights, Q);
     return hipGetLastError();
 }
 

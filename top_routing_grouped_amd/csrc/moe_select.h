@@ -1,0 +1,294 @@
+// Device functions shared by the routing kernels: per-token top-K selection
+// (one wave64 per token) and the single-workgroup permute.
+//
+// Selection (Treebeard, "How Treebeard routes Qwen3.6 MoE tokens", "Routing
+// math"; edge0 "MoE Routing and Experts", "Routing families"):
+//   softmax family: p = softmax(z) over all E experts, I = TopK(p, K),
+//     alpha_i = p_i / max(sum_{j in I} p_j, 2^-14).  Softmax is strictly
+//     increasing, so the top-K is taken on the logits.
+//   sigmoid group family: s = sigmoid(z) in fp32, sel = s + expert_bias,
+//     groups of E/n_group contiguous experts scored by the sum of their two
+//     best sel, the best topk_group groups kept, top-K of sel inside them,
+//     alpha = routed_scaling * s_I / max(sum s_I, 2^-14)  (bias excluded).
+// K rounds of a wave-wide maximum over 64-bit keys (score bits << 32 |
+// ~index) break ties toward the lower index and put the k-th best in slot k.
+//
+// Permute (Treebeard, "Intel SYCL path", steps 1-4): count the pairs per
+// expert, offsets by exclusive scan, active-expert list, stable scatter of
+// flat pair ids t*K + k (ballot per id bit finds equal experts inside a
+// wave; earlier waves' counts and a running cursor give the position), and
+// the GEMM tile list over active experts.
+#pragma once
+
+#include <math.h>
+
+#include "moe_device.h"
+
+namespace moe {
+
+constexpr float kClamp = 0x1p-14f;  // smallest normal fp16
+
+// Orders LDS accesses of one wave (lanes of a wave exchange data through LDS).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Logit of expert e for token t: sum of `ksplit` partial sums in fixed order.
+__device__ __forceinline__ float logit_at(const float* __restrict__ z, int ksplit, size_t split_stride, size_t idx) {
+    float v = z[idx];
+    for (int s = 1; s < ksplit; ++s) v += z[idx + s * split_stride];
+    return v;
+}
+
+struct SelParams {
+    const float* logits;  // [ksplit][T][E]
+    int ksplit;
+    int T, E, K;
+    int family;  // 0 softmax, 1 sigmoid group
+    int G, TG;
+    float scaling;
+    const float* bias;
+};
+
+// Selects token t's experts; lane k < K returns slot k in (*id, *w).
+// sel_s/sig_s: this wave's LDS scratch of 64*NV floats each (sigmoid family).
+template <int NV>
+__device__ __forceinline__ void select_token(const SelParams& P, int t, float* sel_s, float* sig_s, int* id_out,
+                                             float* w_out) {
+    const int lane = threadIdx.x & 63;
+    const int E = P.E, K = P.K;
+    const size_t stride = size_t(P.T) * E;
+    const size_t row = size_t(t) * E;
+    float v[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int e = lane + 64 * j;
+        v[j] = e < E ? logit_at(P.logits, P.ksplit, stride, row + e) : -INFINITY;
+    }
+    uint32_t taken = 0;
+    int my_id = 0;
+    if (P.family == 0) {
+        float m = v[0];
+#pragma unroll
+        for (int j = 1; j < NV; ++j) m = fmaxf(m, v[j]);
+        m = wave_max(m);
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+            if (lane + 64 * j < E) s += __expf(v[j] - m);
+        s = wave_sum(s);
+        float my_z = -INFINITY;
+        for (int k = 0; k < K; ++k) {
+            uint64_t best = 0;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const int e = lane + 64 * j;
+                if (e < E && !((taken >> j) & 1u)) {
+                    const uint64_t key = sel_key(v[j], e);
+                    best = key > best ? key : best;
+                }
+            }
+            best = wave_max_u64(best);
+            const int idx = min(max(key_index(best), 0), E - 1);
+            if ((idx & 63) == lane) taken |= 1u << (idx >> 6);
+            if (lane == k) {
+                my_id = idx;
+                my_z = key_score(best);
+            }
+        }
+        const float p = lane < K ? __expf(my_z - m) / s : 0.f;
+        const float denom = fmaxf(wave_sum(p), kClamp);
+        *id_out = my_id;
+        *w_out = p / denom;
+        return;
+    }
+    // sigmoid group top-k
+    const int G = P.G, gs = E / G;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int e = lane + 64 * j;
+        if (e < E) {
+            const float s = sigmoidf_(v[j]);
+            v[j] = s + (P.bias ? P.bias[e] : 0.f);
+            sig_s[e] = s;
+            sel_s[e] = v[j];
+        }
+    }
+    wave_lds_sync();
+    float gscore = -INFINITY;
+    if (lane < G) {
+        float b1 = -INFINITY, b2 = -INFINITY;
+        for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
+            const float x = sel_s[e];
+            if (x > b1) {
+                b2 = b1;
+                b1 = x;
+            } else if (x > b2) {
+                b2 = x;
+            }
+        }
+        gscore = b1 + b2;
+    }
+    uint64_t kept = 0;
+    for (int g = 0; g < P.TG; ++g) {
+        uint64_t key = (lane < G && !((kept >> lane) & 1ull)) ? sel_key(gscore, lane) : 0;
+        key = wave_max_u64(key);
+        kept |= 1ull << min(max(key_index(key), 0), G - 1);
+    }
+    for (int k = 0; k < K; ++k) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int e = lane + 64 * j;
+            if (e < E && !((taken >> j) & 1u) && ((kept >> (e / gs)) & 1ull)) {
+                const uint64_t key = sel_key(v[j], e);
+                best = key > best ? key : best;
+            }
+        }
+        best = wave_max_u64(best);
+        const int idx = min(max(key_index(best), 0), E - 1);
+        if ((idx & 63) == lane) taken |= 1u << (idx >> 6);
+        if (lane == k) my_id = idx;
+    }
+    const float s = lane < K ? sig_s[my_id] : 0.f;
+    const float denom = fmaxf(wave_sum(s), kClamp);
+    *id_out = my_id;
+    *w_out = P.scaling * s / denom;
+    wave_lds_sync();  // sel_s/sig_s are reused by the wave's next token
+}
+
+// ------------------------------------------------------------------ permute
+constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / 64;
+
+// Exclusive scan over the 1024 threads of the block.  `sh` holds >= 16 ints.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* sh) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += o;
+    }
+    if (lane == 63) sh[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        int w = lane < kPermWaves ? sh[lane] : 0;
+#pragma unroll
+        for (int d = 1; d < kPermWaves; d <<= 1) {
+            const int o = __shfl_up(w, d, 64);
+            if (lane >= d) w += o;
+        }
+        if (lane < kPermWaves) sh[lane] = w;
+    }
+    __syncthreads();
+    const int excl = (wave > 0 ? sh[wave - 1] : 0) + inc - v;
+    *total = sh[kPermWaves - 1];
+    __syncthreads();
+    return excl;
+}
+
+// GEMM tiles of expert e (rows [begin, begin+cnt)) from tile index `start`;
+// tiles past max_tiles are dropped.
+__device__ __forceinline__ void write_tiles(int4* tiles, int start, int e, int begin, int cnt, int tile_rows,
+                                            int max_tiles) {
+    for (int j = 0, r = 0; r < cnt; ++j, r += tile_rows) {
+        const int ti = start + j;
+        if (ti >= max_tiles) break;
+        tiles[ti] = make_int4(e, begin + r, min(tile_rows, cnt - r), 0);
+    }
+}
+
+struct PermParams {
+    const int32_t* ids;  // [n_pairs] (global or LDS)
+    int n_pairs, E, id_bits;
+    int32_t* offsets;
+    int32_t* active;
+    int32_t* n_active;
+    int32_t* sorted_pairs;
+    int4* tiles;
+    int32_t* n_tiles;
+    int tile_rows, max_tiles;
+};
+
+// LDS words the permute needs for E experts.
+__host__ __device__ constexpr size_t permute_lds_words(int E) { return size_t(3 * E + 32) + size_t(kPermWaves) * E / 2; }
+
+// Whole-block permute; `lds` holds permute_lds_words(E) words.  Called by
+// all 1024 threads of the block.
+__device__ __forceinline__ void permute_block(const PermParams& P, int* lds) {
+    const int E = P.E;
+    int* cnt = lds;             // [E]
+    int* base = cnt + E;        // [E]
+    int* cursor = base + E;     // [E]
+    int* sh = cursor + E;       // [32]
+    uint16_t* wcnt = reinterpret_cast<uint16_t*>(sh + 32);  // [16][E]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    for (int e = tid; e < E; e += kPermThreads) {
+        cnt[e] = 0;
+        cursor[e] = 0;
+    }
+    for (int i = tid; i < kPermWaves * E; i += kPermThreads) wcnt[i] = 0;
+    __syncthreads();
+    for (int p = tid; p < P.n_pairs; p += kPermThreads) {
+        const int e = P.ids[p];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+
+    const int c = tid < E ? cnt[tid] : 0;
+    int total;
+    const int off = block_exclusive_scan(c, &total, sh);
+    int n_act;
+    const int apos = block_exclusive_scan(c > 0 ? 1 : 0, &n_act, sh);
+    const int nt = (c + P.tile_rows - 1) / P.tile_rows;
+    int tiles_total;
+    const int tstart = block_exclusive_scan(nt, &tiles_total, sh);
+    if (tid < E) {
+        base[tid] = off;
+        P.offsets[tid] = off;
+        if (c > 0) {
+            P.active[apos] = tid;
+            if (P.tiles) write_tiles(P.tiles, tstart, tid, off, c, P.tile_rows, P.max_tiles);
+        }
+    }
+    if (tid == 0) {
+        P.offsets[E] = total;
+        *P.n_active = n_act;
+        if (P.n_tiles) *P.n_tiles = min(tiles_total, P.max_tiles);
+    }
+    __syncthreads();
+
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int r0 = 0; r0 < P.n_pairs; r0 += kPermThreads) {
+        const int p = r0 + tid;
+        int e = p < P.n_pairs ? P.ids[p] : -1;
+        const bool valid = e >= 0 && e < E;
+        if (!valid) e = 0;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < P.id_bits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t bb = __ballot(bit);
+            peers &= bit ? bb : ~bb;
+        }
+        const int rank = __popcll(peers & lt_mask);
+        const int wc = __popcll(peers);
+        if (valid && rank == 0) wcnt[wave * E + e] = uint16_t(wc);
+        __syncthreads();
+        if (valid) {
+            int before = 0;
+            for (int w = 0; w < wave; ++w) before += wcnt[w * E + e];
+            P.sorted_pairs[base[e] + cursor[e] + before + rank] = p;
+        }
+        __syncthreads();
+        if (valid && rank == 0) {
+            atomicAdd(&cursor[e], wc);
+            wcnt[wave * E + e] = 0;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace moe
