@@ -81,7 +81,7 @@ class Instance:
                           aux_stream=aux)
 
     def stage(self, stage):
-        moe.layer_stage(self.cfg, self.ws_struct, self.x, self.wts, stage, self.ws)
+        moe.layer_stage(self.cfg, self.ws_struct, self.x, stage, self.ws)
 
     def n_active(self):
         return int(np.unique(self.ids.cpu().numpy()).size)
@@ -101,16 +101,26 @@ def layer_flops(spec):
     return 2.0 * T * (E * D + K * 3 * D * F + 3 * D * Fs + (D if spec.shared_gate and Fs else 0))
 
 
+def shared_in_routed_launch(spec):
+    """Small T*K: the library runs the shared expert inside the routed launches."""
+    T, K, E = spec.n_tokens, spec.top_k, spec.n_experts
+    return T * K <= 256 and T * K < 64 * E and spec.d_ff_shared > 0
+
+
 def gateup_bytes(spec, n_active):
     """Algorithmic bytes of one routed gate/up launch: the active experts' gate
-    and up matrices read once, the token rows read, the bf16 SwiGLU rows written."""
-    T, D, K, F = spec.n_tokens, spec.d_model, spec.top_k, spec.d_ff
+    and up matrices read once (plus the shared expert's when the launch carries
+    it), the token rows read, the bf16 SwiGLU rows written."""
+    T, D, K, F, Fs = spec.n_tokens, spec.d_model, spec.top_k, spec.d_ff, spec.d_ff_shared
     bw = BYTES_PER_PARAM[spec.expert_dtype]
-    return n_active * 2 * D * F * bw + T * D * 2 + T * K * F * 2
+    shared = shared_in_routed_launch(spec)
+    return (n_active * 2 * D * F * bw + (2 * D * Fs * bw if shared else 0) + T * D * 2
+            + (T * K * F + (T * Fs if shared else 0)) * 2)
 
 
 def gateup_flops(spec):
-    return 2.0 * spec.n_tokens * spec.top_k * 2 * spec.d_model * spec.d_ff
+    shared = shared_in_routed_launch(spec)
+    return 2.0 * spec.n_tokens * 2 * spec.d_model * (spec.top_k * spec.d_ff + (spec.d_ff_shared if shared else 0))
 
 
 def build_instances(spec, L, log_prefix):

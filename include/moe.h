@@ -167,12 +167,19 @@ moe_status moe_shared_expert(const moe_config* cfg, const void* x, const moe_wei
 moe_status moe_combine(const moe_config* cfg, const float* slot_out, const float* shared_out,
                        const float* residual, float* out, moe_stream_t stream);
 
-/* The whole layer: route -> permute -> experts, the shared expert on
- * aux_stream when it is non-NULL (forked from and joined back into
- * `stream` with library-owned events; otherwise on `stream`), then combine.
- * residual [T, D] fp32; out [T, D] fp32 (may alias residual).  topk_ids_out
- * [T, K] and topk_weights_out [T, K] receive the routing when non-NULL.
- * Internally the routed slot rows are staged in bf16 for bf16/u4 weights. */
+/* The whole layer: route -> permute -> experts -> combine, with the shared
+ * expert.  residual [T, D] fp32; out [T, D] fp32 (may alias residual).
+ * topk_ids_out [T, K] and topk_weights_out [T, K] receive the routing when
+ * non-NULL.  Internally the routed slot rows are staged in bf16 for bf16/u4
+ * weights.  Schedules:
+ *   T*K <= 256 (and experts averaging < 64 pairs): a single stream; the
+ *     shared expert is one more work item of the routed gate/up and down
+ *     launches, its sigmoid gate logit is computed with the routing, and each
+ *     GEMM workgroup finds its expert and pairs from the routing ids itself
+ *     (no separate permute launch).  aux_stream is not used.
+ *   otherwise: the shared expert runs on aux_stream when it is non-NULL
+ *     (forked from and joined back into `stream` with library-owned events;
+ *     otherwise on `stream`) while routing and the permute run. */
 moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, const void* x,
                              const float* residual, float* out, int32_t* topk_ids_out,
                              float* topk_weights_out, void* ws, size_t ws_bytes,
@@ -187,14 +194,12 @@ typedef enum {
 
 /* Measurement aid: re-launches one kernel stage of the last
  * moe_layer_forward that ran with this cfg, weights, x and ws, reading the
- * stage's inputs from the workspace (routing, permutation, tile list, h) and
- * rewriting the same workspace outputs, so the stage can be timed alone on
- * the real routing of that call.  topk_weights is the buffer the forward
- * received as topk_weights_out (NULL if it received NULL).  It has no effect
- * on the caller's out/residual. */
-moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, const void* x,
-                           const float* topk_weights, moe_stage stage, void* ws, size_t ws_bytes,
-                           moe_stream_t stream);
+ * stage's inputs from the workspace (routing, permutation or tile list, h)
+ * and rewriting the same workspace outputs, so the stage can be timed alone
+ * on the real routing of that call.  It has no effect on the caller's
+ * out/residual or routing outputs. */
+moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, const void* x, moe_stage stage,
+                           void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);

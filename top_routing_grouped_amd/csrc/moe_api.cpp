@@ -40,11 +40,20 @@ int wkind_of(moe_dtype d) {
 // K elements per chunk a wave consumes: fp32 16, bf16/u4 128.
 int kspan_of(moe_dtype expert) { return expert == MOE_F32 ? 16 : 128; }
 
-// tokens per routed GEMM tile: 16 when experts average fewer than 64 pairs.
-int routed_tf(const moe_config& c) {
-    return (int64_t)c.n_tokens * c.top_k >= (int64_t)64 * c.n_experts ? 4 : 1;
-}
+// Routed GEMM tiles: experts averaging >= 64 pairs use 64-token tiles, or the
+// LDS-tiled 128-token kernel for bf16 weights; fewer pairs use 16-token tiles
+// (weights streamed straight into registers).
+bool routed_large(const moe_config& c) { return (int64_t)c.n_tokens * c.top_k >= (int64_t)64 * c.n_experts; }
+bool routed_tiled(const moe_config& c) { return routed_large(c) && c.expert_dtype == MOE_BF16; }
+int routed_tf(const moe_config& c) { return routed_large(c) ? 4 : 1; }
+int routed_tile_rows(const moe_config& c) { return routed_tiled(c) ? moe::tiled_rows() : 16 * routed_tf(c); }
 int dense_tf(const moe_config& c) { return c.n_tokens >= 64 ? 4 : 1; }
+bool dense_tiled(const moe_config& c, moe_dtype d) { return c.n_tokens >= 128 && d == MOE_BF16; }
+// Small T*K: one stream; every GEMM workgroup finds its expert and pairs from
+// the routing ids itself (no permute launch) and the shared expert is an
+// extra work item of the routed launches.
+bool small_path(const moe_config& c) { return !routed_large(c) && (int64_t)c.n_tokens * c.top_k <= 256; }
+int h_ld(const moe_config& c) { return std::max(c.d_ff, c.d_ff_shared); }
 
 // Router logits: K split over workgroups for small T (each wave one chunk).
 int router_ksplit(const moe_config& c) {
@@ -66,7 +75,7 @@ Layout layout(const moe_config& c) {
     const size_t T = c.n_tokens, E = c.n_experts, K = c.top_k, D = c.d_model, F = c.d_ff, Fs = c.d_ff_shared;
     const size_t TK = T * K;
     const size_t hb = c.expert_dtype == MOE_F32 ? 4 : 2;
-    const size_t mt = size_t(max_tiles(TK, int(E), 16 * routed_tf(c)));
+    const size_t mt = size_t(max_tiles(TK, int(E), routed_tile_rows(c)));
     Layout L{};
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -84,8 +93,9 @@ Layout layout(const moe_config& c) {
     L.n_tiles = take(4);
     L.pairs = take(TK * 4);
     L.tiles = take(mt * 16);
-    L.h = take(TK * F * hb);
-    L.slots = take(TK * D * hb);
+    const size_t Fh = size_t(std::max(c.d_ff, c.d_ff_shared));
+    L.h = take(std::max(TK * F, (TK + T) * Fh) * hb);
+    L.slots = take(std::max(TK * D, T * (K + 1) * D) * hb);
     L.hs = take(T * Fs * hb);
     L.ys = take(T * D * 4);
     L.total = o;
@@ -169,14 +179,21 @@ moe_status stage_logits(const moe_config& c, const Layout& L, void* ws, const vo
     a.act = x; a.n_act_rows = T; a.n_rows = T;
     a.out = at<float>(ws, L.logits);
     a.ksplit = router_ksplit(c);
+    if (a.ksplit == 1 && dense_tiled(c, c.router_dtype)) {
+        HIP_TRY(moe::launch_gemm_tiled(moe::kDenseStore, false, a, (T + moe::tiled_rows() - 1) / moe::tiled_rows(), s));
+        return MOE_OK;
+    }
     const int tf = dense_tf(c);
     HIP_TRY(moe::launch_gemm(moe::kDenseStore, c.router_dtype == MOE_F32 ? moe::kWF32 : moe::kWBF16, false, a,
                              (T + 16 * tf - 1) / (16 * tf), tf, s));
     return MOE_OK;
 }
 
-moe::SelParams sel_params(const moe_config& c, const Layout& L, void* ws, const float* bias) {
+moe::SelParams sel_params(const moe_config& c, const Layout& L, void* ws, const float* bias,
+                          int32_t* ids2 = nullptr, float* wts2 = nullptr) {
     moe::SelParams P{};
+    P.ids2 = ids2;
+    P.wts2 = wts2;
     P.logits = at<float>(ws, L.logits);
     P.ksplit = router_ksplit(c);
     P.T = c.n_tokens; P.E = c.n_experts; P.K = c.top_k;
@@ -216,6 +233,10 @@ moe_status stage_gateup(const moe_config& c, const Layout& L, void* ws, const vo
     a.act = x; a.n_act_rows = T;
     a.tiles = tiles; a.n_tiles = n_tiles; a.pairs = pairs; a.n_pairs = TK; a.topk = K;
     a.out = at<void>(ws, L.h);
+    if (routed_tiled(c)) {
+        HIP_TRY(moe::launch_gemm_tiled(moe::kRoutedGateUp, true, a, int(max_tiles(TK, c.n_experts, routed_tile_rows(c))), s));
+        return MOE_OK;
+    }
     HIP_TRY(moe::launch_gemm(moe::kRoutedGateUp, wkind_of(c.expert_dtype), c.expert_dtype != MOE_F32, a, grid, tf, s));
     return MOE_OK;
 }
@@ -230,7 +251,58 @@ moe_status stage_down(const moe_config& c, const Layout& L, void* ws, const moe_
     d.act = at<void>(ws, L.h); d.n_act_rows = TK;
     d.tiles = tiles; d.n_tiles = n_tiles; d.pairs = pairs; d.n_pairs = TK; d.topk = K;
     d.out = slot_out; d.row_scale = wts;
+    if (routed_tiled(c)) {
+        HIP_TRY(moe::launch_gemm_tiled(moe::kRoutedDown, slot_bf16, d, int(max_tiles(TK, c.n_experts, routed_tile_rows(c))), s));
+        return MOE_OK;
+    }
     HIP_TRY(moe::launch_gemm(moe::kRoutedDown, wkind_of(c.expert_dtype), slot_bf16, d, grid, tf, s));
+    return MOE_OK;
+}
+
+moe::GemmArgs small_args(const moe_config& c, const Layout& L, void* ws, const moe_weights& w, bool gateup) {
+    moe::GemmArgs a{};
+    const int T = c.n_tokens, K = c.top_k, TK = T * K;
+    a.ids = at<int32_t>(ws, L.ids);
+    a.n_pairs = TK; a.n_tokens = T; a.n_experts = c.n_experts; a.topk = K; a.n_banks = c.n_experts;
+    a.has_shared = c.d_ff_shared > 0;
+    const moe_matrix& r0 = gateup ? w.gate : w.down;
+    a.w0 = r0.w; a.s0 = r0.scale; a.m0 = r0.min;
+    if (gateup) { a.w1 = w.up.w; a.s1 = w.up.scale; a.m1 = w.up.min; }
+    if (a.has_shared) {
+        const moe_matrix& q0 = gateup ? w.shared_gate : w.shared_down;
+        a.sw0 = q0.w; a.ss0 = q0.scale; a.sm0 = q0.min;
+        if (gateup) { a.sw1 = w.shared_up.w; a.ss1 = w.shared_up.scale; a.sm1 = w.shared_up.min; }
+    }
+    if (gateup) {
+        a.N = c.d_ff; a.sN = c.d_ff_shared; a.K = c.d_model; a.sK = c.d_model;
+        a.n_act_rows = T;
+        a.out_ld = h_ld(c);
+    } else {
+        a.N = c.d_model; a.sN = c.d_model; a.K = c.d_ff; a.sK = c.d_ff_shared > 0 ? c.d_ff_shared : c.d_ff;
+        a.n_act_rows = TK + T;
+        a.act_ld = h_ld(c);
+        a.row_scale = at<float>(ws, L.wts);
+        a.gate_logit = w.shared_gate_vec ? at<float>(ws, L.gate_logit) : nullptr;
+    }
+    return a;
+}
+
+moe_status stage_small_gateup(const moe_config& c, const Layout& L, void* ws, const void* x, const moe_weights& w,
+                              hipStream_t s) {
+    moe::GemmArgs a = small_args(c, L, ws, w, true);
+    a.act = x;
+    a.out = at<void>(ws, L.h);
+    const int grid = (a.has_shared ? 1 : 0) + std::min(c.n_experts, c.n_tokens * c.top_k);
+    HIP_TRY(moe::launch_gemm(moe::kSmallGateUp, wkind_of(c.expert_dtype), c.expert_dtype != MOE_F32, a, grid, 1, s));
+    return MOE_OK;
+}
+
+moe_status stage_small_down(const moe_config& c, const Layout& L, void* ws, const moe_weights& w, hipStream_t s) {
+    moe::GemmArgs a = small_args(c, L, ws, w, false);
+    a.act = at<void>(ws, L.h);
+    a.out = at<void>(ws, L.slots);
+    const int grid = (a.has_shared ? 1 : 0) + std::min(c.n_experts, c.n_tokens * c.top_k);
+    HIP_TRY(moe::launch_gemm(moe::kSmallDown, wkind_of(c.expert_dtype), c.expert_dtype != MOE_F32, a, grid, 1, s));
     return MOE_OK;
 }
 
@@ -257,9 +329,15 @@ moe_status stage_shared(const moe_config& c, const Layout& L, void* ws, const vo
     void* hs = at<void>(ws, L.hs);
     moe::GemmArgs a = gemm_args(w.shared_gate, &w.shared_up, c.d_ff_shared, c.d_model, 1);
     a.act = x; a.n_act_rows = T; a.n_rows = T; a.out = hs;
-    HIP_TRY(moe::launch_gemm(moe::kDenseGateUp, wk, hbf, a, grid, tf, s));
     moe::GemmArgs d = gemm_args(w.shared_down, nullptr, c.d_model, c.d_ff_shared, 1);
     d.act = hs; d.n_act_rows = T; d.n_rows = T; d.out = shared_out; d.row_scale = gl;
+    if (dense_tiled(c, c.expert_dtype)) {
+        const int g = (T + moe::tiled_rows() - 1) / moe::tiled_rows();
+        HIP_TRY(moe::launch_gemm_tiled(moe::kDenseGateUp, true, a, g, s));
+        HIP_TRY(moe::launch_gemm_tiled(moe::kDenseDown, false, d, g, s));
+        return MOE_OK;
+    }
+    HIP_TRY(moe::launch_gemm(moe::kDenseGateUp, wk, hbf, a, grid, tf, s));
     HIP_TRY(moe::launch_gemm(moe::kDenseDown, wk, false, d, grid, tf, s));
     return MOE_OK;
 }
@@ -346,7 +424,7 @@ moe_status moe_experts(const moe_config* cfg, const void* x, const moe_weights* 
     (void)hipGetLastError();
     const Layout L = layout(*cfg);
     const int TK = cfg->n_tokens * cfg->top_k;
-    const int tile_rows = 16 * routed_tf(*cfg);
+    const int tile_rows = routed_tile_rows(*cfg);
     int4* tiles = at<int4>(ws, L.tiles);
     int32_t* nt = at<int32_t>(ws, L.n_tiles);
     HIP_TRY(moe::launch_build_tiles(expert_offsets, active_experts, n_active, cfg->n_experts, TK, tiles, nt,
@@ -394,8 +472,27 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
     const Layout L = layout(c);
     const bool has_shared = c.d_ff_shared > 0;
     const bool slot_bf16 = c.expert_dtype != MOE_F32;
-    float* ys = has_shared ? at<float>(ws, L.ys) : nullptr;
+    int32_t* ids = at<int32_t>(ws, L.ids);
+    float* wts = at<float>(ws, L.wts);
+    const moe::SelParams P = sel_params(c, L, ws, weights->expert_bias, topk_ids_out, topk_weights_out);
 
+    if (small_path(c)) {
+        // one stream: logits -> selection (+ shared gate logit) -> gate/up -> down -> combine
+        if (moe_status st = stage_logits(c, L, ws, x, weights->router, stream)) return st;
+        moe::GateParams G{};
+        if (has_shared && weights->shared_gate_vec) {
+            G.x = x; G.w = weights->shared_gate_vec; G.D = c.d_model; G.x_f32 = c.act_dtype == MOE_F32;
+            G.out = at<float>(ws, L.gate_logit);
+        }
+        HIP_TRY(moe::launch_route_select_gate(P, G, ids, wts, stream));
+        if (moe_status st = stage_small_gateup(c, L, ws, x, *weights, stream)) return st;
+        if (moe_status st = stage_small_down(c, L, ws, *weights, stream)) return st;
+        HIP_TRY(moe::launch_combine(at<void>(ws, L.slots), slot_bf16, nullptr, residual, out, c.n_tokens,
+                                    c.top_k + (has_shared ? 1 : 0), c.d_model, stream));
+        return MOE_OK;
+    }
+
+    float* ys = has_shared ? at<float>(ws, L.ys) : nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     const bool fork = has_shared && aux_stream && aux_stream != stream;
     if (fork) {
@@ -408,9 +505,7 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
         if (moe_status st = stage_shared(c, L, ws, x, *weights, ys, stream)) return st;
     }
 
-    int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
-    float* wts = topk_weights_out ? topk_weights_out : at<float>(ws, L.wts);
-    const int tile_rows = 16 * routed_tf(c);
+    const int tile_rows = routed_tile_rows(c);
     int32_t* pairs = at<int32_t>(ws, L.pairs);
     int4* tiles = at<int4>(ws, L.tiles);
     int32_t* nt = at<int32_t>(ws, L.n_tiles);
@@ -418,9 +513,9 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
                                           at<int32_t>(ws, L.n_active), pairs, tiles, nt, tile_rows);
     if (moe_status st = stage_logits(c, L, ws, x, weights->router, stream)) return st;
     if (moe::route_permute_fusable(c.n_tokens, c.n_experts, c.top_k)) {
-        HIP_TRY(moe::launch_route_permute(sel_params(c, L, ws, weights->expert_bias), ids, wts, Q, stream));
+        HIP_TRY(moe::launch_route_permute(P, ids, wts, Q, stream));
     } else {
-        HIP_TRY(moe::launch_route_select(sel_params(c, L, ws, weights->expert_bias), ids, wts, stream));
+        HIP_TRY(moe::launch_route_select(P, ids, wts, stream));
         HIP_TRY(moe::launch_permute(Q, stream));
     }
     void* slots = at<void>(ws, L.slots);
@@ -431,14 +526,13 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
     return MOE_OK;
 }
 
-moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, const void* x,
-                           const float* topk_weights, moe_stage stage, void* ws, size_t ws_bytes,
-                           moe_stream_t stream) {
+moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, const void* x, moe_stage stage,
+                           void* ws, size_t ws_bytes, moe_stream_t stream) {
     g_err[0] = 0;
     if (moe_status st = check_config(cfg)) return st;
     if (cfg->n_tokens == 0) return MOE_OK;
     if (!x || !weights || !weights->router) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL argument");
-    if (moe_status st = check_weights(*cfg, weights, true, false)) return st;
+    if (moe_status st = check_weights(*cfg, weights, true, true)) return st;
     if (moe_status st = check_ws(*cfg, ws, ws_bytes)) return st;
     (void)hipGetLastError();
     const moe_config& c = *cfg;
@@ -448,10 +542,13 @@ moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, co
     int32_t* nt = at<int32_t>(ws, L.n_tiles);
     switch (stage) {
         case MOE_STAGE_ROUTER_LOGITS: return stage_logits(c, L, ws, x, weights->router, stream);
-        case MOE_STAGE_GATE_UP: return stage_gateup(c, L, ws, x, *weights, pairs, tiles, nt, stream);
+        case MOE_STAGE_GATE_UP:
+            if (small_path(c)) return stage_small_gateup(c, L, ws, x, *weights, stream);
+            return stage_gateup(c, L, ws, x, *weights, pairs, tiles, nt, stream);
         case MOE_STAGE_DOWN:
-            return stage_down(c, L, ws, *weights, pairs, tiles, nt, topk_weights ? topk_weights : at<float>(ws, L.wts),
-                              at<void>(ws, L.slots), c.expert_dtype != MOE_F32, stream);
+            if (small_path(c)) return stage_small_down(c, L, ws, *weights, stream);
+            return stage_down(c, L, ws, *weights, pairs, tiles, nt, at<float>(ws, L.wts), at<void>(ws, L.slots),
+                              c.expert_dtype != MOE_F32, stream);
     }
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown stage %d", int(stage));
 }

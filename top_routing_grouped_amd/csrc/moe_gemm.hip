@@ -138,23 +138,98 @@ __device__ __forceinline__ void mma_chunk(f32x4& acc, const Frag<F32>& a, const 
     }
 }
 
+// --------------------------------------------------------------- small-T tiles
+// Small T*K: workgroup item 0 is the shared expert (all T tokens, when the
+// layer has one); item 1 + a is the a-th distinct expert among the T*K
+// routed pairs in ascending expert id, and m-tile z takes its pairs
+// [16z, 16z + 16) in ascending pair id.  The routing ids are read directly:
+// a bit set of the experts present (LDS atomics), the a-th set bit, and a
+// ballot rank of the matching pairs.  Returns the row count (0: no work).
+__device__ int small_tile(const GemmArgs& a, int item, int mt, int* rows, int* e_out) {
+    __shared__ uint32_t pres[32];
+    __shared__ int meta[2];
+    __shared__ int wsum[4];
+    const int tid = threadIdx.x;
+    const int TK = a.n_pairs;
+    if (item < 0) {  // shared expert: tokens 16*mt + i
+        const int cnt = min(16, a.n_tokens - 16 * mt);
+        if (tid < 16) rows[tid] = 16 * mt + tid;
+        *e_out = -1;
+        __syncthreads();
+        return max(cnt, 0);
+    }
+    if (tid < 32) pres[tid] = 0;
+    __syncthreads();
+    for (int p = tid; p < TK; p += 256) {
+        const int e = a.ids[p];
+        if (e >= 0 && e < a.n_experts) atomicOr(&pres[e >> 5], 1u << (e & 31));
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int left = item, found = -1;
+        for (int w = 0; w < (a.n_experts + 31) / 32 && found < 0; ++w) {
+            uint32_t bits = pres[w];
+            const int c = __popc(bits);
+            if (left < c) {
+                for (int i = 0; i < left; ++i) bits &= bits - 1;
+                found = w * 32 + __ffs(bits) - 1;
+            }
+            left -= c;
+        }
+        meta[0] = found;
+    }
+    __syncthreads();
+    const int e = meta[0];
+    *e_out = e;
+    if (e < 0) return 0;
+    const int lane = tid & 63, wave = tid >> 6;
+    const bool m = tid < TK && a.ids[tid] == e;  // TK <= 256: one pair per thread
+    const uint64_t b = __ballot(m);
+    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    if (lane == 0) wsum[wave] = __popcll(b);
+    __syncthreads();
+    int off = 0;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    const int pos = off + __popcll(b & lt) - 16 * mt;
+    if (m && pos >= 0 && pos < 16) rows[pos] = tid;
+    const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    return max(0, min(16, total - 16 * mt));
+}
+
 // --------------------------------------------------------------- kernel
-// MODE: kRoutedGateUp | kRoutedDown | kDenseGateUp | kDenseDown | kDenseStore
+// MODE: kRoutedGateUp | kRoutedDown | kDenseGateUp | kDenseDown | kDenseStore | kSmallGateUp | kSmallDown
 // WK: weight kind; OUTBF: output stored as bf16 (else fp32)
 // TF: 16-token fragments per tile; WN x WKS waves = 4 (rows x K split)
 template <int MODE, int WK, bool OUTBF, int TF, int WN, int WKS>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     constexpr bool F32 = (WK == kWF32);
-    constexpr bool DUAL = (MODE == kRoutedGateUp || MODE == kDenseGateUp);
+    constexpr bool SMALL = (MODE == kSmallGateUp || MODE == kSmallDown);
+    constexpr bool DUAL = (MODE == kRoutedGateUp || MODE == kDenseGateUp || MODE == kSmallGateUp);
     constexpr bool ROUTED = (MODE == kRoutedGateUp || MODE == kRoutedDown);
     constexpr int KL = WTraits<WK>::KL;
     constexpr int SPAN = 4 * KL;
     constexpr int BM = 16 * TF;
     constexpr int NM = DUAL ? 2 : 1;
+    static_assert(!SMALL || TF == 1, "small-T tiles are 16 rows");
 
-    // ---- tile
-    int e = 0, begin, count;
-    if constexpr (ROUTED) {
+    // ---- tile: expert (bank) e, rows [begin, begin + count) or explicit rows (small T)
+    __shared__ int srows[16];
+    int e = 0, begin = 0, count;
+    bool shared_item = false;
+    int N = a.N, K = a.K;
+    const void *w0 = a.w0, *s0 = a.s0, *m0 = a.m0, *w1 = a.w1, *s1 = a.s1, *m1 = a.m1;
+    if constexpr (SMALL) {
+        const int item = int(blockIdx.x) - (a.has_shared ? 1 : 0);
+        count = small_tile(a, item, blockIdx.z, srows, &e);
+        if (count <= 0) return;
+        if (item < 0) {
+            shared_item = true;
+            e = 0;
+            w0 = a.sw0; s0 = a.ss0; m0 = a.sm0; w1 = a.sw1; s1 = a.ss1; m1 = a.sm1;
+            if constexpr (MODE == kSmallGateUp) N = a.sN; else K = a.sK;
+        }
+    } else if constexpr (ROUTED) {
         const int tile = blockIdx.x;
         if (tile >= *a.n_tiles) return;
         const int4 t = a.tiles[tile];
@@ -165,6 +240,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         count = min(BM, a.n_rows - begin);
         if (count <= 0) return;
     }
+    const int act_ld = a.act_ld > 0 ? a.act_ld : K;
+    const int out_ld = a.out_ld > 0 ? a.out_ld : N;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -172,7 +249,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     const int wk = wave / WN;
     const int q = lane >> 4;
     const int r = lane & 15;
-    const int N = a.N, K = a.K;
     // dense store may split K over blockIdx.z (partial sums to separate planes)
     const int ksub = (MODE == kDenseStore) ? K / max(a.ksplit, 1) : K;
     const int kbase = (MODE == kDenseStore) ? int(blockIdx.z) * ksub : 0;
@@ -190,12 +266,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
             if constexpr (MODE == kRoutedGateUp) {
                 const int pair = a.pairs[begin + i];
                 arow = (pair >= 0 && pair < a.n_pairs) ? pair / a.topk : -1;
+            } else if constexpr (MODE == kSmallGateUp) {
+                arow = shared_item ? srows[i] : srows[i] / a.topk;  // token
+            } else if constexpr (MODE == kSmallDown) {
+                arow = shared_item ? a.n_pairs + srows[i] : srows[i];  // h row: pair, or T*K + token
             } else {
                 arow = begin + i;
             }
             if (arow >= 0 && arow < a.n_act_rows)
-                p = F32 ? static_cast<const void*>(static_cast<const float*>(a.act) + size_t(arow) * K)
-                        : static_cast<const void*>(static_cast<const uint16_t*>(a.act) + size_t(arow) * K);
+                p = F32 ? static_cast<const void*>(static_cast<const float*>(a.act) + size_t(arow) * act_ld)
+                        : static_cast<const void*>(static_cast<const uint16_t*>(a.act) + size_t(arow) * act_ld);
         }
         xrow[j] = p;
     }
@@ -215,8 +295,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         for (int c = 0; c < nchunks; ++c) {
             const int kc = kbeg + c * SPAN;
             Frag<F32> wa[NM];
-            load_w<WK>(wa[0], a.w0, a.s0, a.m0, wrow, K, kc, q);
-            if constexpr (DUAL) load_w<WK>(wa[1], a.w1, a.s1, a.m1, wrow, K, kc, q);
+            load_w<WK>(wa[0], w0, s0, m0, wrow, K, kc, q);
+            if constexpr (DUAL) load_w<WK>(wa[1], w1, s1, m1, wrow, K, kc, q);
             Frag<F32> xb[TF];
 #pragma unroll
             for (int j = 0; j < TF; ++j) load_x<WK>(xb[j], xrow[j], kc, q);
@@ -269,7 +349,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                 const float g = acc[0][j][t];
                 v[t] = g / (1.0f + __expf(-g)) * acc[1][j][t];
             }
-            dest = size_t(begin + i);
+            if constexpr (MODE == kSmallGateUp)
+                dest = shared_item ? size_t(a.n_pairs + srows[i]) : size_t(srows[i]);
+            else
+                dest = size_t(begin + i);
         } else if constexpr (MODE == kRoutedDown) {
             const int pair = a.pairs[begin + i];
             if (pair < 0 || pair >= a.n_pairs) continue;
@@ -277,6 +360,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) v[t] = s * acc[0][j][t];
             dest = size_t(pair);
+        } else if constexpr (MODE == kSmallDown) {
+            // slot rows per token: K routed (+ the shared expert in slot K)
+            const int id = srows[i];
+            const int spt = a.topk + (a.has_shared ? 1 : 0);
+            float s;
+            if (shared_item) {
+                s = a.gate_logit ? sigmoidf_(a.gate_logit[id]) : 1.0f;
+                dest = size_t(id) * spt + a.topk;
+            } else {
+                s = a.row_scale[id];
+                dest = size_t(id / a.topk) * spt + id % a.topk;
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = s * acc[0][j][t];
         } else if constexpr (MODE == kDenseDown) {
             const float s = a.row_scale ? sigmoidf_(a.row_scale[begin + i]) : 1.0f;
 #pragma unroll
@@ -289,40 +386,53 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         }
         if constexpr (OUTBF) {
             uint2 pk = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + dest * N + f0) = pk;
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + dest * out_ld + f0) = pk;
         } else {
-            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + dest * N + f0) =
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + dest * out_ld + f0) =
                 make_float4(v[0], v[1], v[2], v[3]);
         }
     }
 }
 
 // --------------------------------------------------------------- launchers
+// K the waves of a small-T workgroup split: both the routed and the shared
+// item must divide evenly, so take the smaller of the two reduction lengths'
+// common divisibility (they are both multiples of the chunk span).
+static int gcd_k(const GemmArgs& a) {
+    int x = a.K, y = a.sK > 0 ? a.sK : a.K;
+    while (y) { const int t = x % y; x = y; y = t; }
+    return x;
+}
+
 template <int MODE, int WK, bool OUTBF>
 static hipError_t launch_cfg(const GemmArgs& a, int grid_x, int tf, hipStream_t s) {
     // waves split the workgroup's K range 4, 2 or 1 ways (rows 16, 32, 64)
-    const int ks = (MODE == kDenseStore && a.ksplit > 1) ? a.ksplit : 1;
-    const int kwg = a.K / ks;
+    constexpr bool SMALL = (MODE == kSmallGateUp || MODE == kSmallDown);
+    int ks = (MODE == kDenseStore && a.ksplit > 1) ? a.ksplit : 1;
+    if (SMALL) ks = (a.n_tokens + 15) / 16;  // grid.z = 16-token m-tiles (an expert holds <= T pairs)
+    const int kwg = (MODE == kDenseStore) ? a.K / ks : (SMALL && a.has_shared ? gcd_k(a) : a.K);
+    if constexpr (SMALL) tf = 1;
+    const int nrows = (MODE == kSmallGateUp && a.has_shared && a.sN > a.N) ? a.sN : a.N;
     constexpr int SPAN = 4 * WTraits<WK>::KL;
     const bool ksplit4 = (kwg % (4 * SPAN) == 0);
     const bool ksplit2 = (kwg % (2 * SPAN) == 0);
-    if (tf == 1) {
+    if (tf == 1 || SMALL) {
         if (ksplit4) {
-            dim3 g(grid_x, (a.N + 15) / 16, ks);
+            dim3 g(grid_x, (nrows + 15) / 16, ks);
             gemm_kernel<MODE, WK, OUTBF, 1, 1, 4><<<g, 256, 0, s>>>(a);
         } else if (ksplit2) {
-            dim3 g(grid_x, (a.N + 31) / 32, ks);
+            dim3 g(grid_x, (nrows + 31) / 32, ks);
             gemm_kernel<MODE, WK, OUTBF, 1, 2, 2><<<g, 256, 0, s>>>(a);
         } else {
-            dim3 g(grid_x, (a.N + 63) / 64, ks);
+            dim3 g(grid_x, (nrows + 63) / 64, ks);
             gemm_kernel<MODE, WK, OUTBF, 1, 4, 1><<<g, 256, 0, s>>>(a);
         }
-    } else {
+    } else if constexpr (!SMALL) {
         if (ksplit4) {
-            dim3 g(grid_x, (a.N + 15) / 16, ks);
+            dim3 g(grid_x, (nrows + 15) / 16, ks);
             gemm_kernel<MODE, WK, OUTBF, 4, 1, 4><<<g, 256, 0, s>>>(a);
         } else {
-            dim3 g(grid_x, (a.N + 63) / 64, ks);
+            dim3 g(grid_x, (nrows + 63) / 64, ks);
             gemm_kernel<MODE, WK, OUTBF, 4, 4, 1><<<g, 256, 0, s>>>(a);
         }
     }
@@ -341,6 +451,8 @@ static hipError_t dispatch_wk(const GemmArgs& a, int wkind, bool outbf, int grid
 hipError_t launch_gemm(int mode, int wkind, bool outbf, const GemmArgs& a, int grid_x, int tf, hipStream_t s) {
     if (grid_x <= 0) return hipSuccess;
     switch (mode) {
+        case kSmallGateUp: return dispatch_wk<kSmallGateUp>(a, wkind, outbf, grid_x, tf, s);
+        case kSmallDown: return dispatch_wk<kSmallDown>(a, wkind, outbf, grid_x, tf, s);
         case kRoutedGateUp: return dispatch_wk<kRoutedGateUp>(a, wkind, outbf, grid_x, tf, s);
         case kRoutedDown: return dispatch_wk<kRoutedDown>(a, wkind, outbf, grid_x, tf, s);
         case kDenseGateUp: return dispatch_wk<kDenseGateUp>(a, wkind, outbf, grid_x, tf, s);

@@ -1,0 +1,228 @@
+// LDS-tiled bf16 MFMA kernels for the grouped expert GEMMs at large token
+// counts (Treebeard, "How Treebeard routes Qwen3.6 MoE tokens", "Routed
+// expert computation" and "Shared expert computation"; the per-expert
+// grouping follows the "Intel SYCL path": one tile works on one active
+// expert's packed pairs, so each weight block is loaded for up to 128 of them).
+//
+// Workgroup tile: 128 weight rows x 128 token rows, K in steps of 64, two
+// LDS buffers (one barrier per step; the next step's global loads are in
+// flight while the current step's MFMAs run).  For gate/up the 128 weight
+// rows are 64 gate rows and the same 64 up rows, so each lane ends with
+// matching gate and up accumulators and applies SwiGLU in registers.
+// 4 waves in a 2 x 2 grid; each wave owns 64 weight rows x 64 tokens as
+// 4 x 4 fragments of v_mfma_f32_16x16x32_bf16 (weights = A, tokens = B).
+// LDS rows are padded to 144 bytes so a wave's 16-byte fragment reads hit
+// distinct banks.
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BW = 128;       // weight rows per tile
+constexpr int BT = 128;       // token rows per tile
+constexpr int BK = 64;        // K per step
+constexpr int RS = BK + 8;    // LDS row stride in bf16 elements (144 bytes)
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* base) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base));
+}
+
+}  // namespace
+
+template <int MODE, bool OUTBF>
+__global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
+    constexpr bool DUAL = (MODE == kRoutedGateUp || MODE == kDenseGateUp);
+    constexpr bool ROUTED = (MODE == kRoutedGateUp || MODE == kRoutedDown);
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BW * RS];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BT * RS];
+
+    int e = 0, begin, count;
+    if constexpr (ROUTED) {
+        const int tile = blockIdx.x;
+        if (tile >= *a.n_tiles) return;
+        const int4 t = a.tiles[tile];
+        e = t.x; begin = t.y; count = t.z;
+        if (e < 0 || e >= a.n_banks || begin < 0 || count <= 0 || begin + count > a.n_pairs) return;
+    } else {
+        begin = blockIdx.x * BT;
+        count = min(BT, a.n_rows - begin);
+        if (count <= 0) return;
+    }
+    const int N = a.N, K = a.K;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q = lane >> 4, r = lane & 15;
+    const int wm = wave & 1, wn = wave >> 1;
+    // weight-row block: gate/up covers features [f0, f0+64) of both banks
+    const int row_blk = blockIdx.y;
+
+    // ---- global load assignment: 4 pieces of 16 B per thread per operand
+    // piece p = tid + 256*i: row p/8, 16-byte column p%8 (8 threads per 128-byte row segment)
+    const uint16_t* wsrc[4];
+    const uint16_t* xsrc[4];
+    int lrow[4], lcol[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = tid + kThreads * i;
+        const int row = p >> 3, col = (p & 7) * 8;
+        lrow[i] = row;
+        lcol[i] = col;
+        const uint16_t* wb;
+        int wr;
+        if constexpr (DUAL) {
+            wb = static_cast<const uint16_t*>(row < 64 ? a.w0 : a.w1);
+            wr = row_blk * 64 + (row & 63);
+        } else {
+            wb = static_cast<const uint16_t*>(a.w0);
+            wr = row_blk * BW + row;
+        }
+        wsrc[i] = (wr < N) ? wb + (size_t(e) * N + wr) * K + col : nullptr;
+        const uint16_t* xs = nullptr;
+        if (row < count) {
+            int arow;
+            if constexpr (MODE == kRoutedGateUp) {
+                const int pair = a.pairs[begin + row];
+                arow = (pair >= 0 && pair < a.n_pairs) ? pair / a.topk : -1;
+            } else {
+                arow = begin + row;
+            }
+            if (arow >= 0 && arow < a.n_act_rows) xs = static_cast<const uint16_t*>(a.act) + size_t(arow) * K + col;
+        }
+        xsrc[i] = xs;
+    }
+
+    u32x4 wreg[4], xreg[4];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            wreg[i] = wsrc[i] ? *reinterpret_cast<const u32x4*>(wsrc[i] + k0) : u32x4{0, 0, 0, 0};
+            xreg[i] = xsrc[i] ? *reinterpret_cast<const u32x4*>(xsrc[i] + k0) : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<u32x4*>(&As[buf][lrow[i] * RS + lcol[i]]) = wreg[i];
+            *reinterpret_cast<u32x4*>(&Bs[buf][lrow[i] * RS + lcol[i]]) = xreg[i];
+        }
+    };
+
+    // wave's fragment rows inside the tile
+    int arow_l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (DUAL)  // frags 0,1: gate rows; 2,3: the matching up rows
+            arow_l[i] = (i >= 2 ? 64 : 0) + wm * 32 + (i & 1) * 16 + r;
+        else
+            arow_l[i] = wm * 64 + i * 16 + r;
+    }
+    const int brow_l = wn * 64 + r;
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = K / BK;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            bf16x8 af[4], bfr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = lds_frag(&As[cur][arow_l[i] * RS + ks * 32 + q * 8]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bfr[j] = lds_frag(&Bs[cur][(brow_l + j * 16) * RS + ks * 32 + q * 8]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk) lstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane holds rows (4q .. 4q+3) of fragment i, token column r of fragment j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tok = wn * 64 + j * 16 + r;
+        if (tok >= count) continue;
+        if constexpr (DUAL) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int f = row_blk * 64 + wm * 32 + i * 16 + 4 * q;
+                if (f >= N) continue;
+                float v[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float g = acc[i][j][t];
+                    v[t] = g / (1.0f + __expf(-g)) * acc[i + 2][j][t];
+                }
+                const size_t o = size_t(begin + tok) * N + f;
+                if constexpr (OUTBF)
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                else
+                    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        } else {
+            size_t dest;
+            float s = 1.0f;
+            if constexpr (MODE == kRoutedDown) {
+                const int pair = a.pairs[begin + tok];
+                if (pair < 0 || pair >= a.n_pairs) continue;
+                dest = size_t(pair);
+                s = a.row_scale[pair];
+            } else if constexpr (MODE == kDenseDown) {
+                dest = size_t(begin + tok);
+                if (a.row_scale) s = sigmoidf_(a.row_scale[begin + tok]);
+            } else {
+                dest = size_t(begin + tok);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d = row_blk * BW + wm * 64 + i * 16 + 4 * q;
+                if (d >= N) continue;
+                const float v0 = s * acc[i][j][0], v1 = s * acc[i][j][1], v2 = s * acc[i][j][2], v3 = s * acc[i][j][3];
+                const size_t o = dest * N + d;
+                if constexpr (OUTBF)
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) =
+                        make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+                else
+                    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) = make_float4(v0, v1, v2, v3);
+            }
+        }
+    }
+}
+
+int tiled_rows() { return BT; }
+
+hipError_t launch_gemm_tiled(int mode, bool outbf, const GemmArgs& a, int grid_x, hipStream_t s) {
+    if (grid_x <= 0) return hipSuccess;
+    const bool dual = (mode == kRoutedGateUp || mode == kDenseGateUp);
+    const int gy = dual ? (a.N + 63) / 64 : (a.N + BW - 1) / BW;
+    const dim3 g(grid_x, gy);
+    switch (mode) {
+        case kRoutedGateUp: gemm_tiled_kernel<kRoutedGateUp, true><<<g, kThreads, 0, s>>>(a); break;
+        case kRoutedDown:
+            if (outbf) gemm_tiled_kernel<kRoutedDown, true><<<g, kThreads, 0, s>>>(a);
+            else gemm_tiled_kernel<kRoutedDown, false><<<g, kThreads, 0, s>>>(a);
+            break;
+        case kDenseGateUp: gemm_tiled_kernel<kDenseGateUp, true><<<g, kThreads, 0, s>>>(a); break;
+        case kDenseDown: gemm_tiled_kernel<kDenseDown, false><<<g, kThreads, 0, s>>>(a); break;
+        default: gemm_tiled_kernel<kDenseStore, false><<<g, kThreads, 0, s>>>(a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -16,7 +16,9 @@ enum {
     kRoutedDown = 1,    // tiles from the permute; h rows in permuted order; alpha * . -> slot[pair]
     kDenseGateUp = 2,   // all T rows; SwiGLU -> h[t]
     kDenseDown = 3,     // all T rows; sigmoid(gate logit) * . (or 1) -> out[t]
-    kDenseStore = 4     // all T rows; plain fp32 store (router logits)
+    kDenseStore = 4,    // all T rows; plain fp32 store (router logits)
+    kSmallGateUp = 5,   // small T*K: tile derived from topk ids in-kernel; shared expert as item 0
+    kSmallDown = 6      // small T*K: same tiles; writes slot rows t*(K+1)+k, shared to slot K
 };
 
 struct GemmArgs {
@@ -39,15 +41,32 @@ struct GemmArgs {
     void* out;              // [rows][N] fp32 or bf16 (dense store: [ksplit][rows][N])
     const float* row_scale; // routed down: weights[pair]; dense down: gate logits or null
     int ksplit;             // dense store only: K split across blockIdx.z (partial sums)
+    // small-T modes
+    const int32_t* ids;     // topk ids [T*K]
+    int n_tokens;
+    int n_experts;
+    int has_shared;
+    const void* sw0; const void* ss0; const void* sm0;  // shared gate (or shared down)
+    const void* sw1; const void* ss1; const void* sm1;  // shared up
+    const float* gate_logit;  // [T] shared gate logits or null (s = 1)
+    int sN, sK;               // shared item: output rows (gate/up) / reduction length (down)
+    int act_ld, out_ld;       // row strides when they differ from K / N (0 = default)
 };
 
 hipError_t launch_gemm(int mode, int wkind, bool outbf, const GemmArgs& a, int grid_x, int tf, hipStream_t s);
+// bf16 LDS-tiled variant (128 weight rows x 128 tokens per workgroup); K % 64 == 0
+hipError_t launch_gemm_tiled(int mode, bool outbf, const GemmArgs& a, int grid_x, hipStream_t s);
+int tiled_rows();
 
 // routing (parameter blocks in moe_select.h)
 struct SelParams;
 struct PermParams;
 hipError_t launch_route_select(const SelParams& P, int32_t* ids, float* weights, hipStream_t s);
 bool route_permute_fusable(int T, int E, int K);
+// shared-gate logit per token inside the selection kernel (small T path)
+struct GateParams { const void* x; const void* w; int D; int x_f32; float* out; };
+hipError_t launch_route_select_gate(const SelParams& P, const GateParams& G, int32_t* ids, float* weights,
+                                    hipStream_t s);
 hipError_t launch_route_permute(const SelParams& P, int32_t* ids, float* weights, const PermParams& Q,
                                 hipStream_t s);
 hipError_t launch_gate_logit(const void* x, bool x_f32, const void* wvec, int T, int D, float* out, hipStream_t s);
@@ -63,5 +82,6 @@ hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* active, con
 // combine: out = residual + (sum_k slot[t,k,:] + shared[t,:])
 hipError_t launch_combine(const void* slots, bool slots_bf16, const float* shared, const float* residual,
                           float* out, int T, int K, int D, hipStream_t s);
+// small T: the slot rows hold K routed slots + the shared expert (K+1 per token)
 
 }  // namespace moe

@@ -20,22 +20,30 @@
 
 namespace moe {
 
-// One wave per token; blocks of 4 tokens.
+// One wave per token; blocks of 4 tokens.  Optionally also the shared-expert
+// gate logit w_shared . x_t of the token (Treebeard, "Shared expert
+// computation"), issued first so its loads overlap the selection.
 template <int NV>
-__global__ __launch_bounds__(256) void route_select_kernel(SelParams P, int32_t* __restrict__ ids,
+__global__ __launch_bounds__(256) void route_select_kernel(SelParams P, GateParams G, int32_t* __restrict__ ids,
                                                            float* __restrict__ wts) {
     __shared__ float sel_s[4][64 * NV];
     __shared__ float sig_s[4][64 * NV];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     if (t >= P.T) return;  // no block-wide barrier below
+    float gl = 0.f;
+    if (G.w) gl = wave_dot_row(G.x, G.w, t, G.D, G.x_f32 != 0);
     int id;
     float w;
     select_token<NV>(P, t, sel_s[wave], sig_s[wave], &id, &w);
     if (lane < P.K) {
-        ids[size_t(t) * P.K + lane] = id;
-        wts[size_t(t) * P.K + lane] = w;
+        const size_t o = size_t(t) * P.K + lane;
+        ids[o] = id;
+        wts[o] = w;
+        if (P.ids2) P.ids2[o] = id;
+        if (P.wts2) P.wts2[o] = w;
     }
+    if (G.w && lane == 0) G.out[t] = gl;
 }
 
 // Small T: every token's selection, then the permute, in one 1024-thread
@@ -55,8 +63,11 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_kernel(SelParams P
         float w;
         select_token<4>(P, t, sel_s[wave], sig_s[wave], &id, &w);
         if (lane < P.K) {
-            ids[size_t(t) * P.K + lane] = id;
-            wts[size_t(t) * P.K + lane] = w;
+            const size_t o = size_t(t) * P.K + lane;
+            ids[o] = id;
+            wts[o] = w;
+            if (P.ids2) P.ids2[o] = id;
+            if (P.wts2) P.wts2[o] = w;
             ids_s[t * P.K + lane] = id;
         }
     }
@@ -66,19 +77,25 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_kernel(SelParams P
 }
 
 template <int NV>
-static void launch_nv(const SelParams& P, int32_t* ids, float* wts, hipStream_t s) {
-    route_select_kernel<NV><<<(P.T + 3) / 4, 256, 0, s>>>(P, ids, wts);
+static void launch_nv(const SelParams& P, const GateParams& G, int32_t* ids, float* wts, hipStream_t s) {
+    route_select_kernel<NV><<<(P.T + 3) / 4, 256, 0, s>>>(P, G, ids, wts);
+}
+
+hipError_t launch_route_select_gate(const SelParams& P, const GateParams& G, int32_t* ids, float* weights,
+                                    hipStream_t s) {
+    if (P.T <= 0) return hipSuccess;
+    const int nv = (P.E + 63) / 64;
+    if (nv <= 1) launch_nv<1>(P, G, ids, weights, s);
+    else if (nv <= 2) launch_nv<2>(P, G, ids, weights, s);
+    else if (nv <= 4) launch_nv<4>(P, G, ids, weights, s);
+    else if (nv <= 8) launch_nv<8>(P, G, ids, weights, s);
+    else launch_nv<16>(P, G, ids, weights, s);
+    return hipGetLastError();
 }
 
 hipError_t launch_route_select(const SelParams& P, int32_t* ids, float* weights, hipStream_t s) {
-    if (P.T <= 0) return hipSuccess;
-    const int nv = (P.E + 63) / 64;
-    if (nv <= 1) launch_nv<1>(P, ids, weights, s);
-    else if (nv <= 2) launch_nv<2>(P, ids, weights, s);
-    else if (nv <= 4) launch_nv<4>(P, ids, weights, s);
-    else if (nv <= 8) launch_nv<8>(P, ids, weights, s);
-    else launch_nv<16>(P, ids, weights, s);
-    return hipGetLastError();
+    GateParams G{};
+    return launch_route_select_gate(P, G, ids, weights, s);
 }
 
 bool route_permute_fusable(int T, int E, int K) { return E <= kFusedMaxE && T * K <= kFusedMaxPairs && T <= 64; }

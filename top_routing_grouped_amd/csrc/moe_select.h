@@ -49,7 +49,41 @@ struct SelParams {
     int G, TG;
     float scaling;
     const float* bias;
+    int32_t* ids2;  // optional second copy of the outputs
+    float* wts2;
 };
+
+// w . x_t for one token, fp32 accumulation, result in every lane.
+__device__ __forceinline__ float wave_dot_row(const void* x, const void* w, int t, int D, bool f32) {
+    const int lane = threadIdx.x & 63;
+    float acc = 0.f;
+    if (f32) {
+        const float* xr = static_cast<const float*>(x) + size_t(t) * D;
+        const float* wr = static_cast<const float*>(w);
+        for (int k = lane * 4; k < D; k += 256) {
+            const float4 a = *reinterpret_cast<const float4*>(xr + k);
+            const float4 b = *reinterpret_cast<const float4*>(wr + k);
+            acc = fmaf(a.x, b.x, acc);
+            acc = fmaf(a.y, b.y, acc);
+            acc = fmaf(a.z, b.z, acc);
+            acc = fmaf(a.w, b.w, acc);
+        }
+    } else {
+        const uint16_t* xr = static_cast<const uint16_t*>(x) + size_t(t) * D;
+        const uint16_t* wr = static_cast<const uint16_t*>(w);
+        for (int k = lane * 8; k < D; k += 512) {
+            const uint4 a = *reinterpret_cast<const uint4*>(xr + k);
+            const uint4 b = *reinterpret_cast<const uint4*>(wr + k);
+            const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc = fmaf(bf16_lo(av[i]), bf16_lo(bv[i]), acc);
+                acc = fmaf(bf16_hi(av[i]), bf16_hi(bv[i]), acc);
+            }
+        }
+    }
+    return wave_sum(acc);
+}
 
 // Selects token t's experts; lane k < K returns slot k in (*id, *w).
 // sel_s/sig_s: this wave's LDS scratch of 64*NV floats each (sigmoid family).

@@ -78,7 +78,7 @@ def lib() -> ctypes.CDLL:
             "moe_shared_expert": [cfg, P, wts, P, P, S, P],
             "moe_combine": [cfg, P, P, P, P, P],
             "moe_layer_forward": [cfg, wts, P, P, P, P, P, P, S, P, P],
-            "moe_layer_stage": [cfg, wts, P, P, I32, P, S, P],
+            "moe_layer_stage": [cfg, wts, P, I32, P, S, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -182,7 +182,7 @@ def layer_forward(cfg, wstruct: MoeWeights, x, residual, out, ids_out=None, weig
            "moe_layer_forward")
 
 
-def layer_stage(cfg, wstruct: MoeWeights, x, topk_weights, stage: int, ws, stream=None):
+def layer_stage(cfg, wstruct: MoeWeights, x, stage: int, ws, stream=None):
     """Re-launch one kernel stage of the last layer_forward on `ws` (measurement aid)."""
-    _check(lib().moe_layer_stage(ctypes.byref(cfg), ctypes.byref(wstruct), _ptr(x), _ptr(topk_weights), stage,
-                                 _ptr(ws), ws.numel(), _stream(stream)), "moe_layer_stage")
+    _check(lib().moe_layer_stage(ctypes.byref(cfg), ctypes.byref(wstruct), _ptr(x), stage, _ptr(ws), ws.numel(),
+                                 _stream(stream)), "moe_layer_stage")
