@@ -136,34 +136,47 @@ def build_instances(spec, L, log_prefix):
 
 
 def time_layer(insts, steps, warmup):
+    """ms per layer forward.  The L instances' forwards are captured in order
+    into one graph (a chain of L layers, as a decoder stack would launch
+    them) plus one single-layer graph per instance for a remainder, so that
+    exactly `steps` forwards run in the timed region."""
     aux = torch.cuda.Stream()
     # eager warm-up (creates the library's fork/join events), then capture
     for inst in insts:
         inst.forward(aux)
     torch.cuda.synchronize()
-    ref_out = insts[0].out.clone()
+    ref_out = [inst.out.clone() for inst in insts]
     cap = torch.cuda.Stream()
     for inst in insts:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
             inst.forward(aux)
         inst.graph = g
+    chain = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(chain, stream=cap):
+        for inst in insts:
+            inst.forward(aux)
     torch.cuda.synchronize()
-    # the captured forward must reproduce the eager result bit for bit, replay after replay
-    for _ in range(3):
-        insts[0].out.fill_(float("nan"))
-        insts[0].graph.replay()
+    # captured forwards must reproduce the eager results bit for bit, replay after replay
+    for rep in range(3):
+        for inst in insts:
+            inst.out.fill_(float("nan"))
+        (chain if rep % 2 else insts[0].graph).replay()
         torch.cuda.synchronize()
-        if not torch.equal(insts[0].out.view(torch.int32), ref_out.view(torch.int32)):
-            raise RuntimeError("graph replay differs from the eager forward")
+        check = insts if rep % 2 else insts[:1]
+        for inst, ref in zip(check, ref_out):
+            if not torch.equal(inst.out.view(torch.int32), ref.view(torch.int32)):
+                raise RuntimeError("graph replay differs from the eager forward")
     L = len(insts)
-    for i in range(warmup):
-        insts[i % L].graph.replay()
+    for i in range(max(1, warmup // L)):
+        chain.replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(steps):
-        insts[i % L].graph.replay()
+    for _ in range(steps // L):
+        chain.replay()
+    for i in range(steps % L):
+        insts[i].graph.replay()
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps

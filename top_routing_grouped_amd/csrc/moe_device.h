@@ -48,6 +48,63 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
+// Faster wave reductions: all-reduce inside each 16-lane row with DPP
+// permutations (xor 1, xor 2 by quad permutes; the 8- and 16-lane mirrors),
+// then the four row results combined through scalar registers.  Fixed
+// combination order, so deterministic; the result is wave-uniform.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_mov_dpp(int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i inside 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i inside 16
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppHalfMirror>(v);
+    v += dpp_f32<kDppMirror>(v);
+    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppMirror>(v));
+    return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_dpp_u64(uint64_t v) {
+    const uint32_t lo = dpp_u32<CTRL>(uint32_t(v)), hi = dpp_u32<CTRL>(uint32_t(v >> 32));
+    const uint64_t o = (uint64_t(hi) << 32) | lo;
+    return o > v ? o : v;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+    const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), l));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), l));
+    return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+    v = max_dpp_u64<kDppXor1>(v);
+    v = max_dpp_u64<kDppXor2>(v);
+    v = max_dpp_u64<kDppHalfMirror>(v);
+    v = max_dpp_u64<kDppMirror>(v);
+    uint64_t a = readlane_u64(v, 0), b = readlane_u64(v, 16), c = readlane_u64(v, 32), d = readlane_u64(v, 48);
+    a = a > b ? a : b;
+    c = c > d ? c : d;
+    return a > c ? a : c;
+}
+
 // Total order on floats as unsigned integers (larger float -> larger key).
 __device__ __forceinline__ uint32_t orderable(float f) {
     uint32_t u = __float_as_uint(f);

@@ -139,62 +139,74 @@ __device__ __forceinline__ void mma_chunk(f32x4& acc, const Frag<F32>& a, const 
 }
 
 // --------------------------------------------------------------- small-T tiles
-// Small T*K: workgroup item 0 is the shared expert (all T tokens, when the
-// layer has one); item 1 + a is the a-th distinct expert among the T*K
-// routed pairs in ascending expert id, and m-tile z takes its pairs
-// [16z, 16z + 16) in ascending pair id.  The routing ids are read directly:
-// a bit set of the experts present (LDS atomics), the a-th set bit, and a
-// ballot rank of the matching pairs.  Returns the row count (0: no work).
-__device__ int small_tile(const GemmArgs& a, int item, int mt, int* rows, int* e_out) {
-    __shared__ uint32_t pres[32];
-    __shared__ int meta[2];
-    __shared__ int wsum[4];
-    const int tid = threadIdx.x;
-    const int TK = a.n_pairs;
+// Small T*K (<= 256 pairs): workgroup item 0 is the shared expert (all T
+// tokens, when the layer has one); item 1 + a is the a-th distinct expert
+// among the routed pairs in ascending expert id, and m-tile z takes its
+// pairs [16z, 16z + 16) in ascending pair id.  Every wave derives this on
+// its own from the routing ids (a bit set of the experts present in the
+// wave's LDS slice, the a-th set bit, ballot ranks of the matching pairs),
+// so no workgroup barrier is needed; all waves reach the same answer.
+// Returns the row count (0: no work); rows_w[0..count) are pair ids
+// (routed) or token ids (shared).
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ int small_tile(const GemmArgs& a, int item, int mt, int* rows_w, int* e_out) {
+    __shared__ uint32_t pres_all[4][32];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (item < 0) {  // shared expert: tokens 16*mt + i
-        const int cnt = min(16, a.n_tokens - 16 * mt);
-        if (tid < 16) rows[tid] = 16 * mt + tid;
+        if (lane < 16) rows_w[lane] = 16 * mt + lane;
         *e_out = -1;
-        __syncthreads();
-        return max(cnt, 0);
+        wave_lds_fence();
+        return max(0, min(16, a.n_tokens - 16 * mt));
     }
-    if (tid < 32) pres[tid] = 0;
-    __syncthreads();
-    for (int p = tid; p < TK; p += 256) {
-        const int e = a.ids[p];
-        if (e >= 0 && e < a.n_experts) atomicOr(&pres[e >> 5], 1u << (e & 31));
+    uint32_t* pres = pres_all[wave];
+    if (lane < 32) pres[lane] = 0;
+    wave_lds_fence();
+    const int TK = a.n_pairs;
+    int idv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int p = lane + 64 * j;
+        int e = p < TK ? a.ids[p] : -1;
+        if (e < 0 || e >= a.n_experts) e = -1;
+        idv[j] = e;
+        if (e >= 0) atomicOr(&pres[e >> 5], 1u << (e & 31));
     }
-    __syncthreads();
-    if (tid == 0) {
-        int left = item, found = -1;
-        for (int w = 0; w < (a.n_experts + 31) / 32 && found < 0; ++w) {
-            uint32_t bits = pres[w];
-            const int c = __popc(bits);
-            if (left < c) {
-                for (int i = 0; i < left; ++i) bits &= bits - 1;
-                found = w * 32 + __ffs(bits) - 1;
-            }
-            left -= c;
-        }
-        meta[0] = found;
+    wave_lds_fence();
+    const uint32_t word = lane < 32 ? pres[lane] : 0u;
+    const int c = __popc(word);
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
     }
-    __syncthreads();
-    const int e = meta[0];
+    const uint64_t ball = __ballot(lane < 32 && incl > item);
+    if (ball == 0) {
+        *e_out = -1;
+        return 0;
+    }
+    const int w = __ffsll((unsigned long long)ball) - 1;
+    const int before = __builtin_amdgcn_readlane(incl - c, w);
+    uint32_t bits = uint32_t(__builtin_amdgcn_readlane(int(word), w));
+    for (int i = before; i < item; ++i) bits &= bits - 1;
+    const int e = w * 32 + __ffs(bits) - 1;
     *e_out = e;
-    if (e < 0) return 0;
-    const int lane = tid & 63, wave = tid >> 6;
-    const bool m = tid < TK && a.ids[tid] == e;  // TK <= 256: one pair per thread
-    const uint64_t b = __ballot(m);
     const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    if (lane == 0) wsum[wave] = __popcll(b);
-    __syncthreads();
-    int off = 0;
-    for (int w = 0; w < wave; ++w) off += wsum[w];
-    const int pos = off + __popcll(b & lt) - 16 * mt;
-    if (m && pos >= 0 && pos < 16) rows[pos] = tid;
-    const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-    return max(0, min(16, total - 16 * mt));
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bool m = idv[j] == e;
+        const uint64_t b = __ballot(m);
+        const int pos = base + __popcll(b & lt) - 16 * mt;
+        if (m && pos >= 0 && pos < 16) rows_w[pos] = lane + 64 * j;
+        base += __popcll(b);
+    }
+    wave_lds_fence();
+    return max(0, min(16, base - 16 * mt));
 }
 
 // --------------------------------------------------------------- kernel
@@ -214,7 +226,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     static_assert(!SMALL || TF == 1, "small-T tiles are 16 rows");
 
     // ---- tile: expert (bank) e, rows [begin, begin + count) or explicit rows (small T)
-    __shared__ int srows[16];
+    __shared__ int srows_all[4][16];
+    int* srows = srows_all[threadIdx.x >> 6];
     int e = 0, begin = 0, count;
     bool shared_item = false;
     int N = a.N, K = a.K;
@@ -416,7 +429,10 @@ static hipError_t launch_cfg(const GemmArgs& a, int grid_x, int tf, hipStream_t 
     constexpr int SPAN = 4 * WTraits<WK>::KL;
     const bool ksplit4 = (kwg % (4 * SPAN) == 0);
     const bool ksplit2 = (kwg % (2 * SPAN) == 0);
-    if (tf == 1 || SMALL) {
+    if (MODE == kSmallDown && kwg % SPAN == 0) {
+        dim3 g(grid_x, (nrows + 63) / 64, ks);
+        gemm_kernel<MODE, WK, OUTBF, 1, 4, 1><<<g, 256, 0, s>>>(a);
+    } else if (tf == 1 || SMALL) {
         if (ksplit4) {
             dim3 g(grid_x, (nrows + 15) / 16, ks);
             gemm_kernel<MODE, WK, OUTBF, 1, 1, 4><<<g, 256, 0, s>>>(a);

@@ -31,11 +31,11 @@ __global__ __launch_bounds__(256) void route_select_kernel(SelParams P, GatePara
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     if (t >= P.T) return;  // no block-wide barrier below
-    float gl = 0.f;
-    if (G.w) gl = wave_dot_row(G.x, G.w, t, G.D, G.x_f32 != 0);
     int id;
     float w;
     select_token<NV>(P, t, sel_s[wave], sig_s[wave], &id, &w);
+    float gl = 0.f;
+    if (G.w) gl = wave_dot_row(G.x, G.w, t, G.D, G.x_f32 != 0);
     if (lane < P.K) {
         const size_t o = size_t(t) * P.K + lane;
         ids[o] = id;

@@ -82,7 +82,7 @@ __device__ __forceinline__ float wave_dot_row(const void* x, const void* w, int 
             }
         }
     }
-    return wave_sum(acc);
+    return wave_sum_dpp(acc);
 }
 
 // Selects token t's experts; lane k < K returns slot k in (*id, *w).
@@ -106,12 +106,12 @@ __device__ __forceinline__ void select_token(const SelParams& P, int t, float* s
         float m = v[0];
 #pragma unroll
         for (int j = 1; j < NV; ++j) m = fmaxf(m, v[j]);
-        m = wave_max(m);
+        m = wave_max_dpp(m);
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < NV; ++j)
             if (lane + 64 * j < E) s += __expf(v[j] - m);
-        s = wave_sum(s);
+        s = wave_sum_dpp(s);
         float my_z = -INFINITY;
         for (int k = 0; k < K; ++k) {
             uint64_t best = 0;
@@ -123,7 +123,7 @@ __device__ __forceinline__ void select_token(const SelParams& P, int t, float* s
                     best = key > best ? key : best;
                 }
             }
-            best = wave_max_u64(best);
+            best = wave_max_u64_dpp(best);
             const int idx = min(max(key_index(best), 0), E - 1);
             if ((idx & 63) == lane) taken |= 1u << (idx >> 6);
             if (lane == k) {
@@ -132,7 +132,7 @@ __device__ __forceinline__ void select_token(const SelParams& P, int t, float* s
             }
         }
         const float p = lane < K ? __expf(my_z - m) / s : 0.f;
-        const float denom = fmaxf(wave_sum(p), kClamp);
+        const float denom = fmaxf(wave_sum_dpp(p), kClamp);
         *id_out = my_id;
         *w_out = p / denom;
         return;
@@ -167,7 +167,7 @@ __device__ __forceinline__ void select_token(const SelParams& P, int t, float* s
     uint64_t kept = 0;
     for (int g = 0; g < P.TG; ++g) {
         uint64_t key = (lane < G && !((kept >> lane) & 1ull)) ? sel_key(gscore, lane) : 0;
-        key = wave_max_u64(key);
+        key = wave_max_u64_dpp(key);
         kept |= 1ull << min(max(key_index(key), 0), G - 1);
     }
     for (int k = 0; k < K; ++k) {
@@ -180,13 +180,13 @@ __device__ __forceinline__ void select_token(const SelParams& P, int t, float* s
                 best = key > best ? key : best;
             }
         }
-        best = wave_max_u64(best);
+        best = wave_max_u64_dpp(best);
         const int idx = min(max(key_index(best), 0), E - 1);
         if ((idx & 63) == lane) taken |= 1u << (idx >> 6);
         if (lane == k) my_id = idx;
     }
     const float s = lane < K ? sig_s[my_id] : 0.f;
-    const float denom = fmaxf(wave_sum(s), kClamp);
+    const float denom = fmaxf(wave_sum_dpp(s), kClamp);
     *id_out = my_id;
     *w_out = P.scaling * s / denom;
     wave_lds_sync();  // sel_s/sig_s are reused by the wave's next token
