@@ -309,6 +309,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+                    help="profiling aid: run one workload and print its log line only")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -320,7 +322,12 @@ def main():
     torch.cuda.set_device(0)
     moe.lib()
 
+    if args.only == "prefill":
+        run_workload("qwen_prefill_skew", 4096, min(args.instances, 4), args.steps, args.warmup, args.stage_reps)
+        return
     dec = run_workload("qwen_decode", 8, args.instances, args.steps, args.warmup, args.stage_reps)
+    if args.only == "decode":
+        return
     spec = dec["spec"]
     gu_traffic = traffic_record("gateup", "qwen_decode_T8", dec["gateup_bytes"])
     line = {

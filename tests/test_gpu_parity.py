@@ -111,9 +111,9 @@ def test_permute_bit_exact(T, E, K, mode):
     np.testing.assert_array_equal(sp, ref.sorted_pairs)
 
 
-def test_permute_drops_out_of_range_ids():
+@pytest.mark.parametrize("T,E,K", [(50, 64, 4), (3000, 256, 4)])
+def test_permute_drops_out_of_range_ids(T, E, K):
     rng = np.random.default_rng(3)
-    T, E, K = 50, 64, 4
     ids = np.stack([rng.permutation(E)[:K] for _ in range(T)])
     ids[3, 1] = -5
     ids[7, 0] = E + 3

@@ -41,15 +41,30 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BW * RS];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BT * RS];
 
+    // XCD-aware order: workgroups are dispatched to the 8 XCDs round-robin,
+    // so block b runs on XCD b % 8.  Each XCD takes one contiguous run of the
+    // (tile, row block) work list, row block fastest: the row blocks of a
+    // token tile (same gathered token rows) and neighbouring tiles of the same
+    // expert (same weight rows) then share that XCD's L2.
+    constexpr bool DUAL_ = DUAL;
+    const int nrb = DUAL_ ? (a.N + 63) / 64 : (a.N + BW - 1) / BW;
+    const int n_tiles_real = ROUTED ? *a.n_tiles : (a.n_rows + BT - 1) / BT;
+    const int n_items = n_tiles_real * nrb;
+    const int chunk = (n_items + 7) / 8;
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    if (local >= chunk) return;
+    const int item = xcd * chunk + local;
+    if (item >= n_items) return;
+    const int tile = item / nrb;
+    const int row_blk = item - tile * nrb;
+
     int e = 0, begin, count;
     if constexpr (ROUTED) {
-        const int tile = blockIdx.x;
-        if (tile >= *a.n_tiles) return;
         const int4 t = a.tiles[tile];
         e = t.x; begin = t.y; count = t.z;
         if (e < 0 || e >= a.n_banks || begin < 0 || count <= 0 || begin + count > a.n_pairs) return;
     } else {
-        begin = blockIdx.x * BT;
+        begin = tile * BT;
         count = min(BT, a.n_rows - begin);
         if (count <= 0) return;
     }
@@ -57,8 +72,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int q = lane >> 4, r = lane & 15;
     const int wm = wave & 1, wn = wave >> 1;
-    // weight-row block: gate/up covers features [f0, f0+64) of both banks
-    const int row_blk = blockIdx.y;
+    // weight-row block row_blk: gate/up covers features [64*row_blk, +64) of both banks
 
     // ---- global load assignment: 4 pieces of 16 B per thread per operand
     // piece p = tid + 256*i: row p/8, 16-byte column p%8 (8 threads per 128-byte row segment)
@@ -210,8 +224,9 @@ int tiled_rows() { return BT; }
 hipError_t launch_gemm_tiled(int mode, bool outbf, const GemmArgs& a, int grid_x, hipStream_t s) {
     if (grid_x <= 0) return hipSuccess;
     const bool dual = (mode == kRoutedGateUp || mode == kDenseGateUp);
-    const int gy = dual ? (a.N + 63) / 64 : (a.N + BW - 1) / BW;
-    const dim3 g(grid_x, gy);
+    const long long nrb = dual ? (a.N + 63) / 64 : (a.N + BW - 1) / BW;
+    const long long items = (long long)grid_x * nrb;
+    const dim3 g(unsigned(8 * ((items + 7) / 8)));
     switch (mode) {
         case kRoutedGateUp: gemm_tiled_kernel<kRoutedGateUp, true><<<g, kThreads, 0, s>>>(a); break;
         case kRoutedDown:

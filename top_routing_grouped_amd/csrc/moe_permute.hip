@@ -36,8 +36,78 @@ int max_tiles_for(int n_pairs, int E, int tile_rows) {
     return int(((long long)n_pairs + act * (tile_rows - 1)) / tile_rows);
 }
 
+// Many pairs: one workgroup per expert.  Every workgroup builds the full
+// per-expert histogram in LDS (the same in all of them), takes its expert's
+// offset, active-list slot and first tile from prefix sums over the smaller
+// experts, and gathers its expert's pair ids in ascending order with
+// per-wave ballots.  No cross-workgroup communication, so the result is the
+// same stable order as the single-workgroup permute.
+__global__ __launch_bounds__(kPermThreads) void permute_wide_kernel(PermParams P) {
+    extern __shared__ int hist[];  // [E] then 32 scratch ints
+    int* sh = hist + P.E;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = P.E, me = blockIdx.x;
+    for (int e = tid; e < E; e += kPermThreads) hist[e] = 0;
+    __syncthreads();
+    for (int p = tid; p < P.n_pairs; p += kPermThreads) {
+        const int e = P.ids[p];
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    const int c = tid < E ? hist[tid] : 0;
+    const int nt = (c + P.tile_rows - 1) / P.tile_rows;
+    int total, n_act, n_tiles;
+    const int off = block_exclusive_scan(c, &total, sh);
+    const int apos = block_exclusive_scan(c > 0 ? 1 : 0, &n_act, sh);
+    const int tpos = block_exclusive_scan(nt, &n_tiles, sh);
+    __shared__ int mine[4];
+    if (tid == me) {
+        mine[0] = off;
+        mine[1] = c;
+        mine[2] = apos;
+        mine[3] = tpos;
+    }
+    __syncthreads();
+    const int base = mine[0], cnt = mine[1];
+    if (tid == 0) {
+        P.offsets[me] = base;
+        if (cnt > 0) {
+            P.active[mine[2]] = me;
+            if (P.tiles) write_tiles(P.tiles, mine[3], me, base, cnt, P.tile_rows, P.max_tiles);
+        }
+        if (me == 0) {
+            P.offsets[E] = total;
+            *P.n_active = n_act;
+            if (P.n_tiles) *P.n_tiles = min(n_tiles, P.max_tiles);
+        }
+    }
+    if (cnt == 0) return;  // uniform
+    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    int running = 0;
+    for (int r0 = 0; r0 < P.n_pairs; r0 += kPermThreads) {
+        const int p = r0 + tid;
+        const bool m = p < P.n_pairs && P.ids[p] == me;
+        const uint64_t b = __ballot(m);
+        if (lane == 0) sh[wave] = __popcll(b);
+        __syncthreads();
+        int before = running, sum = 0;
+        for (int w = 0; w < kPermWaves; ++w) {
+            const int v = sh[w];
+            if (w < wave) before += v;
+            sum += v;
+        }
+        if (m) P.sorted_pairs[base + before + __popcll(b & lt)] = p;
+        running += sum;
+        __syncthreads();
+    }
+}
+
 hipError_t launch_permute(const PermParams& P, hipStream_t s) {
-    permute_kernel<<<1, kPermThreads, permute_smem_bytes(P.E), s>>>(P);
+    if (P.n_pairs >= 4096) {
+        permute_wide_kernel<<<P.E, kPermThreads, size_t(P.E + 32) * 4, s>>>(P);
+    } else {
+        permute_kernel<<<1, kPermThreads, permute_smem_bytes(P.E), s>>>(P);
+    }
     return hipGetLastError();
 }
 

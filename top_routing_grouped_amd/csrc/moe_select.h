@@ -34,13 +34,6 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
-// Logit of expert e for token t: sum of `ksplit` partial sums in fixed order.
-__device__ __forceinline__ float logit_at(const float* __restrict__ z, int ksplit, size_t split_stride, size_t idx) {
-    float v = z[idx];
-    for (int s = 1; s < ksplit; ++s) v += z[idx + s * split_stride];
-    return v;
-}
-
 struct SelParams {
     const float* logits;  // [ksplit][T][E]
     int ksplit;
@@ -94,11 +87,24 @@ __device__ __forceinline__ void select_token(const SelParams& P, int t, float* s
     const int E = P.E, K = P.K;
     const size_t stride = size_t(P.T) * E;
     const size_t row = size_t(t) * E;
-    float v[NV];
+    // all partial logits are loaded before any is summed (one memory round trip)
+    constexpr int kMaxSplit = 8;
+    float part[NV][kMaxSplit];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int e = lane + 64 * j;
-        v[j] = e < E ? logit_at(P.logits, P.ksplit, stride, row + e) : -INFINITY;
+#pragma unroll
+        for (int s = 0; s < kMaxSplit; ++s)
+            part[j][s] = (e < E && s < P.ksplit) ? P.logits[row + e + s * stride] : 0.f;
+    }
+    float v[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        float acc = part[j][0];
+#pragma unroll
+        for (int s = 1; s < kMaxSplit; ++s)
+            if (s < P.ksplit) acc += part[j][s];
+        v[j] = lane + 64 * j < E ? acc : -INFINITY;
     }
     uint32_t taken = 0;
     int my_id = 0;
