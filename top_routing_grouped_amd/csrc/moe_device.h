@@ -123,4 +123,8 @@ __device__ __forceinline__ float key_score(uint64_t key) { return from_orderable
 
 __device__ __forceinline__ float sigmoidf_(float v) { return 1.0f / (1.0f + __expf(-v)); }
 
+// A value every lane of the wave holds alike, moved to a scalar register so
+// branches on it are scalar and addresses built from it stay scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 }  // namespace moe

@@ -105,7 +105,8 @@ __device__ __forceinline__ void load_w(Frag<WK == kWF32>& f, const void* w, cons
 }
 
 // Activation chunk (bf16 or fp32 rows) in the weights' K order, zeros for an
-// absent token.
+// absent token (with 1-2 tokens per expert most lanes hold none, and skipping
+// their loads measures faster than reading a stand-in row).
 template <int WK>
 __device__ __forceinline__ void load_x(Frag<WK == kWF32>& f, const void* rowp, int kc, int q) {
     if constexpr (WK == kWF32) {
@@ -234,7 +235,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     const void *w0 = a.w0, *s0 = a.s0, *m0 = a.m0, *w1 = a.w1, *s1 = a.s1, *m1 = a.m1;
     if constexpr (SMALL) {
         const int item = int(blockIdx.x) - (a.has_shared ? 1 : 0);
-        count = small_tile(a, item, blockIdx.z, srows, &e);
+        count = uniform(small_tile(a, item, blockIdx.z, srows, &e));
+        e = uniform(e);
         if (count <= 0) return;
         if (item < 0) {
             shared_item = true;
@@ -244,9 +246,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         }
     } else if constexpr (ROUTED) {
         const int tile = blockIdx.x;
-        if (tile >= *a.n_tiles) return;
+        if (tile >= uniform(*a.n_tiles)) return;
         const int4 t = a.tiles[tile];
-        e = t.x; begin = t.y; count = t.z;
+        e = uniform(t.x); begin = uniform(t.y); count = uniform(t.z);
         if (e < 0 || e >= a.n_banks || begin < 0 || count <= 0 || begin + count > a.n_pairs) return;
     } else {
         begin = blockIdx.x * BM;

@@ -4,17 +4,22 @@
 // grouping follows the "Intel SYCL path": one tile works on one active
 // expert's packed pairs, so each weight block is loaded for up to 128 of them).
 //
-// Workgroup tile: 128 weight rows x 128 token rows, K in steps of 64, two
-// LDS buffers (one barrier per step; the next step's global loads are in
-// flight while the current step's MFMAs run).  For gate/up the 128 weight
-// rows are 64 gate rows and the same 64 up rows, so each lane ends with
-// matching gate and up accumulators and applies SwiGLU in registers.
-// 4 waves in a 2 x 2 grid; each wave owns 64 weight rows x 64 tokens as
-// 4 x 4 fragments of v_mfma_f32_16x16x32_bf16 (weights = A, tokens = B).
-// LDS rows are padded to 144 bytes so a wave's 16-byte fragment reads hit
-// distinct banks.
+// Workgroup tile: 128 weight rows x 128 token rows, K in steps of 64.  Two
+// LDS buffers and two register buffers: the global loads of step k+2 are
+// issued while step k's MFMAs run and step k+1's data moves from registers to
+// LDS, one barrier per step.  For gate/up the 128 weight rows are 64 gate
+// rows and the same 64 up rows, so each lane ends with matching gate and up
+// accumulators and applies SwiGLU in registers.  4 waves in a 2 x 2 grid;
+// each wave owns 64 weight rows x 64 tokens as 4 x 4 fragments of
+// v_mfma_f32_16x16x32_bf16 (weights = A, tokens = B); token fragments past
+// the tile's row count issue no MFMAs.  LDS rows are 128 bytes with the
+// 16-byte pieces of row r XOR-swizzled by (r/2) mod 8, so both the 8-lanes-
+// per-row stores and the 16-rows-per-fragment reads of a wave touch 16
+// distinct 4-bank groups.
 #include "moe_device.h"
 #include "moe_kernels.h"
+
+#include <type_traits>
 
 namespace moe {
 
@@ -25,8 +30,27 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int BW = 128;       // weight rows per tile
 constexpr int BT = 128;       // token rows per tile
 constexpr int BK = 64;        // K per step
-constexpr int RS = BK + 8;    // LDS row stride in bf16 elements (144 bytes)
 constexpr int kThreads = 256;
+
+// LDS row layout: 0 = rows padded to 144 bytes, 1 = 128-byte rows with the
+// 16-byte pieces XOR-swizzled by (r/2) mod 8, 2 = swizzled by r mod 8.
+#ifndef MOE_TILED_LDS_LAYOUT
+#define MOE_TILED_LDS_LAYOUT 1
+#endif
+// global prefetch distance in K steps (1 or 2)
+#ifndef MOE_TILED_PREFETCH
+#define MOE_TILED_PREFETCH 2
+#endif
+constexpr int kLayout = MOE_TILED_LDS_LAYOUT;
+constexpr int kPrefetch = MOE_TILED_PREFETCH;
+constexpr int RS = kLayout == 0 ? BK + 8 : BK;  // LDS row stride (elements)
+
+// element offset of 16-byte piece p of LDS row r
+__device__ __forceinline__ int lds_off(int r, int p) {
+    if constexpr (kLayout == 0) return r * RS + (p << 3);
+    else if constexpr (kLayout == 1) return r * RS + ((p ^ ((r >> 1) & 7)) << 3);
+    else return r * RS + ((p ^ (r & 7)) << 3);
+}
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* base) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base));
@@ -48,7 +72,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
     // expert (same weight rows) then share that XCD's L2.
     constexpr bool DUAL_ = DUAL;
     const int nrb = DUAL_ ? (a.N + 63) / 64 : (a.N + BW - 1) / BW;
-    const int n_tiles_real = ROUTED ? *a.n_tiles : (a.n_rows + BT - 1) / BT;
+    const int n_tiles_real = ROUTED ? uniform(*a.n_tiles) : (a.n_rows + BT - 1) / BT;
     const int n_items = n_tiles_real * nrb;
     const int chunk = (n_items + 7) / 8;
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
@@ -61,7 +85,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
     int e = 0, begin, count;
     if constexpr (ROUTED) {
         const int4 t = a.tiles[tile];
-        e = t.x; begin = t.y; count = t.z;
+        e = uniform(t.x); begin = uniform(t.y); count = uniform(t.z);
         if (e < 0 || e >= a.n_banks || begin < 0 || count <= 0 || begin + count > a.n_pairs) return;
     } else {
         begin = tile * BT;
@@ -94,34 +118,40 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
             wb = static_cast<const uint16_t*>(a.w0);
             wr = row_blk * BW + row;
         }
-        wsrc[i] = (wr < N) ? wb + (size_t(e) * N + wr) * K + col : nullptr;
-        const uint16_t* xs = nullptr;
+        // Every load is unconditional (no branch, so no wait for older loads
+        // inside the K loop): absent weight rows and token rows read a valid
+        // row instead; they only feed output rows / token columns that are
+        // never stored.
+        wsrc[i] = wb + (size_t(e) * N + min(wr, N - 1)) * K + col;
+        int arow = -1;
         if (row < count) {
-            int arow;
             if constexpr (MODE == kRoutedGateUp) {
                 const int pair = a.pairs[begin + row];
                 arow = (pair >= 0 && pair < a.n_pairs) ? pair / a.topk : -1;
             } else {
                 arow = begin + row;
             }
-            if (arow >= 0 && arow < a.n_act_rows) xs = static_cast<const uint16_t*>(a.act) + size_t(arow) * K + col;
         }
-        xsrc[i] = xs;
+        if (arow < 0 || arow >= a.n_act_rows) arow = 0;
+        xsrc[i] = static_cast<const uint16_t*>(a.act) + size_t(arow) * K + col;
     }
 
-    u32x4 wreg[4], xreg[4];
-    auto gload = [&](int k0) {
+    u32x4 wreg[2][4], xreg[2][4];
+    auto gload = [&](int rb, int k0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            wreg[i] = wsrc[i] ? *reinterpret_cast<const u32x4*>(wsrc[i] + k0) : u32x4{0, 0, 0, 0};
-            xreg[i] = xsrc[i] ? *reinterpret_cast<const u32x4*>(xsrc[i] + k0) : u32x4{0, 0, 0, 0};
+            wreg[rb][i] = *reinterpret_cast<const u32x4*>(wsrc[i] + k0);
+            xreg[rb][i] = *reinterpret_cast<const u32x4*>(xsrc[i] + k0);
         }
     };
-    auto lstore = [&](int buf) {
+    int soff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) soff[i] = lds_off(lrow[i], lcol[i] >> 3);
+    auto lstore = [&](int rb, int buf) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<u32x4*>(&As[buf][lrow[i] * RS + lcol[i]]) = wreg[i];
-            *reinterpret_cast<u32x4*>(&Bs[buf][lrow[i] * RS + lcol[i]]) = xreg[i];
+            *reinterpret_cast<u32x4*>(&As[buf][soff[i]]) = wreg[rb][i];
+            *reinterpret_cast<u32x4*>(&Bs[buf][soff[i]]) = xreg[rb][i];
         }
     };
 
@@ -135,6 +165,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
             arow_l[i] = wm * 64 + i * 16 + r;
     }
     const int brow_l = wn * 64 + r;
+    // token fragments of this wave that hold at least one row
+    const int nfrag = uniform(min(4, max(0, (count - wn * 64 + 15) / 16)));
 
     f32x4 acc[4][4];
 #pragma unroll
@@ -143,28 +175,64 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = K / BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
+    // One K step: MFMAs from LDS buffer `cur`.  FULL: all 4 token fragments
+    // hold rows (no per-fragment test inside the loop).
+    auto compute = [&](int cur, auto full) {
+        constexpr bool FULL = decltype(full)::value;
 #pragma unroll
         for (int ks = 0; ks < BK / 32; ++ks) {
             bf16x8 af[4], bfr[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = lds_frag(&As[cur][arow_l[i] * RS + ks * 32 + q * 8]);
+            for (int i = 0; i < 4; ++i) af[i] = lds_frag(&As[cur][lds_off(arow_l[i], ks * 4 + q)]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bfr[j] = lds_frag(&Bs[cur][(brow_l + j * 16) * RS + ks * 32 + q * 8]);
+            for (int j = 0; j < 4; ++j) bfr[j] = lds_frag(&Bs[cur][lds_off(brow_l + j * 16, ks * 4 + q)]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j) {
+                if (!FULL && j >= nfrag) break;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int i = 0; i < 4; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            }
         }
-        if (kt + 1 < nk) lstore(cur ^ 1);
-        __syncthreads();
-    }
+    };
+    auto main_loop = [&](auto full) {
+        if constexpr (kPrefetch == 1) {
+            gload(0, 0);
+            lstore(0, 0);
+            __syncthreads();
+            for (int kt = 0; kt < nk; ++kt) {
+                const int cur = kt & 1;
+                if (kt + 1 < nk) gload(0, (kt + 1) * BK);
+                compute(cur, full);
+                if (kt + 1 < nk) lstore(0, cur ^ 1);
+                __syncthreads();
+            }
+        } else {
+            // register buffers alternate with the K step; the loop is unrolled by
+            // two so each buffer index is a compile-time constant
+            gload(0, 0);
+            if (nk > 1) gload(1, BK);
+            lstore(0, 0);
+            __syncthreads();
+            for (int kt = 0; kt < nk; kt += 2) {
+                if (kt + 2 < nk) gload(0, (kt + 2) * BK);
+                compute(0, full);
+                if (kt + 1 < nk) lstore(1, 1);
+                __syncthreads();
+                if (kt + 1 >= nk) break;
+                if (kt + 3 < nk) gload(1, (kt + 3) * BK);
+                compute(1, full);
+                if (kt + 2 < nk) lstore(0, 0);
+                __syncthreads();
+            }
+        }
+    };
+    // the branch is on a wave-uniform value; a workgroup's waves may take
+    // different branches (both reach the same barriers)
+    if (nfrag == 4)
+        main_loop(std::true_type{});
+    else
+        main_loop(std::false_type{});
 
     // ---- epilogue: lane holds rows (4q .. 4q+3) of fragment i, token column r of fragment j
 #pragma unroll
