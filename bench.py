@@ -272,6 +272,17 @@ def clone_weights_to_host(w):
     return c
 
 
+def copy_calibration(nbytes=1 << 30):
+    """One device-to-device copy of `nbytes` (reads and writes nbytes each),
+    whose counter readings scale FETCH_SIZE / WRITE_SIZE to bytes."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {nbytes} bytes")
+
+
 def run_workload(name, T, L, steps, warmup, stage_reps):
     spec = WORKLOADS[name].with_tokens(T)
     insts = build_instances(spec, L, f"{name} T={T}")
@@ -309,6 +320,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="profiling aid: finish with a 1 GiB device-to-device copy (known bytes for counter scaling)")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="profiling aid: run one workload and print its log line only")
     args = ap.parse_args()
@@ -327,6 +340,8 @@ def main():
         return
     dec = run_workload("qwen_decode", 8, args.instances, args.steps, args.warmup, args.stage_reps)
     if args.only == "decode":
+        if args.copy_calibration:
+            copy_calibration()
         return
     spec = dec["spec"]
     gu_traffic = traffic_record("gateup", "qwen_decode_T8", dec["gateup_bytes"])
