@@ -209,21 +209,41 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
             }
         } else {
             // register buffers alternate with the K step; the loop is unrolled by
-            // two so each buffer index is a compile-time constant
+            // two so each buffer index is a compile-time constant.  The steady
+            // state has no conditional load (a branch there makes the compiler
+            // wait for the loads in flight); sched_barrier keeps each step's
+            // prefetch at the top of the step, ahead of its MFMAs.
             gload(0, 0);
             if (nk > 1) gload(1, BK);
             lstore(0, 0);
             __syncthreads();
-            for (int kt = 0; kt < nk; kt += 2) {
-                if (kt + 2 < nk) gload(0, (kt + 2) * BK);
+            int kt = 0;
+            for (; kt + 3 < nk; kt += 2) {
+                gload(0, (kt + 2) * BK);
+                __builtin_amdgcn_sched_barrier(0);
                 compute(0, full);
-                if (kt + 1 < nk) lstore(1, 1);
+                lstore(1, 1);
                 __syncthreads();
-                if (kt + 1 >= nk) break;
-                if (kt + 3 < nk) gload(1, (kt + 3) * BK);
+                gload(1, (kt + 3) * BK);
+                __builtin_amdgcn_sched_barrier(0);
                 compute(1, full);
-                if (kt + 2 < nk) lstore(0, 0);
+                lstore(0, 0);
                 __syncthreads();
+            }
+            // tail: 1 step (nk == 1), else 2 or 3 steps left; register buffer 1
+            // holds step kt + 1 when nk > 1
+            const int left = nk - kt;
+            if (left == 3) gload(0, (kt + 2) * BK);
+            compute(0, full);
+            if (left >= 2) {
+                lstore(1, 1);
+                __syncthreads();
+                compute(1, full);
+                if (left == 3) {
+                    lstore(0, 0);
+                    __syncthreads();
+                    compute(0, full);
+                }
             }
         }
     };
