@@ -55,11 +55,16 @@ bool dense_tiled(const moe_config& c, moe_dtype d) { return c.n_tokens >= 128 &&
 bool small_path(const moe_config& c) { return !routed_large(c) && (int64_t)c.n_tokens * c.top_k <= 256; }
 int h_ld(const moe_config& c) { return std::max(c.d_ff, c.d_ff_shared); }
 
-// Router logits: K split over workgroups for small T (each wave one chunk).
+// Router logits: for small T, K is split over up to 8 workgroups (partial
+// planes the selection sums), each split a whole number of 4-wave chunks; 1
+// when no such split exists (a split must divide d_model exactly, or part of
+// the reduction would be dropped).
 int router_ksplit(const moe_config& c) {
     if (c.n_tokens > 64) return 1;
     const int per = 4 * kspan_of(c.router_dtype == MOE_F32 ? MOE_F32 : MOE_BF16);
-    return std::max(1, std::min(c.d_model / per, 8));
+    for (int s = 8; s > 1; --s)
+        if (c.d_model % (s * per) == 0) return s;
+    return 1;
 }
 
 int64_t max_tiles(int64_t n_pairs, int E, int tile_rows) {

@@ -83,6 +83,15 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
     v = fmaxf(v, dpp_f32<kDppMirror>(v));
     return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+    v = max(v, dpp_u32<kDppXor1>(v));
+    v = max(v, dpp_u32<kDppXor2>(v));
+    v = max(v, dpp_u32<kDppHalfMirror>(v));
+    v = max(v, dpp_u32<kDppMirror>(v));
+    const uint32_t a = uint32_t(__builtin_amdgcn_readlane(int(v), 0)), b = uint32_t(__builtin_amdgcn_readlane(int(v), 16));
+    const uint32_t c = uint32_t(__builtin_amdgcn_readlane(int(v), 32)), d = uint32_t(__builtin_amdgcn_readlane(int(v), 48));
+    return max(max(a, b), max(c, d));
+}
 template <int CTRL>
 __device__ __forceinline__ uint64_t max_dpp_u64(uint64_t v) {
     const uint32_t lo = dpp_u32<CTRL>(uint32_t(v)), hi = dpp_u32<CTRL>(uint32_t(v >> 32));

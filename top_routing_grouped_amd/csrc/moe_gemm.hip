@@ -306,7 +306,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         const int kper = ksub / WKS;
         const int kbeg = kbase + wk * kper;
         const int nchunks = kper / SPAN;
-#pragma unroll 2
+        // small T: a wave's chunks (4 at decode shapes) are all requested
+        // before the first is used
+#pragma unroll(SMALL ? 4 : 2)
         for (int c = 0; c < nchunks; ++c) {
             const int kc = kbeg + c * SPAN;
             Frag<F32> wa[NM];

@@ -33,7 +33,16 @@ __global__ __launch_bounds__(256) void route_select_kernel(SelParams P, GatePara
     if (t >= P.T) return;  // no block-wide barrier below
     int id;
     float w;
-    select_token<NV>(P, t, sel_s[wave], sig_s[wave], &id, &w);
+    if (P.family == 0) {
+        const int tt[1] = {t};
+        int ids1[1];
+        float w1[1];
+        select_softmax_lanes<NV, 1>(P, tt, ids1, w1);
+        id = ids1[0];
+        w = w1[0];
+    } else {
+        select_token<NV>(P, t, sel_s[wave], sig_s[wave], &id, &w);
+    }
     float gl = 0.f;
     if (G.w) gl = wave_dot_row(G.x, G.w, t, G.D, G.x_f32 != 0);
     if (lane < P.K) {

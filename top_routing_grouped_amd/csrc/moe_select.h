@@ -78,26 +78,28 @@ __device__ __forceinline__ float wave_dot_row(const void* x, const void* w, int 
     return wave_sum_dpp(acc);
 }
 
-// Selects token t's experts; lane k < K returns slot k in (*id, *w).
-// sel_s/sig_s: this wave's LDS scratch of 64*NV floats each (sigmoid family).
+// Logits of token t for lane's experts lane + 64 j (-inf past E): the K-split
+// partial planes summed in order.
 template <int NV>
-__device__ __forceinline__ void select_token(const SelParams& P, int t, float* sel_s, float* sig_s, int* id_out,
-                                             float* w_out) {
+__device__ __forceinline__ void token_logits(const SelParams& P, int t, float (&v)[NV]) {
     const int lane = threadIdx.x & 63;
-    const int E = P.E, K = P.K;
+    const int E = P.E;
     const size_t stride = size_t(P.T) * E;
     const size_t row = size_t(t) * E;
-    // all partial logits are loaded before any is summed (one memory round trip)
+    // all partial logits are loaded before any is summed (one memory round
+    // trip): the loads are unconditional, from clamped addresses, so that no
+    // branch or register reuse puts a wait between them
     constexpr int kMaxSplit = 8;
     float part[NV][kMaxSplit];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-        const int e = lane + 64 * j;
+        const int e = min(lane + 64 * j, E - 1);
 #pragma unroll
-        for (int s = 0; s < kMaxSplit; ++s)
-            part[j][s] = (e < E && s < P.ksplit) ? P.logits[row + e + s * stride] : 0.f;
+        for (int s = 0; s < kMaxSplit; ++s) {
+            const float* src = P.logits + row + e + min(s, P.ksplit - 1) * stride;
+            part[j][s] = *src;
+        }
     }
-    float v[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         float acc = part[j][0];
@@ -106,6 +108,16 @@ __device__ __forceinline__ void select_token(const SelParams& P, int t, float* s
             if (s < P.ksplit) acc += part[j][s];
         v[j] = lane + 64 * j < E ? acc : -INFINITY;
     }
+}
+
+// Selects the experts of a token from its logits v (token_logits); lane
+// k < K returns slot k in (*id, *w).  sel_s/sig_s: this wave's LDS scratch of
+// 64*NV floats each (sigmoid family).
+template <int NV>
+__device__ __forceinline__ void select_from_logits(const SelParams& P, float (&v)[NV], float* sel_s, float* sig_s,
+                                                   int* id_out, float* w_out) {
+    const int lane = threadIdx.x & 63;
+    const int E = P.E, K = P.K;
     uint32_t taken = 0;
     int my_id = 0;
     if (P.family == 0) {
@@ -196,6 +208,129 @@ __device__ __forceinline__ void select_token(const SelParams& P, int t, float* s
     *id_out = my_id;
     *w_out = P.scaling * s / denom;
     wave_lds_sync();  // sel_s/sig_s are reused by the wave's next token
+}
+
+// Softmax family top-K of B tokens at once (B = 1 or 2; their dependent
+// reduction chains interleave).  Lane l holds the logits of experts NV*l ..
+// NV*l + NV - 1, so a lower lane always holds lower expert ids: each round,
+// every lane offers its best untaken expert (ties to the lower id), the wave
+// takes the maximum of the 32-bit order-preserving score keys, and the lowest
+// lane offering that maximum (one ballot) holds the winner.  Lane k < K
+// returns slot k in (id[b], w[b]).
+template <int NV, int B>
+__device__ __forceinline__ void select_softmax_lanes(const SelParams& P, const int (&t)[B], int (&id)[B],
+                                                     float (&w)[B]) {
+    const int lane = threadIdx.x & 63;
+    const int E = P.E, K = P.K;
+    const size_t stride = size_t(P.T) * E;
+    const bool valid = NV * lane < E;  // E % 16 == 0: all or none of a lane's experts exist
+    float v[B][NV];
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int j = 0; j < NV; ++j) v[b][j] = 0.f;
+    {
+        // every load unconditional, from clamped addresses (no branch or
+        // register reuse puts a wait between them); masked afterwards
+        constexpr int kMaxSplit = 8;
+        float part[B][kMaxSplit][NV];
+        const int l = valid ? lane : 0;
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int s = 0; s < kMaxSplit; ++s) {
+                {
+                    const float* src = P.logits + min(s, P.ksplit - 1) * stride + size_t(t[b]) * E + NV * l;
+                    if constexpr (NV == 1) {
+                        part[b][s][0] = *src;
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < NV; j += 2) {
+                            const float2 u = *reinterpret_cast<const float2*>(src + j);
+                            part[b][s][j] = u.x;
+                            part[b][s][j + 1] = u.y;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int s = 0; s < kMaxSplit; ++s)
+                if (s < P.ksplit)
+#pragma unroll
+                    for (int j = 0; j < NV; ++j) v[b][j] += part[b][s][j];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int j = 0; j < NV; ++j) v[b][j] = valid ? v[b][j] : 0.f;
+    }
+    float m[B], ssum[B];
+    uint32_t key[B][NV], taken[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float lm = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) lm = valid ? fmaxf(lm, v[b][j]) : lm;
+        m[b] = wave_max_dpp(lm);
+        float ls = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            ls += valid ? __expf(v[b][j] - m[b]) : 0.f;
+            key[b][j] = valid ? orderable(v[b][j]) : 0u;  // any real score orders above 0
+        }
+        ssum[b] = wave_sum_dpp(ls);
+        taken[b] = 0;
+    }
+    int my_id[B];
+    uint32_t my_key[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) { my_id[b] = 0; my_key[b] = 0; }
+    for (int k = 0; k < K; ++k) {
+        uint32_t best[B];
+        int bj[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            best[b] = 0;
+            bj[b] = 0;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const bool ok = !((taken[b] >> j) & 1u) && key[b][j] > best[b];
+                best[b] = ok ? key[b][j] : best[b];
+                bj[b] = ok ? j : bj[b];
+            }
+        }
+        uint32_t mx[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) mx[b] = wave_max_u32_dpp(best[b]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const uint64_t ball = __ballot(best[b] == mx[b]);
+            const int wl = __ffsll((unsigned long long)ball) - 1;
+            const int wj = __builtin_amdgcn_readlane(bj[b], wl);
+            if (lane == wl) taken[b] |= 1u << wj;
+            if (lane == k) {
+                my_id[b] = NV * wl + wj;
+                my_key[b] = mx[b];
+            }
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const float p = lane < K ? __expf(from_orderable(my_key[b]) - m[b]) / ssum[b] : 0.f;
+        const float denom = fmaxf(wave_sum_dpp(p), kClamp);
+        id[b] = my_id[b];
+        w[b] = p / denom;
+    }
+}
+
+// Selects token t's experts; lane k < K returns slot k in (*id, *w).
+template <int NV>
+__device__ __forceinline__ void select_token(const SelParams& P, int t, float* sel_s, float* sig_s, int* id_out,
+                                             float* w_out) {
+    float v[NV];
+    token_logits<NV>(P, t, v);
+    select_from_logits<NV>(P, v, sel_s, sig_s, id_out, w_out);
 }
 
 // ------------------------------------------------------------------ permute
