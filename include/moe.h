@@ -134,7 +134,9 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* router,
  *   n_active       [1] int32,
  *   sorted_pairs   [T*K] int32   flat pair ids t*K + k grouped by expert,
  *                                ascending inside each expert (stable).
- * Ids outside [0, E) are not counted and get no row. */
+ * Ids outside [0, E) are not counted and get no row.  ws may be NULL; with a
+ * workspace of moe_workspace_size bytes, 4096 or more pairs are permuted in
+ * parallel chunks (count, scan, scatter) instead of by one workgroup. */
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids,
                        int32_t* expert_offsets, int32_t* active_experts, int32_t* n_active,
                        int32_t* sorted_pairs, void* ws, size_t ws_bytes, moe_stream_t stream);

@@ -77,7 +77,9 @@ def test_route_all_ties_lowest_index(family):
 
 
 # ------------------------------------------------------------------ permute
-def _run_permute(E, K, ids_np):
+def _run_permute(E, K, ids_np, with_ws=True):
+    """Permute through the C ABI; with a workspace, many pairs take the chunked
+    (count / scan / scatter) path, without one the single-workgroup path."""
     T = ids_np.shape[0]
     cfg = moe.make_config(T, 256, E, K, 128, 0)
     ids = torch.from_numpy(ids_np.astype(np.int32)).cuda()
@@ -85,7 +87,8 @@ def _run_permute(E, K, ids_np):
     act = torch.full((E,), -1, dtype=torch.int32, device="cuda")
     na = torch.full((1,), -1, dtype=torch.int32, device="cuda")
     sp = torch.full((T * K,), -1, dtype=torch.int32, device="cuda")
-    moe.permute(cfg, ids, off, act, na, sp)
+    ws = moe.alloc_workspace(cfg) if with_ws else None
+    moe.permute(cfg, ids, off, act, na, sp, ws)
     torch.cuda.synchronize()
     return off.cpu().numpy(), act.cpu().numpy(), int(na.item()), sp.cpu().numpy()
 
@@ -103,12 +106,13 @@ def test_permute_bit_exact(T, E, K, mode):
         p = 1.0 / np.arange(1, E + 1) ** 1.1
         p /= p.sum()
         ids = np.stack([rng.choice(E, K, replace=False, p=p) for _ in range(T)])
-    off, act, na, sp = _run_permute(E, K, ids)
     ref = O.permute(ids, E)
-    np.testing.assert_array_equal(off, ref.offsets)
-    assert na == ref.n_active
-    np.testing.assert_array_equal(act[:na], ref.active)
-    np.testing.assert_array_equal(sp, ref.sorted_pairs)
+    for with_ws in (True, False):
+        off, act, na, sp = _run_permute(E, K, ids, with_ws)
+        np.testing.assert_array_equal(off, ref.offsets)
+        assert na == ref.n_active
+        np.testing.assert_array_equal(act[:na], ref.active)
+        np.testing.assert_array_equal(sp, ref.sorted_pairs)
 
 
 @pytest.mark.parametrize("T,E,K", [(50, 64, 4), (3000, 256, 4)])
@@ -117,7 +121,7 @@ def test_permute_drops_out_of_range_ids(T, E, K):
     ids = np.stack([rng.permutation(E)[:K] for _ in range(T)])
     ids[3, 1] = -5
     ids[7, 0] = E + 3
-    off, act, na, sp = _run_permute(E, K, ids)
+    off, act, na, sp = _run_permute(E, K, ids, with_ws=T * K >= 4096)
     keep = (ids.ravel() >= 0) & (ids.ravel() < E)
     assert off[E] == keep.sum()
     counts = np.bincount(ids.ravel()[keep], minlength=E)

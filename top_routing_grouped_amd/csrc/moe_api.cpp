@@ -60,6 +60,15 @@ int h_ld(const moe_config& c) { return std::max(c.d_ff, c.d_ff_shared); }
 // when no such split exists (a split must divide d_model exactly, or part of
 // the reduction would be dropped).
 int router_ksplit(const moe_config& c) {
+    if (dense_tiled(c, c.router_dtype)) {
+        // LDS-tiled logits: enough K splits for ~256 workgroups, each a
+        // multiple of the 64-wide K step
+        const long long items = (long long)((c.n_tokens + moe::tiled_rows_dense() - 1) / moe::tiled_rows_dense()) *
+                                ((c.n_experts + moe::tiled_rows_dense() - 1) / moe::tiled_rows_dense());
+        int s = int(std::min<long long>(8, std::max<long long>(1, (256 + items - 1) / items)));
+        while (s > 1 && c.d_model % (s * 64)) --s;
+        return s;
+    }
     if (c.n_tokens > 64) return 1;
     const int per = 4 * kspan_of(c.router_dtype == MOE_F32 ? MOE_F32 : MOE_BF16);
     for (int s = 8; s > 1; --s)
@@ -73,7 +82,7 @@ int64_t max_tiles(int64_t n_pairs, int E, int tile_rows) {
 }
 
 struct Layout {
-    size_t logits, gate_logit, ids, wts, offsets, active, n_active, n_tiles, pairs, tiles, h, slots, hs, ys, total;
+    size_t chunk_base, logits, gate_logit, ids, wts, offsets, active, n_active, n_tiles, pairs, tiles, h, slots, hs, ys, total;
 };
 
 Layout layout(const moe_config& c) {
@@ -88,6 +97,7 @@ Layout layout(const moe_config& c) {
         o += align256(bytes);
         return at;
     };
+    L.chunk_base = take(size_t(moe::perm_chunks(int(TK))) * E * 4);
     L.logits = take(size_t(router_ksplit(c)) * T * E * 4);
     L.gate_logit = take(T * 4);
     L.ids = take(TK * 4);
@@ -184,8 +194,8 @@ moe_status stage_logits(const moe_config& c, const Layout& L, void* ws, const vo
     a.act = x; a.n_act_rows = T; a.n_rows = T;
     a.out = at<float>(ws, L.logits);
     a.ksplit = router_ksplit(c);
-    if (a.ksplit == 1 && dense_tiled(c, c.router_dtype)) {
-        HIP_TRY(moe::launch_gemm_tiled(moe::kDenseStore, false, a, (T + moe::tiled_rows() - 1) / moe::tiled_rows(), s));
+    if (dense_tiled(c, c.router_dtype)) {
+        HIP_TRY(moe::launch_gemm_tiled(moe::kDenseStore, false, a, (T + moe::tiled_rows_dense() - 1) / moe::tiled_rows_dense(), s));
         return MOE_OK;
     }
     const int tf = dense_tf(c);
@@ -209,8 +219,10 @@ moe::SelParams sel_params(const moe_config& c, const Layout& L, void* ws, const 
 }
 
 moe::PermParams perm_params(const moe_config& c, const int32_t* ids, int32_t* offsets, int32_t* active,
-                            int32_t* n_active, int32_t* sorted_pairs, int4* tiles, int32_t* n_tiles, int tile_rows) {
+                            int32_t* n_active, int32_t* sorted_pairs, int4* tiles, int32_t* n_tiles, int tile_rows,
+                            int32_t* chunk_base) {
     moe::PermParams Q{};
+    Q.chunk_base = chunk_base;
     Q.ids = ids;
     Q.n_pairs = c.n_tokens * c.top_k;
     Q.E = c.n_experts;
@@ -337,7 +349,7 @@ moe_status stage_shared(const moe_config& c, const Layout& L, void* ws, const vo
     moe::GemmArgs d = gemm_args(w.shared_down, nullptr, c.d_model, c.d_ff_shared, 1);
     d.act = hs; d.n_act_rows = T; d.n_rows = T; d.out = shared_out; d.row_scale = gl;
     if (dense_tiled(c, c.expert_dtype)) {
-        const int g = (T + moe::tiled_rows() - 1) / moe::tiled_rows();
+        const int g = (T + moe::tiled_rows_dense() - 1) / moe::tiled_rows_dense();
         HIP_TRY(moe::launch_gemm_tiled(moe::kDenseGateUp, true, a, g, s));
         HIP_TRY(moe::launch_gemm_tiled(moe::kDenseDown, false, d, g, s));
         return MOE_OK;
@@ -402,15 +414,17 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* 
                        int32_t* active_experts, int32_t* n_active, int32_t* sorted_pairs, void* ws, size_t ws_bytes,
                        moe_stream_t stream) {
     g_err[0] = 0;
-    (void)ws;
-    (void)ws_bytes;
     if (moe_status st = check_config(cfg)) return st;
     if (cfg->n_tokens == 0) return MOE_OK;
     if (!topk_ids || !expert_offsets || !active_experts || !n_active || !sorted_pairs)
         return fail(MOE_ERR_INVALID_ARGUMENT, "NULL tensor argument");
+    // the chunked permute's scratch, when the caller gives a workspace
+    int32_t* chunk_base = nullptr;
+    if (ws && ws_bytes >= layout(*cfg).total && reinterpret_cast<uintptr_t>(ws) % 256 == 0)
+        chunk_base = at<int32_t>(ws, layout(*cfg).chunk_base);
     (void)hipGetLastError();
     HIP_TRY(moe::launch_permute(perm_params(*cfg, topk_ids, expert_offsets, active_experts, n_active, sorted_pairs,
-                                            nullptr, nullptr, 16),
+                                            nullptr, nullptr, 16, chunk_base),
                                 stream));
     return MOE_OK;
 }
@@ -515,7 +529,8 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
     int4* tiles = at<int4>(ws, L.tiles);
     int32_t* nt = at<int32_t>(ws, L.n_tiles);
     const moe::PermParams Q = perm_params(c, ids, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.active),
-                                          at<int32_t>(ws, L.n_active), pairs, tiles, nt, tile_rows);
+                                          at<int32_t>(ws, L.n_active), pairs, tiles, nt, tile_rows,
+                                          at<int32_t>(ws, L.chunk_base));
     if (moe_status st = stage_logits(c, L, ws, x, weights->router, stream)) return st;
     if (moe::route_permute_fusable(c.n_tokens, c.n_experts, c.top_k)) {
         HIP_TRY(moe::launch_route_permute(P, ids, wts, Q, stream));

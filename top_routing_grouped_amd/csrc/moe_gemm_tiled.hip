@@ -2,23 +2,29 @@
 // counts (Treebeard, "How Treebeard routes Qwen3.6 MoE tokens", "Routed
 // expert computation" and "Shared expert computation"; the per-expert
 // grouping follows the "Intel SYCL path": one tile works on one active
-// expert's packed pairs, so each weight block is loaded for up to 128 of them).
+// expert's packed pairs, so each weight block is loaded once for up to a
+// whole tile of them).
 //
-// Workgroup tile: 128 weight rows x 128 token rows, K in steps of 64.  Two
-// LDS buffers and two register buffers: the global loads of step k+2 are
-// issued while step k's MFMAs run and step k+1's data moves from registers to
-// LDS, one barrier per step.  For gate/up the 128 weight rows are 64 gate
-// rows and the same 64 up rows, so each lane ends with matching gate and up
-// accumulators and applies SwiGLU in registers.  4 waves in a 2 x 2 grid;
-// each wave owns 64 weight rows x 64 tokens as 4 x 4 fragments of
-// v_mfma_f32_16x16x32_bf16 (weights = A, tokens = B); token fragments past
-// the tile's row count issue no MFMAs.  LDS rows are 128 bytes with the
-// 16-byte pieces of row r XOR-swizzled by (r/2) mod 8, so both the 8-lanes-
-// per-row stores and the 16-rows-per-fragment reads of a wave touch 16
-// distinct 4-bank groups.
+// Workgroup tile: BW weight rows x BT token rows, K in steps of 64, NW waves
+// in a WM x WN grid; each wave owns (BW/WM) weight rows x (BT/WN) tokens as
+// fragments of v_mfma_f32_16x16x32_bf16 (weights = A, tokens = B); token
+// fragments past the tile's row count issue no MFMAs.  Two LDS buffers and
+// PF register buffers: the global loads of step k+PF are issued while step
+// k's MFMAs run, one barrier per step.  For gate/up the BW weight rows are
+// BW/2 gate rows and the same BW/2 up rows, so each lane ends with matching
+// gate and up accumulators and applies SwiGLU in registers.  LDS rows are 128
+// bytes with the 16-byte pieces of row r XOR-swizzled by (r/2) mod 8, so both
+// the 8-lanes-per-row stores and the 16-rows-per-fragment reads of a wave
+// touch 16 distinct 4-bank groups.
+//
+// The kernel is bound by how many bytes the memory system can keep in flight
+// for it (loaded latency is microseconds), so the tile is made as large as the
+// LDS and register file allow: 256 x 256 moves half the bytes per MFMA of a
+// 128 x 128 tile.
 #include "moe_device.h"
 #include "moe_kernels.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace moe {
@@ -27,30 +33,47 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BW = 128;       // weight rows per tile
-constexpr int BT = 128;       // token rows per tile
-constexpr int BK = 64;        // K per step
-constexpr int kThreads = 256;
+constexpr int BK = 64;  // K per step
+constexpr int RS = BK;  // LDS row stride (elements)
 
-// LDS row layout: 0 = rows padded to 144 bytes, 1 = 128-byte rows with the
-// 16-byte pieces XOR-swizzled by (r/2) mod 8, 2 = swizzled by r mod 8.
-#ifndef MOE_TILED_LDS_LAYOUT
-#define MOE_TILED_LDS_LAYOUT 1
+// Tile configuration: BW weight rows x BT tokens, NW waves as WM x WN, PF
+// register prefetch stages, MINB workgroups per CU for the launch bounds.
+template <int BW_, int BT_, int WM_, int WN_, int PF_, int MINB_>
+struct Cfg {
+    static constexpr int BW = BW_, BT = BT_, WM = WM_, WN = WN_, NW = WM_ * WN_, PF = PF_, MINB = MINB_;
+    static constexpr int THREADS = NW * 64;
+    static constexpr int FM = BW / WM / 16;  // weight fragments per wave
+    static constexpr int FT = BT / WN / 16;  // token fragments per wave
+    static constexpr int LA = BW * 8 / THREADS;  // 16-byte weight pieces per thread per step
+    static constexpr int LB = BT * 8 / THREADS;  // 16-byte token pieces per thread per step
+    static_assert(LA * THREADS == BW * 8 && LB * THREADS == BT * 8, "whole pieces per thread");
+    static_assert(FM % 2 == 0, "gate/up pairs of fragments");
+};
+// Routed experts: 256 x 256, 8 waves of 64 x 128, one register stage ahead
+// (register file: 128 accumulators + operands per lane at 2 waves per SIMD).
+#ifndef MOE_TILED_ROUTED
+#define MOE_TILED_ROUTED 6
 #endif
-// global prefetch distance in K steps (1 or 2)
-#ifndef MOE_TILED_PREFETCH
-#define MOE_TILED_PREFETCH 2
+#if MOE_TILED_ROUTED == 1
+using CfgLarge = Cfg<256, 256, 4, 2, 1, 1>;
+#elif MOE_TILED_ROUTED == 2
+using CfgLarge = Cfg<128, 128, 2, 2, 1, 2>;
+#elif MOE_TILED_ROUTED == 3
+using CfgLarge = Cfg<128, 128, 2, 2, 2, 1>;
+#elif MOE_TILED_ROUTED == 4
+using CfgLarge = Cfg<256, 128, 4, 2, 1, 1>;
+#elif MOE_TILED_ROUTED == 5
+using CfgLarge = Cfg<128, 256, 2, 4, 1, 1>;
+#elif MOE_TILED_ROUTED == 6
+using CfgLarge = Cfg<256, 128, 4, 2, 2, 1>;
 #endif
-constexpr int kLayout = MOE_TILED_LDS_LAYOUT;
-constexpr int kPrefetch = MOE_TILED_PREFETCH;
-constexpr int RS = kLayout == 0 ? BK + 8 : BK;  // LDS row stride (elements)
+// Dense products (shared expert, router logits): 128 x 128, 4 waves of
+// 64 x 64, one register stage ahead, 2 workgroups per CU (a dense T = 4096
+// product has too few 256 x 256 tiles to fill the chip).
+using CfgSmall = Cfg<128, 128, 2, 2, 1, 2>;
 
 // element offset of 16-byte piece p of LDS row r
-__device__ __forceinline__ int lds_off(int r, int p) {
-    if constexpr (kLayout == 0) return r * RS + (p << 3);
-    else if constexpr (kLayout == 1) return r * RS + ((p ^ ((r >> 1) & 7)) << 3);
-    else return r * RS + ((p ^ (r & 7)) << 3);
-}
+__device__ __forceinline__ int lds_off(int r, int p) { return r * RS + ((p ^ ((r >> 1) & 7)) << 3); }
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* base) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base));
@@ -58,62 +81,80 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* base) {
 
 }  // namespace
 
-template <int MODE, bool OUTBF>
-__global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
+template <int MODE, bool OUTBF, class C>
+__global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_tiled_kernel(GemmArgs a) {
+    constexpr int BW = C::BW, BT = C::BT, WM = C::WM, FM = C::FM, FT = C::FT, LA = C::LA, LB = C::LB;
+    constexpr int THREADS = C::THREADS, PF = C::PF;
     constexpr bool DUAL = (MODE == kRoutedGateUp || MODE == kDenseGateUp);
     constexpr bool ROUTED = (MODE == kRoutedGateUp || MODE == kRoutedDown);
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BW * RS];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BT * RS];
 
-    // XCD-aware order: workgroups are dispatched to the 8 XCDs round-robin,
-    // so block b runs on XCD b % 8.  Each XCD takes one contiguous run of the
-    // (tile, row block) work list, row block fastest: the row blocks of a
-    // token tile (same gathered token rows) and neighbouring tiles of the same
-    // expert (same weight rows) then share that XCD's L2.
-    constexpr bool DUAL_ = DUAL;
-    const int nrb = DUAL_ ? (a.N + 63) / 64 : (a.N + BW - 1) / BW;
+    // Work order: weight-stationary inside each expert (row block major,
+    // the expert's token tiles fastest), so a weight block is fetched from
+    // HBM once and re-read from L2 by the expert's other token tiles; the
+    // gathered token rows (a few MiB) stay in the last-level cache.  XCD-aware:
+    // workgroups are dispatched to the 8 XCDs round-robin, so block b runs on
+    // XCD b % 8, and each XCD takes one contiguous run of the work list.
+    constexpr int ROWS = DUAL ? BW / 2 : BW;  // output rows of a row block
+    const int nrb = (a.N + ROWS - 1) / ROWS;
     const int n_tiles_real = ROUTED ? uniform(*a.n_tiles) : (a.n_rows + BT - 1) / BT;
-    const int n_items = n_tiles_real * nrb;
+    // dense store (router logits): K split ksplit ways into partial planes
+    const int ksplit = (MODE == kDenseStore) ? max(a.ksplit, 1) : 1;
+    const int n_items = n_tiles_real * nrb * ksplit;
     const int chunk = (n_items + 7) / 8;
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
     if (local >= chunk) return;
-    const int item = xcd * chunk + local;
-    if (item >= n_items) return;
-    const int tile = item / nrb;
-    const int row_blk = item - tile * nrb;
+    const int item_k = xcd * chunk + local;
+    if (item_k >= n_items) return;
+    const int kz = item_k % ksplit, item = item_k / ksplit;
+    // the expert's tiles [first, first + nt) own items [first*nrb, (first+nt)*nrb)
+    int first = 0, nt = n_tiles_real;
+    if constexpr (ROUTED) {
+        const int w = uniform(a.tiles[item / nrb].w);
+        first = w >> 16;
+        nt = w & 0xffff;
+        const int off = item - first * nrb;
+        if (w < 0 || nt <= 0 || off < 0 || off >= nt * nrb) {  // no expert extent: plain order
+            first = item / nrb;
+            nt = 1;
+        }
+    }
+    const int off = item - first * nrb;
+    const int row_blk = off / nt;
+    const int tile = first + (off - row_blk * nt);
 
     int e = 0, begin, count;
     if constexpr (ROUTED) {
         const int4 t = a.tiles[tile];
         e = uniform(t.x); begin = uniform(t.y); count = uniform(t.z);
-        if (e < 0 || e >= a.n_banks || begin < 0 || count <= 0 || begin + count > a.n_pairs) return;
+        if (e < 0 || e >= a.n_banks || begin < 0 || count <= 0 || count > BT || begin + count > a.n_pairs) return;
     } else {
         begin = tile * BT;
         count = min(BT, a.n_rows - begin);
         if (count <= 0) return;
     }
     const int N = a.N, K = a.K;
+    const int klen = K / ksplit, kbase = kz * klen;  // this block's K range
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int q = lane >> 4, r = lane & 15;
-    const int wm = wave & 1, wn = wave >> 1;
-    // weight-row block row_blk: gate/up covers features [64*row_blk, +64) of both banks
+    const int wm = wave % WM, wn = wave / WM;
 
-    // ---- global load assignment: 4 pieces of 16 B per thread per operand
-    // piece p = tid + 256*i: row p/8, 16-byte column p%8 (8 threads per 128-byte row segment)
-    const uint16_t* wsrc[4];
-    const uint16_t* xsrc[4];
-    int lrow[4], lcol[4];
+    // ---- global load assignment: piece p = tid + THREADS*i is row p/8,
+    // 16-byte column p%8 (8 threads per 128-byte row segment of a K step)
+    const uint16_t* wsrc[LA];
+    const uint16_t* xsrc[LB];
+    int soff_a[LA], soff_b[LB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = tid + kThreads * i;
+    for (int i = 0; i < LA; ++i) {
+        const int p = tid + THREADS * i;
         const int row = p >> 3, col = (p & 7) * 8;
-        lrow[i] = row;
-        lcol[i] = col;
+        soff_a[i] = lds_off(row, col >> 3);
         const uint16_t* wb;
         int wr;
         if constexpr (DUAL) {
-            wb = static_cast<const uint16_t*>(row < 64 ? a.w0 : a.w1);
-            wr = row_blk * 64 + (row & 63);
+            wb = static_cast<const uint16_t*>(row < BW / 2 ? a.w0 : a.w1);
+            wr = row_blk * (BW / 2) + (row & (BW / 2 - 1));
         } else {
             wb = static_cast<const uint16_t*>(a.w0);
             wr = row_blk * BW + row;
@@ -122,7 +163,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
         // inside the K loop): absent weight rows and token rows read a valid
         // row instead; they only feed output rows / token columns that are
         // never stored.
-        wsrc[i] = wb + (size_t(e) * N + min(wr, N - 1)) * K + col;
+        wsrc[i] = wb + (size_t(e) * N + min(wr, N - 1)) * K + kbase + col;
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int p = tid + THREADS * i;
+        const int row = p >> 3, col = (p & 7) * 8;
+        soff_b[i] = lds_off(row, col >> 3);
         int arow = -1;
         if (row < count) {
             if constexpr (MODE == kRoutedGateUp) {
@@ -133,76 +180,71 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
             }
         }
         if (arow < 0 || arow >= a.n_act_rows) arow = 0;
-        xsrc[i] = static_cast<const uint16_t*>(a.act) + size_t(arow) * K + col;
+        xsrc[i] = static_cast<const uint16_t*>(a.act) + size_t(arow) * K + kbase + col;
     }
 
-    u32x4 wreg[2][4], xreg[2][4];
+    u32x4 wreg[PF][LA], xreg[PF][LB];
     auto gload = [&](int rb, int k0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wreg[rb][i] = *reinterpret_cast<const u32x4*>(wsrc[i] + k0);
-            xreg[rb][i] = *reinterpret_cast<const u32x4*>(xsrc[i] + k0);
-        }
-    };
-    int soff[4];
+        for (int i = 0; i < LA; ++i) wreg[rb][i] = *reinterpret_cast<const u32x4*>(wsrc[i] + k0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) soff[i] = lds_off(lrow[i], lcol[i] >> 3);
+        for (int i = 0; i < LB; ++i) xreg[rb][i] = *reinterpret_cast<const u32x4*>(xsrc[i] + k0);
+    };
     auto lstore = [&](int rb, int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<u32x4*>(&As[buf][soff[i]]) = wreg[rb][i];
-            *reinterpret_cast<u32x4*>(&Bs[buf][soff[i]]) = xreg[rb][i];
-        }
+        for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4*>(&As[buf][soff_a[i]]) = wreg[rb][i];
+#pragma unroll
+        for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4*>(&Bs[buf][soff_b[i]]) = xreg[rb][i];
     };
 
     // wave's fragment rows inside the tile
-    int arow_l[4];
+    int arow_l[FM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if constexpr (DUAL)  // frags 0,1: gate rows; 2,3: the matching up rows
-            arow_l[i] = (i >= 2 ? 64 : 0) + wm * 32 + (i & 1) * 16 + r;
+    for (int i = 0; i < FM; ++i) {
+        if constexpr (DUAL)  // the first FM/2 fragments: gate rows; the rest: the matching up rows
+            arow_l[i] = (i >= FM / 2 ? BW / 2 : 0) + wm * (BW / 2 / WM) + (i % (FM / 2)) * 16 + r;
         else
-            arow_l[i] = wm * 64 + i * 16 + r;
+            arow_l[i] = wm * (BW / WM) + i * 16 + r;
     }
-    const int brow_l = wn * 64 + r;
+    const int brow_l = wn * (BT / C::WN) + r;
     // token fragments of this wave that hold at least one row
-    const int nfrag = uniform(min(4, max(0, (count - wn * 64 + 15) / 16)));
+    const int nfrag = uniform(min(FT, max(0, (count - wn * (BT / C::WN) + 15) / 16)));
 
-    f32x4 acc[4][4];
+    f32x4 acc[FM][FT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / BK;
-    // One K step: MFMAs from LDS buffer `cur`.  FULL: all 4 token fragments
+    const int nk = klen / BK;
+    // One K step: MFMAs from LDS buffer `cur`.  FULL: all token fragments
     // hold rows (no per-fragment test inside the loop).
     auto compute = [&](int cur, auto full) {
         constexpr bool FULL = decltype(full)::value;
 #pragma unroll
         for (int ks = 0; ks < BK / 32; ++ks) {
-            bf16x8 af[4], bfr[4];
+            bf16x8 af[FM];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = lds_frag(&As[cur][lds_off(arow_l[i], ks * 4 + q)]);
+            for (int i = 0; i < FM; ++i) af[i] = lds_frag(&As[cur][lds_off(arow_l[i], ks * 4 + q)]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bfr[j] = lds_frag(&Bs[cur][lds_off(brow_l + j * 16, ks * 4 + q)]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < FT; ++j) {
                 if (!FULL && j >= nfrag) break;
+                const bf16x8 bfr = lds_frag(&Bs[cur][lds_off(brow_l + j * 16, ks * 4 + q)]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                for (int i = 0; i < FM; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr, acc[i][j], 0, 0, 0);
             }
         }
     };
     auto main_loop = [&](auto full) {
-        if constexpr (kPrefetch == 1) {
+        if constexpr (PF == 1) {
             gload(0, 0);
             lstore(0, 0);
             __syncthreads();
             for (int kt = 0; kt < nk; ++kt) {
                 const int cur = kt & 1;
                 if (kt + 1 < nk) gload(0, (kt + 1) * BK);
+                __builtin_amdgcn_sched_barrier(0);
                 compute(cur, full);
                 if (kt + 1 < nk) lstore(0, cur ^ 1);
                 __syncthreads();
@@ -249,26 +291,26 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
     };
     // the branch is on a wave-uniform value; a workgroup's waves may take
     // different branches (both reach the same barriers)
-    if (nfrag == 4)
+    if (nfrag == FT)
         main_loop(std::true_type{});
     else
         main_loop(std::false_type{});
 
     // ---- epilogue: lane holds rows (4q .. 4q+3) of fragment i, token column r of fragment j
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int tok = wn * 64 + j * 16 + r;
+    for (int j = 0; j < FT; ++j) {
+        const int tok = wn * (BT / C::WN) + j * 16 + r;
         if (tok >= count) continue;
         if constexpr (DUAL) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int f = row_blk * 64 + wm * 32 + i * 16 + 4 * q;
+            for (int i = 0; i < FM / 2; ++i) {
+                const int f = row_blk * (BW / 2) + wm * (BW / 2 / WM) + i * 16 + 4 * q;
                 if (f >= N) continue;
                 float v[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const float g = acc[i][j][t];
-                    v[t] = g / (1.0f + __expf(-g)) * acc[i + 2][j][t];
+                    v[t] = g / (1.0f + __expf(-g)) * acc[i + FM / 2][j][t];
                 }
                 const size_t o = size_t(begin + tok) * N + f;
                 if constexpr (OUTBF)
@@ -288,12 +330,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
             } else if constexpr (MODE == kDenseDown) {
                 dest = size_t(begin + tok);
                 if (a.row_scale) s = sigmoidf_(a.row_scale[begin + tok]);
-            } else {
-                dest = size_t(begin + tok);
+            } else {  // dense store: partial plane kz
+                dest = size_t(kz) * a.n_rows + begin + tok;
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d = row_blk * BW + wm * 64 + i * 16 + 4 * q;
+            for (int i = 0; i < FM; ++i) {
+                const int d = row_blk * BW + wm * (BW / WM) + i * 16 + 4 * q;
                 if (d >= N) continue;
                 const float v0 = s * acc[i][j][0], v1 = s * acc[i][j][1], v2 = s * acc[i][j][2], v3 = s * acc[i][j][3];
                 const size_t o = dest * N + d;
@@ -307,25 +349,37 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs a) {
     }
 }
 
-int tiled_rows() { return BT; }
+int tiled_rows() { return CfgLarge::BT; }
+int tiled_rows_dense() { return CfgSmall::BT; }
 
-hipError_t launch_gemm_tiled(int mode, bool outbf, const GemmArgs& a, int grid_x, hipStream_t s) {
-    if (grid_x <= 0) return hipSuccess;
+template <class C>
+static hipError_t launch_cfg(int mode, bool outbf, const GemmArgs& a, int grid_x, hipStream_t s) {
     const bool dual = (mode == kRoutedGateUp || mode == kDenseGateUp);
-    const long long nrb = dual ? (a.N + 63) / 64 : (a.N + BW - 1) / BW;
-    const long long items = (long long)grid_x * nrb;
+    const int rows = dual ? C::BW / 2 : C::BW;
+    const long long nrb = (a.N + rows - 1) / rows;
+    const long long items = (long long)grid_x * nrb * (mode == kDenseStore ? std::max(a.ksplit, 1) : 1);
     const dim3 g(unsigned(8 * ((items + 7) / 8)));
+    const dim3 b(C::THREADS);
     switch (mode) {
-        case kRoutedGateUp: gemm_tiled_kernel<kRoutedGateUp, true><<<g, kThreads, 0, s>>>(a); break;
+        case kRoutedGateUp: gemm_tiled_kernel<kRoutedGateUp, true, C><<<g, b, 0, s>>>(a); break;
         case kRoutedDown:
-            if (outbf) gemm_tiled_kernel<kRoutedDown, true><<<g, kThreads, 0, s>>>(a);
-            else gemm_tiled_kernel<kRoutedDown, false><<<g, kThreads, 0, s>>>(a);
+            if (outbf) gemm_tiled_kernel<kRoutedDown, true, C><<<g, b, 0, s>>>(a);
+            else gemm_tiled_kernel<kRoutedDown, false, C><<<g, b, 0, s>>>(a);
             break;
-        case kDenseGateUp: gemm_tiled_kernel<kDenseGateUp, true><<<g, kThreads, 0, s>>>(a); break;
-        case kDenseDown: gemm_tiled_kernel<kDenseDown, false><<<g, kThreads, 0, s>>>(a); break;
-        default: gemm_tiled_kernel<kDenseStore, false><<<g, kThreads, 0, s>>>(a); break;
+        case kDenseGateUp: gemm_tiled_kernel<kDenseGateUp, true, C><<<g, b, 0, s>>>(a); break;
+        case kDenseDown: gemm_tiled_kernel<kDenseDown, false, C><<<g, b, 0, s>>>(a); break;
+        default: gemm_tiled_kernel<kDenseStore, false, C><<<g, b, 0, s>>>(a); break;
     }
     return hipGetLastError();
+}
+
+// Routed modes use the large tile (grid_x = routed tiles of tiled_rows()
+// pairs); dense modes the small one (grid_x = token tiles of
+// tiled_rows_dense() tokens).
+hipError_t launch_gemm_tiled(int mode, bool outbf, const GemmArgs& a, int grid_x, hipStream_t s) {
+    if (grid_x <= 0) return hipSuccess;
+    if (mode == kRoutedGateUp || mode == kRoutedDown) return launch_cfg<CfgLarge>(mode, outbf, a, grid_x, s);
+    return launch_cfg<CfgSmall>(mode, outbf, a, grid_x, s);
 }
 
 }  // namespace moe

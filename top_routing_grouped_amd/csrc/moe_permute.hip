@@ -4,11 +4,12 @@
 // path", steps 1-4): count the T*K (token, slot) pairs per expert, turn the
 // counts into offsets and an active-expert list, pack every flat pair id
 // t*K + k under its expert, and list the GEMM tiles over active experts only.
-// One 1024-thread workgroup: histogram with LDS atomics, block scans, then a
-// stable scatter: inside a wave, lanes holding the same expert are found with
-// one ballot per id bit; earlier waves' counts and a running cursor per
-// expert give every pair its position, so pairs stay in ascending pair-id
-// order inside each expert (the order a stable sort by expert gives).
+// Up to 4096 pairs, one 1024-thread workgroup: histogram with LDS atomics,
+// block scans, then a stable scatter: inside a wave, lanes holding the same
+// expert are found with one ballot per id bit; earlier waves' counts and a
+// running cursor per expert give every pair its position, so pairs stay in
+// ascending pair-id order inside each expert (the order a stable sort by
+// expert gives).  More pairs: the chunked permute below.
 //
 // Combine (Treebeard, "Shared expert computation", last block):
 //   out = residual + (sum_{k ascending} slot[t, k, :] + shared[t, :]).
@@ -36,75 +37,114 @@ int max_tiles_for(int n_pairs, int E, int tile_rows) {
     return int(((long long)n_pairs + act * (tile_rows - 1)) / tile_rows);
 }
 
-// Many pairs: one workgroup per expert.  Every workgroup builds the full
-// per-expert histogram in LDS (the same in all of them), takes its expert's
-// offset, active-list slot and first tile from prefix sums over the smaller
-// experts, and gathers its expert's pair ids in ascending order with
-// per-wave ballots.  No cross-workgroup communication, so the result is the
-// same stable order as the single-workgroup permute.
-__global__ __launch_bounds__(kPermThreads) void permute_wide_kernel(PermParams P) {
-    extern __shared__ int hist[];  // [E] then 32 scratch ints
-    int* sh = hist + P.E;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int E = P.E, me = blockIdx.x;
-    for (int e = tid; e < E; e += kPermThreads) hist[e] = 0;
+// Many pairs: three launches over chunks of kPermChunk pairs.
+//  1. count: each chunk's per-expert histogram (LDS atomics) -> chunk_base[c][e];
+//  2. scan (one workgroup): per expert, the exclusive prefix over chunks and
+//     the total; the totals give offsets, the active list and the tile list,
+//     and chunk_base[c][e] becomes the position of chunk c's first pair of
+//     expert e;
+//  3. scatter: each chunk ranks its pairs within their expert (ballots over
+//     the id bits inside a wave, earlier waves' counts through LDS) and writes
+//     them from chunk_base, so pairs stay in ascending pair-id order inside
+//     each expert (the order a stable sort by expert gives).
+__global__ __launch_bounds__(256) void permute_count_kernel(PermParams P) {
+    extern __shared__ int hist[];  // [E]
+    const int E = P.E, c = blockIdx.x, tid = threadIdx.x;
+    for (int e = tid; e < E; e += 256) hist[e] = 0;
     __syncthreads();
-    for (int p = tid; p < P.n_pairs; p += kPermThreads) {
+    const int p0 = c * kPermChunk, p1 = min(P.n_pairs, p0 + kPermChunk);
+    for (int p = p0 + tid; p < p1; p += 256) {
         const int e = P.ids[p];
         if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
     }
     __syncthreads();
-    const int c = tid < E ? hist[tid] : 0;
-    const int nt = (c + P.tile_rows - 1) / P.tile_rows;
-    int total, n_act, n_tiles;
-    const int off = block_exclusive_scan(c, &total, sh);
-    const int apos = block_exclusive_scan(c > 0 ? 1 : 0, &n_act, sh);
-    const int tpos = block_exclusive_scan(nt, &n_tiles, sh);
-    __shared__ int mine[4];
-    if (tid == me) {
-        mine[0] = off;
-        mine[1] = c;
-        mine[2] = apos;
-        mine[3] = tpos;
+    for (int e = tid; e < E; e += 256) P.chunk_base[size_t(c) * E + e] = hist[e];
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(PermParams P, int nchunks) {
+    __shared__ int sh[32];
+    // chunk counts held in registers G at a time: unconditional loads from
+    // clamped addresses, so they are all in flight together
+    constexpr int G = 16;
+    const int E = P.E, tid = threadIdx.x;
+    int total = 0;
+    if (tid < E) {
+        for (int c0 = 0; c0 < nchunks; c0 += G) {
+            int v[G];
+#pragma unroll
+            for (int i = 0; i < G; ++i) v[i] = P.chunk_base[size_t(min(c0 + i, nchunks - 1)) * E + tid];
+#pragma unroll
+            for (int i = 0; i < G; ++i) total += c0 + i < nchunks ? v[i] : 0;
+        }
     }
-    __syncthreads();
-    const int base = mine[0], cnt = mine[1];
-    if (tid == 0) {
-        P.offsets[me] = base;
+    const int cnt = tid < E ? total : 0;
+    int all, n_act, n_tiles;
+    const int off = block_exclusive_scan(cnt, &all, sh);
+    const int apos = block_exclusive_scan(cnt > 0 ? 1 : 0, &n_act, sh);
+    const int nt = (cnt + P.tile_rows - 1) / P.tile_rows;
+    const int tpos = block_exclusive_scan(P.tiles ? nt : 0, &n_tiles, sh);
+    if (tid < E) {
+        P.offsets[tid] = off;
         if (cnt > 0) {
-            P.active[mine[2]] = me;
-            if (P.tiles) write_tiles(P.tiles, mine[3], me, base, cnt, P.tile_rows, P.max_tiles);
+            P.active[apos] = tid;
+            if (P.tiles) write_tiles(P.tiles, tpos, tid, off, cnt, P.tile_rows, P.max_tiles);
         }
-        if (me == 0) {
-            P.offsets[E] = total;
-            *P.n_active = n_act;
-            if (P.n_tiles) *P.n_tiles = min(n_tiles, P.max_tiles);
+        // chunk c's first pair of expert tid goes to off + (its pairs in chunks < c)
+        int run = off;
+        for (int c0 = 0; c0 < nchunks; c0 += G) {
+            int v[G];
+#pragma unroll
+            for (int i = 0; i < G; ++i) v[i] = P.chunk_base[size_t(min(c0 + i, nchunks - 1)) * E + tid];
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                if (c0 + i < nchunks) {
+                    P.chunk_base[size_t(c0 + i) * E + tid] = run;
+                    run += v[i];
+                }
+            }
         }
     }
-    if (cnt == 0) return;  // uniform
+    if (tid == 0) {
+        P.offsets[E] = all;
+        *P.n_active = n_act;
+        if (P.n_tiles) *P.n_tiles = min(n_tiles, P.max_tiles);
+    }
+}
+
+static_assert(kPermChunk == kPermThreads, "one pair per thread in the scatter");
+
+__global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(PermParams P) {
+    extern __shared__ uint16_t wcnt[];  // [kPermWaves][E]
+    const int E = P.E, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int p = c * kPermChunk + tid;  // one pair per thread (kPermChunk == kPermThreads)
+    int e = p < P.n_pairs ? P.ids[p] : -1;
+    const bool valid = e >= 0 && e < E;
+    if (!valid) e = 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < P.id_bits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        peers &= bit ? bb : ~bb;
+    }
     const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    int running = 0;
-    for (int r0 = 0; r0 < P.n_pairs; r0 += kPermThreads) {
-        const int p = r0 + tid;
-        const bool m = p < P.n_pairs && P.ids[p] == me;
-        const uint64_t b = __ballot(m);
-        if (lane == 0) sh[wave] = __popcll(b);
-        __syncthreads();
-        int before = running, sum = 0;
-        for (int w = 0; w < kPermWaves; ++w) {
-            const int v = sh[w];
-            if (w < wave) before += v;
-            sum += v;
-        }
-        if (m) P.sorted_pairs[base + before + __popcll(b & lt)] = p;
-        running += sum;
-        __syncthreads();
+    const int rank = __popcll(peers & lt);
+    for (int i = tid; i < kPermWaves * E; i += kPermThreads) wcnt[i] = 0;
+    __syncthreads();
+    if (valid && rank == 0) wcnt[wave * E + e] = uint16_t(__popcll(peers));
+    __syncthreads();
+    if (valid) {
+        int before = 0;
+        for (int w = 0; w < wave; ++w) before += wcnt[w * E + e];
+        P.sorted_pairs[P.chunk_base[size_t(c) * E + e] + before + rank] = p;
     }
 }
 
 hipError_t launch_permute(const PermParams& P, hipStream_t s) {
-    if (P.n_pairs >= 4096) {
-        permute_wide_kernel<<<P.E, kPermThreads, size_t(P.E + 32) * 4, s>>>(P);
+    if (P.n_pairs >= 4096 && P.chunk_base) {
+        const int nc = perm_chunks(P.n_pairs);
+        permute_count_kernel<<<nc, 256, size_t(P.E) * 4, s>>>(P);
+        permute_scan_kernel<<<1, kPermThreads, 0, s>>>(P, nc);
+        permute_scatter_kernel<<<nc, kPermThreads, size_t(kPermWaves) * P.E * 2, s>>>(P);
     } else {
         permute_kernel<<<1, kPermThreads, permute_smem_bytes(P.E), s>>>(P);
     }

@@ -365,13 +365,17 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* sh) 
 }
 
 // GEMM tiles of expert e (rows [begin, begin+cnt)) from tile index `start`;
-// tiles past max_tiles are dropped.
+// tiles past max_tiles are dropped.  Field w packs the expert's first tile
+// and tile count (start * 65536 + n) so the GEMM can order its work by
+// weight block; -1 when they do not fit.
 __device__ __forceinline__ void write_tiles(int4* tiles, int start, int e, int begin, int cnt, int tile_rows,
                                             int max_tiles) {
+    const int nt = (cnt + tile_rows - 1) / tile_rows;
+    const int w = (start < 32768 && nt < 65536 && start + nt <= max_tiles) ? start * 65536 + nt : -1;
     for (int j = 0, r = 0; r < cnt; ++j, r += tile_rows) {
         const int ti = start + j;
         if (ti >= max_tiles) break;
-        tiles[ti] = make_int4(e, begin + r, min(tile_rows, cnt - r), 0);
+        tiles[ti] = make_int4(e, begin + r, min(tile_rows, cnt - r), w);
     }
 }
 
@@ -385,7 +389,12 @@ struct PermParams {
     int4* tiles;
     int32_t* n_tiles;
     int tile_rows, max_tiles;
+    int32_t* chunk_base;  // [ceil(n_pairs / kPermChunk)][E] scratch of the chunked permute
 };
+
+// Pairs per chunk of the chunked (many-pair) permute.
+constexpr int kPermChunk = 1024;
+inline int perm_chunks(int n_pairs) { return (n_pairs + kPermChunk - 1) / kPermChunk; }
 
 // LDS words the permute needs for E experts.
 __host__ __device__ constexpr size_t permute_lds_words(int E) { return size_t(3 * E + 32) + size_t(kPermWaves) * E / 2; }
