@@ -17,10 +17,10 @@
 // the 8-lanes-per-row stores and the 16-rows-per-fragment reads of a wave
 // touch 16 distinct 4-bank groups.
 //
-// The kernel is bound by how many bytes the memory system can keep in flight
-// for it (loaded latency is microseconds), so the tile is made as large as the
-// LDS and register file allow: 256 x 256 moves half the bytes per MFMA of a
-// 128 x 128 tile.
+// The kernel is bound by how many bytes the memory system keeps in flight for
+// it (loaded latency is microseconds): the step time is about the latency
+// divided by the number of steps in flight, so the tile is as large, and the
+// register prefetch as deep, as the LDS and the register file allow.
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -49,27 +49,15 @@ struct Cfg {
     static_assert(LA * THREADS == BW * 8 && LB * THREADS == BT * 8, "whole pieces per thread");
     static_assert(FM % 2 == 0, "gate/up pairs of fragments");
 };
-// Routed experts: 256 x 256, 8 waves of 64 x 128, one register stage ahead
-// (register file: 128 accumulators + operands per lane at 2 waves per SIMD).
-#ifndef MOE_TILED_ROUTED
-#define MOE_TILED_ROUTED 6
-#endif
-#if MOE_TILED_ROUTED == 1
-using CfgLarge = Cfg<256, 256, 4, 2, 1, 1>;
-#elif MOE_TILED_ROUTED == 2
-using CfgLarge = Cfg<128, 128, 2, 2, 1, 2>;
-#elif MOE_TILED_ROUTED == 3
-using CfgLarge = Cfg<128, 128, 2, 2, 2, 1>;
-#elif MOE_TILED_ROUTED == 4
-using CfgLarge = Cfg<256, 128, 4, 2, 1, 1>;
-#elif MOE_TILED_ROUTED == 5
-using CfgLarge = Cfg<128, 256, 2, 4, 1, 1>;
-#elif MOE_TILED_ROUTED == 6
+// Routed experts: 256 x 128, 8 waves of 64 x 64, two register stages ahead
+// (64 accumulators + 2 x 24 staging registers + operands per lane fit the
+// 256 registers of 2 waves per SIMD without spilling).  Measured at T = 4096
+// against 256 x 256 (one stage: fewer steps in flight), 128 x 128 (two
+// workgroups per CU: twice the bytes per MFMA) and 16-wave shapes (spills).
 using CfgLarge = Cfg<256, 128, 4, 2, 2, 1>;
-#endif
 // Dense products (shared expert, router logits): 128 x 128, 4 waves of
 // 64 x 64, one register stage ahead, 2 workgroups per CU (a dense T = 4096
-// product has too few 256 x 256 tiles to fill the chip).
+// product has too few 256 x 128 tiles to fill the chip).
 using CfgSmall = Cfg<128, 128, 2, 2, 1, 2>;
 
 // element offset of 16-byte piece p of LDS row r
