@@ -27,7 +27,8 @@ DEVICE = ["-x", "hip", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-flush-denormals-to-zero"]
 
-SOURCES = ["moe_gemm.hip", "moe_gemm_tiled.hip", "moe_route.hip", "moe_permute.hip", "moe_api.cpp"]
+SOURCES = ["moe_gemm.hip", "moe_gemm_tiled.hip", "moe_route.hip", "moe_permute.hip", "moe_down_combine.hip",
+           "moe_api.cpp"]
 
 
 def _compile(src: str) -> str:

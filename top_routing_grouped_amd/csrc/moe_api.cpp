@@ -54,6 +54,12 @@ bool dense_tiled(const moe_config& c, moe_dtype d) { return c.n_tokens >= 128 &&
 // extra work item of the routed launches.
 bool small_path(const moe_config& c) { return !routed_large(c) && (int64_t)c.n_tokens * c.top_k <= 256; }
 int h_ld(const moe_config& c) { return std::max(c.d_ff, c.d_ff_shared); }
+// Small path with bf16 weights: the down projection and the combine are one
+// launch (each workgroup owns a slice of output features for every token).
+bool down_combine_fused(const moe_config& c) {
+    return small_path(c) && c.expert_dtype == MOE_BF16 &&
+           moe::down_combine_supported(c.n_tokens, c.top_k, c.d_model, c.d_ff, c.d_ff_shared);
+}
 
 // Router logits: for small T, K is split over up to 8 workgroups (partial
 // planes the selection sums), each split a whole number of 4-wave chunks; 1
@@ -505,6 +511,18 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
         }
         HIP_TRY(moe::launch_route_select_gate(P, G, ids, wts, stream));
         if (moe_status st = stage_small_gateup(c, L, ws, x, *weights, stream)) return st;
+        if (down_combine_fused(c)) {
+            moe::DownCombineArgs d{};
+            d.h = at<void>(ws, L.h); d.h_ld = h_ld(c);
+            d.ids = ids; d.wts = wts;
+            d.w = weights->down.w; d.ws = has_shared ? weights->shared_down.w : nullptr;
+            d.gate_logit = has_shared && weights->shared_gate_vec ? at<float>(ws, L.gate_logit) : nullptr;
+            d.residual = residual; d.out = out;
+            d.T = c.n_tokens; d.K = c.top_k; d.E = c.n_experts; d.D = c.d_model; d.F = c.d_ff;
+            d.has_shared = has_shared ? 1 : 0;
+            HIP_TRY(moe::launch_down_combine(d, stream));
+            return MOE_OK;
+        }
         if (moe_status st = stage_small_down(c, L, ws, *weights, stream)) return st;
         HIP_TRY(moe::launch_combine(at<void>(ws, L.slots), slot_bf16, nullptr, residual, out, c.n_tokens,
                                     c.top_k + (has_shared ? 1 : 0), c.d_model, stream));

@@ -1,0 +1,178 @@
+// Down projection fused with the combine, for small token counts (Treebeard,
+// "How Treebeard routes Qwen3.6 MoE tokens", "Routed expert computation" and
+// "Shared expert computation", last block):
+//   out[t, :] = residual[t, :] + sum_{k ascending} alpha[t, k] * (W_down[e_tk] h[t*K + k])
+//                              + g_t * (W_shared_down h_shared[t])
+// with g_t the sigmoid of the shared gate logit (1 without a gate vector).
+//
+// A workgroup owns R output features d0 .. d0+R-1 for every token, so it
+// alone reads those rows of every selected expert's down matrix (each byte
+// once from HBM) and sums a token's units (its K routed pairs in ascending
+// k, then the shared expert) in a fixed order: no slot buffer, no second
+// launch, no atomics.  With about one token per selected expert a unit is a
+// matrix-vector product, done with v_dot2 on the VALU: lane (r, s) holds
+// feature d0 + r and the 8-element K blocks s, s + 8, s + 16, ... of it, so a
+// 16-byte load instruction reads R whole 128-byte lines.  The waves split the
+// list of units evenly; a wave's partial sum for a token goes to LDS when the
+// token changes and the workgroup adds the waves' partials in wave order.
+// Two units' loads are in flight per wave while the previous one is used.
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kDcR = 8;             // output features per workgroup
+constexpr int kDcLanes = 64 / kDcR;  // lanes per feature
+constexpr int kDcWaves = 8;
+constexpr int kDcMaxT = 64;
+// Fourth word of a raw (stride 0, byte-addressed) buffer resource on gfx9:
+// 32-bit data format; offsets at or past the record count read zero.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// Each element goes through a scalar copy before the bit cast: clang's
+// __builtin_bit_cast of a vector-element expression (a.y) read element 0.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+}
+__device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float acc) {
+    const uint32_t a0 = a.x, a1 = a.y, a2 = a.z, a3 = a.w, b0 = b.x, b1 = b.y, b2 = b.z, b3 = b.w;
+    return dot2(a3, b3, dot2(a2, b2, dot2(a1, b1, dot2(a0, b0, acc))));
+}
+
+// J: 16-byte loads per lane per unit (F = 64 J)
+template <int J>
+__global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombineArgs a) {
+    __shared__ float part[kDcWaves][kDcMaxT][kDcR];
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    const int r = lane / kDcLanes, s = lane % kDcLanes;
+    const int d0 = blockIdx.x * kDcR;
+    const int T = a.T, K = a.K, S = a.has_shared ? 1 : 0, KS = K + S, TK = T * K;
+    for (int i = tid; i < kDcWaves * kDcMaxT * kDcR; i += kDcWaves * 64) (&part[0][0][0])[i] = 0.f;
+
+    // the wave's units ub .. ue-1 (at most 64): lane l holds unit ub + l's
+    // expert (-1: the shared expert) and scale, read back with readlane
+    const int n_units = T * KS;
+    const int ub = (wave * n_units) / kDcWaves, ue = ((wave + 1) * n_units) / kDcWaves;
+    int u_e = 0;
+    float u_sc = 0.f;
+    if (ub + lane < ue) {
+        const int u = ub + lane, t = u / KS, k = u - t * KS;
+        if (k < K) {
+            const int e = a.ids[t * K + k];
+            const bool ok = e >= 0 && e < a.E;
+            u_e = ok ? e : 0;  // scale 0 for an id out of range
+            u_sc = ok ? a.wts[t * K + k] : 0.f;
+        } else {
+            u_e = -1;
+            u_sc = a.gate_logit ? sigmoidf_(a.gate_logit[t]) : 1.f;
+        }
+    }
+    __syncthreads();
+    const uint16_t* wb = static_cast<const uint16_t*>(a.w);
+    const uint16_t* wsb = static_cast<const uint16_t*>(a.ws);
+    const uint16_t* hb = static_cast<const uint16_t*>(a.h);
+    const int F = 64 * J;
+
+    // unit u: token u / KS, slot u % KS (slot K: the shared expert).  Buffer
+    // loads: the unit's row-slice and h row are scalar bases, a lane's byte
+    // offset inside them is fixed, so issuing a unit writes no VGPR but the
+    // load destinations (address arithmetic on VGPRs made the compiler wait
+    // for the loads in flight before reusing their registers).
+    const uint32_t w_off = uint32_t((r * F + 8 * s) * 2), h_off = uint32_t(16 * s);
+    auto load = [&](int u, u32x4 (&wr)[J], u32x4 (&hr)[J]) __attribute__((always_inline)) {
+        const int t = u / KS, k = u - t * KS;
+        const int e = __builtin_amdgcn_readlane(u_e, u - ub);
+        const uint16_t* wrow = e >= 0 ? wb + (size_t(e) * a.D + d0) * F : wsb + size_t(d0) * F;
+        const size_t hrow = k < K ? size_t(t) * K + k : size_t(TK) + t;
+        const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wrow), 0, kDcR * F * 2, kRsrcWord3);
+        const auto rh = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(hb + hrow * a.h_ld), 0, F * 2, kRsrcWord3);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            wr[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off + 128 * j, 0, 0);
+            hr[j] = __builtin_amdgcn_raw_buffer_load_b128(rh, h_off + 128 * j, 0, 0);
+        }
+    };
+    auto unit_scale = [&](int u) __attribute__((always_inline)) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, u_sc), u - ub));
+    };
+
+    float acc = 0.f;
+    int cur_t = ub < ue ? ub / KS : 0;
+    auto flush = [&]() __attribute__((always_inline)) {
+        float v = acc;
+#pragma unroll
+        for (int m = 1; m < kDcLanes; m <<= 1) v += __shfl_xor(v, m, 64);
+        if (s == 0) part[wave][cur_t][r] = v;
+        acc = 0.f;
+    };
+    auto use = [&](int u, const u32x4 (&wr)[J], const u32x4 (&hr)[J]) __attribute__((always_inline)) {
+        const int t = u / KS;
+        if (t != cur_t) {
+            flush();
+            cur_t = t;
+        }
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; j += 2) {
+            p0 = dot8(wr[j], hr[j], p0);
+            if (j + 1 < J) p1 = dot8(wr[j + 1], hr[j + 1], p1);
+        }
+        acc = fmaf(unit_scale(u), p0 + p1, acc);
+    };
+
+    if (ub < ue) {
+        u32x4 wa[J], ha[J], wn[J], hn[J];
+        load(ub, wa, ha);
+        int u = ub;
+        // two units in flight: the loads of u + 1 (clamped: past the end they
+        // re-read the last unit, unused) are issued before unit u is used
+        for (; u + 2 <= ue; u += 2) {
+            load(u + 1, wn, hn);
+            use(u, wa, ha);
+            load(min(u + 2, ue - 1), wa, ha);
+            use(u + 1, wn, hn);
+        }
+        if (u < ue) use(u, wa, ha);
+        flush();
+    }
+    __syncthreads();
+
+    // waves' partials in wave order, then the residual
+    for (int i = tid; i < T * kDcR; i += kDcWaves * 64) {
+        const int t = i / kDcR, rr = i % kDcR;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kDcWaves; ++w) v += part[w][t][rr];
+        const size_t o = size_t(t) * a.D + d0 + rr;
+        a.out[o] = a.residual[o] + v;
+    }
+}
+
+}  // namespace
+
+bool down_combine_supported(int T, int K, int D, int F, int Fs) {
+    // a wave's units (T * (K + 1) / 8 of them) must fit its 64 lanes
+    if (T <= 0 || T > kDcMaxT || D % kDcR || T * (K + 1) > 64 * kDcWaves) return false;
+    if (Fs != 0 && Fs != F) return false;
+    return F == 128 || F == 256 || F == 512 || F == 768 || F == 1024;
+}
+
+hipError_t launch_down_combine(const DownCombineArgs& a, hipStream_t s) {
+    if (!down_combine_supported(a.T, a.K, a.D, a.F, a.has_shared ? a.F : 0)) return hipErrorInvalidValue;
+    const dim3 g(unsigned(a.D / kDcR)), b(kDcWaves * 64);
+    switch (a.F / 64) {
+        case 2: down_combine_kernel<2><<<g, b, 0, s>>>(a); break;
+        case 4: down_combine_kernel<4><<<g, b, 0, s>>>(a); break;
+        case 8: down_combine_kernel<8><<<g, b, 0, s>>>(a); break;
+        case 12: down_combine_kernel<12><<<g, b, 0, s>>>(a); break;
+        default: down_combine_kernel<16><<<g, b, 0, s>>>(a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

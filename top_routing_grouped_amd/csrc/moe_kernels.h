@@ -83,6 +83,23 @@ hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* active, con
                               hipStream_t s);
 
 // combine: out = residual + (sum_k slot[t,k,:] + shared[t,:])
+// Small T, bf16 weights: down projection and combine in one launch.
+// out[t, :] = residual[t, :] + sum_k wts[t*K+k] * W_down[ids[t*K+k]] h[t*K+k]
+//            + sigmoid(gate_logit[t]) * W_shared_down h[T*K + t]   (gate 1 if NULL).
+struct DownCombineArgs {
+    const void* h;            // [T*K + T][h_ld] bf16: routed pair rows, then shared rows
+    int h_ld;
+    const int32_t* ids;       // [T*K]
+    const float* wts;         // [T*K]
+    const void* w;            // routed down bank [E][D][F] bf16
+    const void* ws;           // shared down [D][F] bf16 (has_shared)
+    const float* gate_logit;  // [T] or NULL
+    const float* residual;    // [T][D]
+    float* out;               // [T][D]
+    int T, K, E, D, F, has_shared;
+};
+bool down_combine_supported(int T, int K, int D, int F, int Fs);
+hipError_t launch_down_combine(const DownCombineArgs& a, hipStream_t s);
 hipError_t launch_combine(const void* slots, bool slots_bf16, const float* shared, const float* residual,
                           float* out, int T, int K, int D, hipStream_t s);
 // small T: the slot rows hold K routed slots + the shared expert (K+1 per token)
