@@ -27,6 +27,9 @@
 #include "moe_device.h"
 #include "moe_kernels.h"
 
+#include <type_traits>
+
+
 namespace moe {
 
 // --------------------------------------------------------------- operands
@@ -306,22 +309,34 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         const int kper = ksub / WKS;
         const int kbeg = kbase + wk * kper;
         const int nchunks = kper / SPAN;
-        // small T: a wave's chunks (4 at decode shapes) are all requested
-        // before the first is used
-#pragma unroll(SMALL ? 4 : 2)
-        for (int c = 0; c < nchunks; ++c) {
-            const int kc = kbeg + c * SPAN;
-            Frag<F32> wa[NM];
-            load_w<WK>(wa[0], w0, s0, m0, wrow, K, kc, q);
-            if constexpr (DUAL) load_w<WK>(wa[1], w1, s1, m1, wrow, K, kc, q);
-            Frag<F32> xb[TF];
+        // U = 2 chunks per trip, all loads before any MFMA: a runtime-count
+        // loop with MFMAs (convergent) is not unrolled by the compiler, so
+        // without this a wave waits a full memory round trip per chunk.
+        // (Measured at decode shapes: 4 chunks per trip halves occupancy for
+        // no gain; the launch is bandwidth bound either way.)
+        constexpr int U = 2;
+        auto trip = [&](int c0, auto u_c) __attribute__((always_inline)) {
+            constexpr int UU = decltype(u_c)::value;
+            Frag<F32> wa[UU][NM];
+            Frag<F32> xb[UU][TF];
 #pragma unroll
-            for (int j = 0; j < TF; ++j) load_x<WK>(xb[j], xrow[j], kc, q);
+            for (int i = 0; i < UU; ++i) {
+                const int kc = kbeg + (c0 + i) * SPAN;
+                load_w<WK>(wa[i][0], w0, s0, m0, wrow, K, kc, q);
+                if constexpr (DUAL) load_w<WK>(wa[i][1], w1, s1, m1, wrow, K, kc, q);
 #pragma unroll
-            for (int m = 0; m < NM; ++m)
+                for (int j = 0; j < TF; ++j) load_x<WK>(xb[i][j], xrow[j], kc, q);
+            }
 #pragma unroll
-                for (int j = 0; j < TF; ++j) mma_chunk<F32>(acc[m][j], wa[m], xb[j]);
-        }
+            for (int i = 0; i < UU; ++i)
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+#pragma unroll
+                    for (int j = 0; j < TF; ++j) mma_chunk<F32>(acc[m][j], wa[i][m], xb[i][j]);
+        };
+        int c = 0;
+        for (; c + U <= nchunks; c += U) trip(c, std::integral_constant<int, U>{});
+        for (; c < nchunks; ++c) trip(c, std::integral_constant<int, 1>{});
     }
 
     // ---- split-K reduction through LDS, fixed order wk = 0, 1, 2, ...

@@ -337,6 +337,299 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_tiled_kernel(GemmArg
     }
 }
 
+// Routed experts, persistent.  With an expert's d_ff-long K (down) an item
+// is only a few K steps, and the plain kernel waits on memory several times
+// per item: decoding the item (two dependent loads), the token rows, the
+// first K steps, and the pair ids and routing weights of its stores.  Here
+// one workgroup per CU walks its XCD's run of items (the same weight-
+// stationary order) and hides all of that behind the previous item: the
+// item list is decoded into LDS once, the next item's token rows and store
+// targets are loaded while the current item's K loop runs, and its first two
+// K steps are loaded during the current item's last two.  Loads are buffer
+// loads from scalar bases (the weight block, the token matrix) with fixed
+// per-lane offsets, so switching items changes no VGPR address, and the
+// weight rows past the matrix read zero (record count of the resource).
+constexpr int kPersistMaxItems = 64;  // items per workgroup (LDS table)
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format (gfx9)
+
+template <int MODE, bool OUTBF, class C>
+__global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_persist_kernel(GemmArgs a) {
+    constexpr int BW = C::BW, BT = C::BT, WM = C::WM, WN = C::WN, FM = C::FM, FT = C::FT, LA = C::LA, LB = C::LB;
+    constexpr int THREADS = C::THREADS;
+    constexpr bool DUAL = (MODE == kRoutedGateUp);
+    constexpr int ROWS = DUAL ? BW / 2 : BW;  // output rows of a row block
+    static_assert(MODE == kRoutedGateUp || MODE == kRoutedDown, "routed modes");
+    static_assert(C::PF == 2, "two register stages");
+    static_assert(!DUAL || (BW / 2) % (THREADS / 8) == 0, "a load piece lies in the gate or the up half");
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BW * RS];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BT * RS];
+    __shared__ int4 items[kPersistMaxItems];
+
+    const int N = a.N, K = a.K, nk = K / BK;
+    const int nrb = (N + ROWS - 1) / ROWS;
+    const int n_items = uniform(*a.n_tiles) * nrb;
+    const int chunk = (n_items + 7) / 8;
+    const int xcd = blockIdx.x & 7, l = blockIdx.x >> 3, nl = gridDim.x >> 3;
+    const int it0 = xcd * chunk + l, it_end = min((xcd + 1) * chunk, n_items);
+    const int n_mine = uniform(it0 < it_end ? min(kPersistMaxItems, (it_end - it0 + nl - 1) / nl) : 0);
+    if (n_mine == 0) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q = lane >> 4, r = lane & 15;
+    const int wm = wave % WM, wn = wave / WM;
+
+    // ---- this workgroup's items: (expert, first pair, pairs, row block); an
+    // invalid tile becomes an empty item (expert 0, no pairs: loads stay in
+    // bounds, nothing is stored)
+    if (tid < n_mine) {
+        const int item = it0 + nl * tid;
+        const int w = a.tiles[item / nrb].w;
+        int first = w >> 16, nt = w & 0xffff;
+        const int o0 = item - first * nrb;
+        if (w < 0 || nt <= 0 || o0 < 0 || o0 >= nt * nrb) {
+            first = item / nrb;
+            nt = 1;
+        }
+        const int off = item - first * nrb, row_blk = off / nt, tile = first + (off - row_blk * nt);
+        const int4 t = a.tiles[tile];
+        const bool ok = t.x >= 0 && t.x < a.n_banks && t.y >= 0 && t.z > 0 && t.z <= BT && t.y + t.z <= a.n_pairs;
+        items[tid] = ok ? make_int4(t.x, t.y, t.z, row_blk) : make_int4(0, 0, 0, 0);
+    }
+    __syncthreads();
+
+    // ---- fixed per-lane pieces: piece p = tid + THREADS*i is tile row p/8,
+    // 16-byte column p%8 of a K step
+    uint32_t aoff[LA];
+    int soff_a[LA], soff_b[LB], brow[LB], bcol[LB];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int p = tid + THREADS * i;
+        const int row = p >> 3, col = (p & 7) * 8;
+        soff_a[i] = lds_off(row, col >> 3);
+        aoff[i] = uint32_t(((DUAL ? (row & (BW / 2 - 1)) : row) * K + col) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int p = tid + THREADS * i;
+        brow[i] = p >> 3;
+        bcol[i] = (p & 7) * 8;
+        soff_b[i] = lds_off(brow[i], bcol[i] >> 3);
+    }
+    const auto rs_x = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.act), 0,
+                                                        uint32_t(size_t(a.n_act_rows) * K * 2), kRsrcWord3);
+    // weight row block of an item (gate/up: the gate and the up halves)
+    auto w_rsrc = [&](const void* bank, int e, int row_blk) __attribute__((always_inline)) {
+        const int r0 = row_blk * ROWS;
+        const uint16_t* p = static_cast<const uint16_t*>(bank) + (size_t(e) * N + r0) * K;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), 0, uint32_t(min(ROWS, N - r0) * K * 2),
+                                                 kRsrcWord3);
+    };
+    auto item_at = [&](int m) __attribute__((always_inline)) {
+        const int4 t = items[m];
+        return make_int4(uniform(t.x), uniform(t.y), uniform(t.z), uniform(t.w));
+    };
+    // token row of B piece i for an item, from its pair id (gate/up) or its
+    // tile row (down); rows past the item's pairs read token row 0
+    auto x_offset = [&](int i, int pair_or_row, bool valid) __attribute__((always_inline)) {
+        int arow = pair_or_row;
+        if constexpr (DUAL) arow = (pair_or_row >= 0 && pair_or_row < a.n_pairs) ? pair_or_row / a.topk : -1;
+        if (!valid || arow < 0 || arow >= a.n_act_rows) arow = 0;
+        return uint32_t((arow * K + bcol[i]) * 2);
+    };
+    auto pair_index = [&](int4 it, int row) __attribute__((always_inline)) {
+        return it.y + (row < it.z ? row : 0);  // in bounds for an empty item too
+    };
+
+    u32x4 wreg[2][LA], xreg[2][LB];
+    auto gload = [&](int stage, const __amdgpu_buffer_rsrc_t& rg, const __amdgpu_buffer_rsrc_t& ru,
+                     const uint32_t (&xo)[LB], int kt) __attribute__((always_inline)) {
+        const int so = kt * BK * 2;
+#pragma unroll
+        for (int i = 0; i < LA; ++i) {
+            const bool up = DUAL && (i * (THREADS / 8) >= BW / 2);
+            wreg[stage][i] = __builtin_amdgcn_raw_buffer_load_b128(up ? ru : rg, aoff[i], so, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < LB; ++i) xreg[stage][i] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, xo[i], so, 0);
+    };
+    auto lstore = [&](int stage, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4*>(&As[buf][soff_a[i]]) = wreg[stage][i];
+#pragma unroll
+        for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4*>(&Bs[buf][soff_b[i]]) = xreg[stage][i];
+    };
+
+    int arow_l[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        if constexpr (DUAL)
+            arow_l[i] = (i >= FM / 2 ? BW / 2 : 0) + wm * (BW / 2 / WM) + (i % (FM / 2)) * 16 + r;
+        else
+            arow_l[i] = wm * (BW / WM) + i * 16 + r;
+    }
+    const int brow_l = wn * (BT / WN) + r;
+    f32x4 acc[FM][FT];
+    // NF (compile time): the wave's token fragments that hold pairs
+    auto compute = [&](int buf, auto nf_c) __attribute__((always_inline)) {
+        constexpr int NF = decltype(nf_c)::value;
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            bf16x8 af[FM];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[i] = lds_frag(&As[buf][lds_off(arow_l[i], ks * 4 + q)]);
+#pragma unroll
+            for (int j = 0; j < NF; ++j) {
+                const bf16x8 bfr = lds_frag(&Bs[buf][lds_off(brow_l + j * 16, ks * 4 + q)]);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr, acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- first item: its token rows, store targets and first two K steps
+    int4 cur = item_at(0);
+    uint32_t xo_cur[LB], xo_nxt[LB];
+    int pn[LB];  // gate/up: pair ids of the next item's token rows
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int v = DUAL ? a.pairs[pair_index(cur, brow[i])] : cur.y + brow[i];
+        xo_cur[i] = x_offset(i, v, brow[i] < cur.z);
+    }
+    // down: pair id (store row) of each of the lane's token columns, one item ahead
+    int ep_cur[FT], ep_nxt[FT];
+    float es_cur[FT];
+    if constexpr (!DUAL) {
+#pragma unroll
+        for (int j = 0; j < FT; ++j) ep_cur[j] = a.pairs[pair_index(cur, wn * (BT / WN) + j * 16 + r)];
+    }
+    auto rg_cur = w_rsrc(a.w0, cur.x, cur.w);
+    auto ru_cur = w_rsrc(DUAL ? a.w1 : a.w0, cur.x, cur.w);
+    gload(0, rg_cur, ru_cur, xo_cur, 0);
+    gload(1, rg_cur, ru_cur, xo_cur, min(1, nk - 1));
+    lstore(0, 0);
+    __syncthreads();
+
+    for (int m = 0; m < n_mine; ++m) {
+        const int4 nxt = item_at(min(m + 1, n_mine - 1));
+        // issued now, used at this item's last K steps / its stores
+#pragma unroll
+        for (int i = 0; i < LB; ++i) pn[i] = DUAL ? a.pairs[pair_index(nxt, brow[i])] : 0;
+        if constexpr (!DUAL) {
+#pragma unroll
+            for (int j = 0; j < FT; ++j) {
+                const int tok = wn * (BT / WN) + j * 16 + r;
+                ep_nxt[j] = a.pairs[pair_index(nxt, tok)];
+                const int pc = ep_cur[j];
+                es_cur[j] = a.row_scale[(pc >= 0 && pc < a.n_pairs) ? pc : 0];
+            }
+        }
+        const auto rg_nxt = w_rsrc(a.w0, nxt.x, nxt.w);
+        const auto ru_nxt = w_rsrc(DUAL ? a.w1 : a.w0, nxt.x, nxt.w);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // K loop; invariant at an even step kt: LDS buffer 0 holds step kt,
+        // register stage 1 holds step kt + 1.  The last trip loads the next
+        // item's steps 0 and 1 (the last item re-reads its own: unused).
+        auto run = [&](auto nf_c) __attribute__((always_inline)) {
+            int kt = 0;
+            for (; kt + 2 < nk; kt += 2) {
+                gload(0, rg_cur, ru_cur, xo_cur, kt + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(0, nf_c);
+                lstore(1, 1);
+                __syncthreads();
+                gload(1, rg_cur, ru_cur, xo_cur, kt + 3);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(1, nf_c);
+                lstore(0, 0);
+                __syncthreads();
+            }
+#pragma unroll
+            for (int i = 0; i < LB; ++i)
+                xo_nxt[i] = x_offset(i, DUAL ? pn[i] : nxt.y + brow[i], brow[i] < nxt.z);
+            gload(0, rg_nxt, ru_nxt, xo_nxt, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(0, nf_c);
+            lstore(1, 1);
+            __syncthreads();
+            gload(1, rg_nxt, ru_nxt, xo_nxt, min(1, nk - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1, nf_c);
+            lstore(0, 0);
+            __syncthreads();
+        };
+        const int nfrag = uniform(min(FT, max(0, (cur.z - wn * (BT / WN) + 15) / 16)));
+        auto dispatch = [&](auto self, auto nf_c) __attribute__((always_inline)) {
+            constexpr int NF = decltype(nf_c)::value;
+            if constexpr (NF == 0)
+                run(nf_c);
+            else if (nfrag == NF)
+                run(nf_c);
+            else
+                self(self, std::integral_constant<int, NF - 1>{});
+        };
+        dispatch(dispatch, std::integral_constant<int, FT>{});
+
+        // ---- stores of this item: lane holds rows 4q..4q+3 of fragment i,
+        // token column r of fragment j
+        const int begin = cur.y, count = cur.z, row_blk = cur.w;
+#pragma unroll
+        for (int j = 0; j < FT; ++j) {
+            const int tok = wn * (BT / WN) + j * 16 + r;
+            if (tok >= count) continue;
+            if constexpr (DUAL) {
+#pragma unroll
+                for (int i = 0; i < FM / 2; ++i) {
+                    const int f = row_blk * (BW / 2) + wm * (BW / 2 / WM) + i * 16 + 4 * q;
+                    if (f >= N) continue;
+                    float v[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const float g = acc[i][j][t];
+                        v[t] = g / (1.0f + __expf(-g)) * acc[i + FM / 2][j][t];
+                    }
+                    const size_t o = size_t(begin + tok) * N + f;
+                    if constexpr (OUTBF)
+                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) =
+                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    else
+                        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) =
+                            make_float4(v[0], v[1], v[2], v[3]);
+                }
+            } else {
+                const int pair = ep_cur[j];
+                if (pair < 0 || pair >= a.n_pairs) continue;
+                const float s = es_cur[j];
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int d = row_blk * BW + wm * (BW / WM) + i * 16 + 4 * q;
+                    if (d >= N) continue;
+                    const float v0 = s * acc[i][j][0], v1 = s * acc[i][j][1], v2 = s * acc[i][j][2],
+                                v3 = s * acc[i][j][3];
+                    const size_t o = size_t(pair) * N + d;
+                    if constexpr (OUTBF)
+                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) =
+                            make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+                    else
+                        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) = make_float4(v0, v1, v2, v3);
+                }
+            }
+        }
+        cur = nxt;
+        rg_cur = rg_nxt;
+        ru_cur = ru_nxt;
+#pragma unroll
+        for (int i = 0; i < LB; ++i) xo_cur[i] = xo_nxt[i];
+        if constexpr (!DUAL) {
+#pragma unroll
+            for (int j = 0; j < FT; ++j) ep_cur[j] = ep_nxt[j];
+        }
+    }
+}
+
 int tiled_rows() { return CfgLarge::BT; }
 int tiled_rows_dense() { return CfgSmall::BT; }
 
@@ -364,8 +657,30 @@ static hipError_t launch_cfg(int mode, bool outbf, const GemmArgs& a, int grid_x
 // Routed modes use the large tile (grid_x = routed tiles of tiled_rows()
 // pairs); dense modes the small one (grid_x = token tiles of
 // tiled_rows_dense() tokens).
+// Persistent routed launch: one workgroup per CU (at most), each XCD's 32
+// taking its run of items in turn.  Needs an even number of K steps, byte
+// offsets inside 32 bits and at most kPersistMaxItems items per workgroup.
+static bool launch_persist(int mode, bool outbf, const GemmArgs& a, int max_tiles, hipStream_t s) {
+    using C = CfgLarge;
+    const int rows = mode == kRoutedGateUp ? C::BW / 2 : C::BW;
+    const long long max_items = (long long)max_tiles * ((a.N + rows - 1) / rows);
+    const long long per_xcd = (max_items + 7) / 8;
+    const int nl = int(std::min<long long>(32, per_xcd));
+    if (nl <= 0 || a.K % (2 * BK) || (per_xcd + nl - 1) / nl > kPersistMaxItems) return false;
+    if ((unsigned long long)a.n_act_rows * a.K * 2 >= (1ull << 32) ||
+        (unsigned long long)rows * a.K * 2 >= (1ull << 32))
+        return false;
+    const dim3 g(unsigned(8 * nl)), b(C::THREADS);
+    if (mode == kRoutedGateUp) gemm_routed_persist_kernel<kRoutedGateUp, true, C><<<g, b, 0, s>>>(a);
+    else if (outbf) gemm_routed_persist_kernel<kRoutedDown, true, C><<<g, b, 0, s>>>(a);
+    else gemm_routed_persist_kernel<kRoutedDown, false, C><<<g, b, 0, s>>>(a);
+    return true;
+}
+
 hipError_t launch_gemm_tiled(int mode, bool outbf, const GemmArgs& a, int grid_x, hipStream_t s) {
     if (grid_x <= 0) return hipSuccess;
+    if ((mode == kRoutedGateUp || mode == kRoutedDown) && launch_persist(mode, outbf, a, grid_x, s))
+        return hipGetLastError();
     if (mode == kRoutedGateUp || mode == kRoutedDown) return launch_cfg<CfgLarge>(mode, outbf, a, grid_x, s);
     return launch_cfg<CfgSmall>(mode, outbf, a, grid_x, s);
 }
