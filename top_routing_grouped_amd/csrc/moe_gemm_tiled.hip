@@ -32,6 +32,7 @@ namespace moe {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 64;  // K per step
 constexpr int RS = BK;  // LDS row stride (elements)
@@ -352,17 +353,72 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_tiled_kernel(GemmArg
 constexpr int kPersistMaxItems = 64;  // items per workgroup (LDS table)
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format (gfx9)
 
+// ---- K steps straight into LDS
+// The K steps go from global memory straight into a ring of three LDS stages
+// (buffer loads with the LDS bit: lane i's 16 bytes land at the stage's
+// address + 16 i, so each lane loads the piece that the XOR swizzle puts at
+// its slot), two steps ahead: no staging registers and no LDS write
+// instructions.  Waits are explicit: the vector memory counter retires in
+// order, so "at most N newer operations in flight" is exact when every
+// operation between two waits has a fixed count per wave.  Per K step each
+// wave issues kDmaPerStep loads; the stores of an item are kStores buffer
+// stores (masked elements go to an offset past the buffer, which the
+// hardware drops) and the next item's prefetch is a fixed number of loads.
+// The barrier is a bare s_barrier: the workgroup fence of __syncthreads would
+// wait for every load in flight.
+template <int N>
+__device__ __forceinline__ void vm_wait_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (0 << 8) | (7 << 4) | (N & 15));
+}
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+// 16 bytes per lane from a buffer straight into LDS at dst + 16 * lane.  A
+// plain device function: inside the kernel template the builtin made the
+// host compilation pass drop the kernel's launch stub without a diagnostic.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(dst), 16, voff, soff, 0, 0);
+}
+// Fragment reads from the ring are inline asm: the compiler, seeing a plain
+// LDS read while DMA into the same array is in flight, waits for every load
+// in flight (it cannot tell the stages apart).  After the asm reads, an
+// explicit lgkmcnt(0) wait that names the fragments as operands keeps their
+// uses (the MFMAs) behind it.
+__device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+__device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+__device__ __forceinline__ void lgkm_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
+constexpr uint32_t kDropOffset = 0x80000000u;  // past every buffer: the store is dropped
+
 template <int MODE, bool OUTBF, class C>
-__global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_persist_kernel(GemmArgs a) {
-    constexpr int BW = C::BW, BT = C::BT, WM = C::WM, WN = C::WN, FM = C::FM, FT = C::FT, LA = C::LA, LB = C::LB;
-    constexpr int THREADS = C::THREADS;
+__global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs a) {
+    constexpr int BW = C::BW, BT = C::BT, WM = C::WM, WN = C::WN, FM = C::FM, FT = C::FT;
+    constexpr int NW = C::NW;
     constexpr bool DUAL = (MODE == kRoutedGateUp);
-    constexpr int ROWS = DUAL ? BW / 2 : BW;  // output rows of a row block
+    constexpr int ROWS = DUAL ? BW / 2 : BW;
+    constexpr int NST = 3;                  // LDS stages
+    constexpr int STAGE = (BW + BT) * RS;   // elements: A rows then B rows
+    constexpr int AJ = BW / 8 / NW;         // 8-row A blocks per wave per step
+    constexpr int BJ = BT / 8 / NW;         // 8-row B blocks per wave per step
+    constexpr int kDmaPerStep = AJ + BJ;
+    constexpr int kStores = DUAL ? FT * FM / 2 : FT * FM;
+    constexpr int kPrefetch = DUAL ? BJ : 2 * FT;
     static_assert(MODE == kRoutedGateUp || MODE == kRoutedDown, "routed modes");
-    static_assert(C::PF == 2, "two register stages");
-    static_assert(!DUAL || (BW / 2) % (THREADS / 8) == 0, "a load piece lies in the gate or the up half");
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BW * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BT * RS];
+    static_assert(AJ * 8 * NW == BW && BJ * 8 * NW == BT, "whole 8-row blocks per wave");
+    static_assert(!DUAL || (NW / 2) * AJ * 8 == BW / 2, "a wave's A rows lie in the gate or the up half");
+    static_assert(6 + kStores + kPrefetch + kDmaPerStep < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[NST][STAGE];
     __shared__ int4 items[kPersistMaxItems];
 
     const int N = a.N, K = a.K, nk = K / BK;
@@ -373,13 +429,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_persist_kernel(Gemm
     const int it0 = xcd * chunk + l, it_end = min((xcd + 1) * chunk, n_items);
     const int n_mine = uniform(it0 < it_end ? min(kPersistMaxItems, (it_end - it0 + nl - 1) / nl) : 0);
     if (n_mine == 0) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int q = lane >> 4, r = lane & 15;
     const int wm = wave % WM, wn = wave / WM;
 
-    // ---- this workgroup's items: (expert, first pair, pairs, row block); an
-    // invalid tile becomes an empty item (expert 0, no pairs: loads stay in
-    // bounds, nothing is stored)
     if (tid < n_mine) {
         const int item = it0 + nl * tid;
         const int w = a.tiles[item / nrb].w;
@@ -396,30 +449,32 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_persist_kernel(Gemm
     }
     __syncthreads();
 
-    // ---- fixed per-lane pieces: piece p = tid + THREADS*i is tile row p/8,
-    // 16-byte column p%8 of a K step
-    uint32_t aoff[LA];
-    int soff_a[LA], soff_b[LB], brow[LB], bcol[LB];
+    // ---- this lane's DMA pieces: A block j covers tile rows wave*8*AJ + 8j ..
+    // +7, lane = 8 * (row in block) + slot; the slot holds logical 16-byte
+    // piece slot ^ ((row >> 1) & 7)
+    uint32_t aoff[AJ];
+    int brow[BJ], bpiece[BJ];
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
-        const int p = tid + THREADS * i;
-        const int row = p >> 3, col = (p & 7) * 8;
-        soff_a[i] = lds_off(row, col >> 3);
-        aoff[i] = uint32_t(((DUAL ? (row & (BW / 2 - 1)) : row) * K + col) * 2);
+    for (int j = 0; j < AJ; ++j) {
+        const int ra = wave * 8 * AJ + 8 * j + (lane >> 3);
+        const int p = (lane & 7) ^ ((ra >> 1) & 7);
+        aoff[j] = uint32_t(((DUAL ? (ra & (BW / 2 - 1)) : ra) * K + 8 * p) * 2);
     }
 #pragma unroll
-    for (int i = 0; i < LB; ++i) {
-        const int p = tid + THREADS * i;
-        brow[i] = p >> 3;
-        bcol[i] = (p & 7) * 8;
-        soff_b[i] = lds_off(brow[i], bcol[i] >> 3);
+    for (int j = 0; j < BJ; ++j) {
+        brow[j] = wave * 8 * BJ + 8 * j + (lane >> 3);
+        bpiece[j] = (lane & 7) ^ ((brow[j] >> 1) & 7);
     }
+    const bool up_wave = DUAL && wave * 8 * AJ >= BW / 2;
     const auto rs_x = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.act), 0,
                                                         uint32_t(size_t(a.n_act_rows) * K * 2), kRsrcWord3);
-    // weight row block of an item (gate/up: the gate and the up halves)
-    auto w_rsrc = [&](const void* bank, int e, int row_blk) __attribute__((always_inline)) {
-        const int r0 = row_blk * ROWS;
-        const uint16_t* p = static_cast<const uint16_t*>(bank) + (size_t(e) * N + r0) * K;
+    const auto rs_out = __builtin_amdgcn_make_buffer_rsrc(
+        a.out, 0, uint32_t(size_t(a.n_pairs) * N * (OUTBF ? 2 : 4)), kRsrcWord3);
+    // this wave's weight rows of an item (gate/up: gate or up half by wave)
+    auto w_rsrc = [&](int4 it) __attribute__((always_inline)) {
+        const int r0 = it.w * ROWS;
+        const void* bank = up_wave ? a.w1 : a.w0;
+        const uint16_t* p = static_cast<const uint16_t*>(bank) + (size_t(it.x) * N + r0) * K;
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), 0, uint32_t(min(ROWS, N - r0) * K * 2),
                                                  kRsrcWord3);
     };
@@ -427,35 +482,26 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_persist_kernel(Gemm
         const int4 t = items[m];
         return make_int4(uniform(t.x), uniform(t.y), uniform(t.z), uniform(t.w));
     };
-    // token row of B piece i for an item, from its pair id (gate/up) or its
-    // tile row (down); rows past the item's pairs read token row 0
-    auto x_offset = [&](int i, int pair_or_row, bool valid) __attribute__((always_inline)) {
+    auto pair_index = [&](int4 it, int row) __attribute__((always_inline)) {
+        return it.y + (row < it.z ? row : 0);
+    };
+    auto x_offset = [&](int j, int pair_or_row, bool valid) __attribute__((always_inline)) {
         int arow = pair_or_row;
         if constexpr (DUAL) arow = (pair_or_row >= 0 && pair_or_row < a.n_pairs) ? pair_or_row / a.topk : -1;
         if (!valid || arow < 0 || arow >= a.n_act_rows) arow = 0;
-        return uint32_t((arow * K + bcol[i]) * 2);
+        return uint32_t((arow * K + 8 * bpiece[j]) * 2);
     };
-    auto pair_index = [&](int4 it, int row) __attribute__((always_inline)) {
-        return it.y + (row < it.z ? row : 0);  // in bounds for an empty item too
-    };
-
-    u32x4 wreg[2][LA], xreg[2][LB];
-    auto gload = [&](int stage, const __amdgpu_buffer_rsrc_t& rg, const __amdgpu_buffer_rsrc_t& ru,
-                     const uint32_t (&xo)[LB], int kt) __attribute__((always_inline)) {
+    // K step kt of an item into LDS stage st
+    auto dma = [&](int st, const __amdgpu_buffer_rsrc_t& rw, const uint32_t (&xo)[BJ], int kt)
+                   __attribute__((always_inline)) {
         const int so = kt * BK * 2;
+        uint16_t* base = &lds[st][0];
 #pragma unroll
-        for (int i = 0; i < LA; ++i) {
-            const bool up = DUAL && (i * (THREADS / 8) >= BW / 2);
-            wreg[stage][i] = __builtin_amdgcn_raw_buffer_load_b128(up ? ru : rg, aoff[i], so, 0);
-        }
+        for (int j = 0; j < AJ; ++j)
+            dma16(rw, base + (wave * 8 * AJ + 8 * j) * RS, aoff[j], so);
 #pragma unroll
-        for (int i = 0; i < LB; ++i) xreg[stage][i] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, xo[i], so, 0);
-    };
-    auto lstore = [&](int stage, int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4*>(&As[buf][soff_a[i]]) = wreg[stage][i];
-#pragma unroll
-        for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4*>(&Bs[buf][soff_b[i]]) = xreg[stage][i];
+        for (int j = 0; j < BJ; ++j)
+            dma16(rs_x, base + (BW + wave * 8 * BJ + 8 * j) * RS, xo[j], so);
     };
 
     int arow_l[FM];
@@ -468,100 +514,136 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_persist_kernel(Gemm
     }
     const int brow_l = wn * (BT / WN) + r;
     f32x4 acc[FM][FT];
-    // NF (compile time): the wave's token fragments that hold pairs
-    auto compute = [&](int buf, auto nf_c) __attribute__((always_inline)) {
+    // byte offsets of the wave's fragments inside a stage: [ks][fragment]
+    uint32_t aofs[2][FM], bofs[2][FT];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) aofs[ks][i] = uint32_t(lds_off(arow_l[i], ks * 4 + q) * 2);
+#pragma unroll
+        for (int jj = 0; jj < FT; ++jj) bofs[ks][jj] = uint32_t((BW * RS + lds_off(brow_l + jj * 16, ks * 4 + q)) * 2);
+    }
+    const uint32_t lds0 = lds_byte_addr(&lds[0][0]);
+    static_assert(BK == 64, "two 32-wide MFMA K steps per stage");
+    auto compute = [&](int st, auto nf_c) __attribute__((always_inline)) {
         constexpr int NF = decltype(nf_c)::value;
+        const uint32_t sb = lds0 + uint32_t(st * STAGE * 2);
+        u32x4 af[2][FM], bfv[2][NF > 0 ? NF : 1];
+        auto reads = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-            bf16x8 af[FM];
+            for (int i = 0; i < FM; ++i) af[ks][i] = ds_read16(sb + aofs[ks][i]);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = lds_frag(&As[buf][lds_off(arow_l[i], ks * 4 + q)]);
+            for (int jj = 0; jj < NF; ++jj) bfv[ks][jj] = ds_read16(sb + bofs[ks][jj]);
+        };
+        auto ready = [&](int ks) __attribute__((always_inline)) {
+            lgkm_wait_all();
 #pragma unroll
-            for (int j = 0; j < NF; ++j) {
-                const bf16x8 bfr = lds_frag(&Bs[buf][lds_off(brow_l + j * 16, ks * 4 + q)]);
+            for (int i = 0; i < FM; ++i) tie(af[ks][i]);
+#pragma unroll
+            for (int jj = 0; jj < NF; ++jj) tie(bfv[ks][jj]);
+        };
+        auto mfmas = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+            for (int jj = 0; jj < NF; ++jj)
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr, acc[i][j], 0, 0, 0);
-            }
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[ks][i]),
+                                                                         __builtin_bit_cast(bf16x8, bfv[ks][jj]),
+                                                                         acc[i][jj], 0, 0, 0);
+        };
+        if constexpr (NF > 0) {
+            reads(0);
+            ready(0);
+            reads(1);  // in flight during the first half's MFMAs
+            mfmas(0);
+            ready(1);
+            mfmas(1);
         }
     };
 
-    // ---- first item: its token rows, store targets and first two K steps
+    // ---- prologue: first item's token rows and store targets, its first two
+    // K steps, and kStores dropped stores so every item starts with the same
+    // count of operations in flight
     int4 cur = item_at(0);
-    uint32_t xo_cur[LB], xo_nxt[LB];
-    int pn[LB];  // gate/up: pair ids of the next item's token rows
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-        const int v = DUAL ? a.pairs[pair_index(cur, brow[i])] : cur.y + brow[i];
-        xo_cur[i] = x_offset(i, v, brow[i] < cur.z);
-    }
-    // down: pair id (store row) of each of the lane's token columns, one item ahead
+    uint32_t xo_cur[BJ], xo_nxt[BJ];
+    int pn[BJ];
     int ep_cur[FT], ep_nxt[FT];
     float es_cur[FT];
+#pragma unroll
+    for (int j = 0; j < BJ; ++j) {
+        const int v = DUAL ? a.pairs[pair_index(cur, brow[j])] : cur.y + brow[j];
+        xo_cur[j] = x_offset(j, v, brow[j] < cur.z);
+    }
     if constexpr (!DUAL) {
 #pragma unroll
         for (int j = 0; j < FT; ++j) ep_cur[j] = a.pairs[pair_index(cur, wn * (BT / WN) + j * 16 + r)];
     }
-    auto rg_cur = w_rsrc(a.w0, cur.x, cur.w);
-    auto ru_cur = w_rsrc(DUAL ? a.w1 : a.w0, cur.x, cur.w);
-    gload(0, rg_cur, ru_cur, xo_cur, 0);
-    gload(1, rg_cur, ru_cur, xo_cur, min(1, nk - 1));
-    lstore(0, 0);
-    __syncthreads();
+    auto rw_cur = w_rsrc(cur);
+    dma(0, rw_cur, xo_cur, 0);
+    dma(1, rw_cur, xo_cur, 1);
+#pragma unroll
+    for (int i = 0; i < kStores; ++i) {  // distinct offsets: identical stores would be merged
+        if constexpr (OUTBF || DUAL)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, rs_out, kDropOffset + 16u * i, 0, 0);
+        else
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, rs_out, kDropOffset + 16u * i, 0, 0);
+    }
+    int g = 0;  // global K step: LDS stage g % 3
+    // the next item's token-row offsets are formed at step kx, after a wait
+    // that covers the item-top prefetch (K steps >= 4); with 2 K steps at step 0
+    const int kx = nk >= 4 ? 2 : 0;
 
     for (int m = 0; m < n_mine; ++m) {
         const int4 nxt = item_at(min(m + 1, n_mine - 1));
-        // issued now, used at this item's last K steps / its stores
+        const auto rw_nxt = w_rsrc(nxt);
+        // item-top prefetch, kPrefetch loads: the next item's token rows
+        // (gate/up) or store rows (down), and this item's routing weights
 #pragma unroll
-        for (int i = 0; i < LB; ++i) pn[i] = DUAL ? a.pairs[pair_index(nxt, brow[i])] : 0;
+        for (int jj = 0; jj < BJ; ++jj) pn[jj] = DUAL ? a.pairs[pair_index(nxt, brow[jj])] : 0;
         if constexpr (!DUAL) {
 #pragma unroll
-            for (int j = 0; j < FT; ++j) {
-                const int tok = wn * (BT / WN) + j * 16 + r;
-                ep_nxt[j] = a.pairs[pair_index(nxt, tok)];
-                const int pc = ep_cur[j];
-                es_cur[j] = a.row_scale[(pc >= 0 && pc < a.n_pairs) ? pc : 0];
+            for (int jj = 0; jj < FT; ++jj) {
+                ep_nxt[jj] = a.pairs[pair_index(nxt, wn * (BT / WN) + jj * 16 + r)];
+                const int pc = ep_cur[jj];
+                es_cur[jj] = a.row_scale[(pc >= 0 && pc < a.n_pairs) ? pc : 0];
             }
         }
-        const auto rg_nxt = w_rsrc(a.w0, nxt.x, nxt.w);
-        const auto ru_nxt = w_rsrc(DUAL ? a.w1 : a.w0, nxt.x, nxt.w);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        // K loop; invariant at an even step kt: LDS buffer 0 holds step kt,
-        // register stage 1 holds step kt + 1.  The last trip loads the next
-        // item's steps 0 and 1 (the last item re-reads its own: unused).
-        auto run = [&](auto nf_c) __attribute__((always_inline)) {
-            int kt = 0;
-            for (; kt + 2 < nk; kt += 2) {
-                gload(0, rg_cur, ru_cur, xo_cur, kt + 2);
-                __builtin_amdgcn_sched_barrier(0);
-                compute(0, nf_c);
-                lstore(1, 1);
-                __syncthreads();
-                gload(1, rg_cur, ru_cur, xo_cur, kt + 3);
-                __builtin_amdgcn_sched_barrier(0);
-                compute(1, nf_c);
-                lstore(0, 0);
-                __syncthreads();
-            }
-#pragma unroll
-            for (int i = 0; i < LB; ++i)
-                xo_nxt[i] = x_offset(i, DUAL ? pn[i] : nxt.y + brow[i], brow[i] < nxt.z);
-            gload(0, rg_nxt, ru_nxt, xo_nxt, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(0, nf_c);
-            lstore(1, 1);
-            __syncthreads();
-            gload(1, rg_nxt, ru_nxt, xo_nxt, min(1, nk - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            compute(1, nf_c);
-            lstore(0, 0);
-            __syncthreads();
-        };
+            for (int jj = 0; jj < FT; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int nfrag = uniform(min(FT, max(0, (cur.z - wn * (BT / WN) + 15) / 16)));
+
+        auto run = [&](auto nf_c) __attribute__((always_inline)) {
+            auto step = [&](int kt) __attribute__((always_inline)) {
+                if (kt == kx) {
+                    if (nk < 4) vm_wait_lgkm0<0>();
+#pragma unroll
+                    for (int jj = 0; jj < BJ; ++jj)
+                        xo_nxt[jj] = x_offset(jj, DUAL ? pn[jj] : nxt.y + brow[jj], brow[jj] < nxt.z);
+                }
+                const int st = (g + 2) % NST;
+                if (kt + 2 < nk)
+                    dma(st, rw_cur, xo_cur, kt + 2);
+                else
+                    dma(st, rw_nxt, xo_nxt, kt + 2 - nk);
+                compute(g % NST, nf_c);
+                ++g;
+            };
+            // steps 0 and 1: newer than their DMA: the next step's DMA, the
+            // stores and the prefetch
+            vm_wait_lgkm0<kDmaPerStep + kStores + kPrefetch>();
+            bare_barrier();
+            step(0);
+            vm_wait_lgkm0<kDmaPerStep + kStores + kPrefetch>();
+            bare_barrier();
+            step(1);
+            for (int kt = 2; kt < nk; ++kt) {
+                vm_wait_lgkm0<kDmaPerStep>();
+                bare_barrier();
+                step(kt);
+            }
+        };
         auto dispatch = [&](auto self, auto nf_c) __attribute__((always_inline)) {
             constexpr int NF = decltype(nf_c)::value;
             if constexpr (NF == 0)
@@ -572,62 +654,63 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_persist_kernel(Gemm
                 self(self, std::integral_constant<int, NF - 1>{});
         };
         dispatch(dispatch, std::integral_constant<int, FT>{});
+        // exactly the two newest steps' DMA may be in flight here; everything
+        // older (the prefetch) is complete
+        vm_wait_lgkm0<2 * kDmaPerStep>();
 
-        // ---- stores of this item: lane holds rows 4q..4q+3 of fragment i,
-        // token column r of fragment j
+        // ---- stores: kStores buffer stores per wave, masked ones dropped
         const int begin = cur.y, count = cur.z, row_blk = cur.w;
 #pragma unroll
         for (int j = 0; j < FT; ++j) {
             const int tok = wn * (BT / WN) + j * 16 + r;
-            if (tok >= count) continue;
+            const bool tok_ok = tok < count;
             if constexpr (DUAL) {
 #pragma unroll
                 for (int i = 0; i < FM / 2; ++i) {
                     const int f = row_blk * (BW / 2) + wm * (BW / 2 / WM) + i * 16 + 4 * q;
-                    if (f >= N) continue;
                     float v[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        const float g = acc[i][j][t];
-                        v[t] = g / (1.0f + __expf(-g)) * acc[i + FM / 2][j][t];
+                        const float gt = acc[i][j][t];
+                        v[t] = gt / (1.0f + __expf(-gt)) * acc[i + FM / 2][j][t];
                     }
-                    const size_t o = size_t(begin + tok) * N + f;
-                    if constexpr (OUTBF)
-                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) =
-                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                    else
-                        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) =
-                            make_float4(v[0], v[1], v[2], v[3]);
+                    const uint32_t o = (tok_ok && f < N) ? uint32_t(((begin + tok) * N + f) * 2) : kDropOffset;
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])},
+                                                          rs_out, o, 0, 0);
                 }
             } else {
                 const int pair = ep_cur[j];
-                if (pair < 0 || pair >= a.n_pairs) continue;
+                const bool ok = tok_ok && pair >= 0 && pair < a.n_pairs;
                 const float s = es_cur[j];
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
                     const int d = row_blk * BW + wm * (BW / WM) + i * 16 + 4 * q;
-                    if (d >= N) continue;
+                    const bool st_ok = ok && d < N;
                     const float v0 = s * acc[i][j][0], v1 = s * acc[i][j][1], v2 = s * acc[i][j][2],
                                 v3 = s * acc[i][j][3];
-                    const size_t o = size_t(pair) * N + d;
-                    if constexpr (OUTBF)
-                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) =
-                            make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-                    else
-                        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) = make_float4(v0, v1, v2, v3);
+                    if constexpr (OUTBF) {
+                        const uint32_t o = st_ok ? uint32_t((pair * N + d) * 2) : kDropOffset;
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)},
+                                                              rs_out, o, 0, 0);
+                    } else {
+                        const uint32_t o = st_ok ? uint32_t((pair * N + d) * 4) : kDropOffset;
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            u32x4{__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3)},
+                            rs_out, o, 0, 0);
+                    }
                 }
             }
         }
         cur = nxt;
-        rg_cur = rg_nxt;
-        ru_cur = ru_nxt;
+        rw_cur = rw_nxt;
 #pragma unroll
-        for (int i = 0; i < LB; ++i) xo_cur[i] = xo_nxt[i];
+        for (int j = 0; j < BJ; ++j) xo_cur[j] = xo_nxt[j];
         if constexpr (!DUAL) {
 #pragma unroll
             for (int j = 0; j < FT; ++j) ep_cur[j] = ep_nxt[j];
         }
     }
+    vm_wait_lgkm0<0>();
 }
 
 int tiled_rows() { return CfgLarge::BT; }
@@ -671,9 +754,11 @@ static bool launch_persist(int mode, bool outbf, const GemmArgs& a, int max_tile
         (unsigned long long)rows * a.K * 2 >= (1ull << 32))
         return false;
     const dim3 g(unsigned(8 * nl)), b(C::THREADS);
-    if (mode == kRoutedGateUp) gemm_routed_persist_kernel<kRoutedGateUp, true, C><<<g, b, 0, s>>>(a);
-    else if (outbf) gemm_routed_persist_kernel<kRoutedDown, true, C><<<g, b, 0, s>>>(a);
-    else gemm_routed_persist_kernel<kRoutedDown, false, C><<<g, b, 0, s>>>(a);
+    // stores address the output with 32-bit offsets below the drop offset
+    if ((unsigned long long)a.n_pairs * a.N * (outbf || mode == kRoutedGateUp ? 2 : 4) >= (1ull << 31)) return false;
+    if (mode == kRoutedGateUp) gemm_routed_dma_kernel<kRoutedGateUp, true, C><<<g, b, 0, s>>>(a);
+    else if (outbf) gemm_routed_dma_kernel<kRoutedDown, true, C><<<g, b, 0, s>>>(a);
+    else gemm_routed_dma_kernel<kRoutedDown, false, C><<<g, b, 0, s>>>(a);
     return true;
 }
 
