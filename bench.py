@@ -171,15 +171,38 @@ def time_layer(insts, steps, warmup):
     for i in range(max(1, warmup // L)):
         chain.replay()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps // L):
+    n_chain = steps // L
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_chain + 2)]
+    evs[0].record()
+    for c in range(n_chain):
         chain.replay()
+        evs[c + 1].record()
     for i in range(steps % L):
         insts[i].graph.replay()
-    end.record()
+    evs[-1].record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    total = evs[0].elapsed_time(evs[-1]) / steps
+    per_chain = sorted(evs[c].elapsed_time(evs[c + 1]) / L for c in range(n_chain))
+    median = per_chain[len(per_chain) // 2] if per_chain else total
+    return total, median
+
+
+def cold_layer_ms(insts, reps=10, flush_bytes=512 << 20):
+    """Single-layer latency after writing a 512 MB buffer (evicts the
+    last-level cache): median over `reps` instances' single-layer graphs."""
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    times = []
+    for i in range(reps):
+        inst = insts[i % len(insts)]
+        flush.fill_(float(i))
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        inst.graph.replay()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    del flush
+    return sorted(times)[len(times) // 2]
 
 
 def time_stage(insts, stage, reps):
@@ -286,7 +309,8 @@ def copy_calibration(nbytes=1 << 30):
 def run_workload(name, T, L, steps, warmup, stage_reps):
     spec = WORKLOADS[name].with_tokens(T)
     insts = build_instances(spec, L, f"{name} T={T}")
-    ms = time_layer(insts, steps, warmup)
+    ms, ms_median = time_layer(insts, steps, warmup)
+    cold_ms = cold_layer_ms(insts)
     n_act = [inst.n_active() for inst in insts]
     mean_act = float(np.mean(n_act))
     byts = float(np.mean([layer_bytes(spec, a) for a in n_act]))
@@ -296,8 +320,11 @@ def run_workload(name, T, L, steps, warmup, stage_reps):
     gu_bytes = float(np.mean([gateup_bytes(spec, a) for a in n_act]))
     gu_flops = gateup_flops(spec)
     gu_t = stage_ms / 1e3
+    t_hbm, t_mfma = byts / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
     res = {
         "spec": spec, "insts": insts, "ms_per_step": ms, "tokens_per_s": T / t,
+        "median_chain_us_per_layer": ms_median * 1e3, "cold_layer_us": cold_ms * 1e3,
+        "mfma_ceiling": t_mfma / max(t_hbm, t_mfma),
         "n_active_mean": mean_act, "layer_bytes": byts, "layer_flops": flops,
         "layer_hbm_frac": byts / t / (HBM_PEAK_GBS * 1e9), "layer_mfma_frac": flops / t / (BF16_PEAK_TFLOPS * 1e12),
         "gateup_ms": stage_ms, "gateup_bytes": gu_bytes, "gateup_flops": gu_flops,
@@ -305,7 +332,8 @@ def run_workload(name, T, L, steps, warmup, stage_reps):
     }
     log(f"{name} T={T}: {ms * 1e3:.1f} us/layer, {T / t:,.0f} tok/s, n_active {mean_act:.1f}, "
         f"layer {byts / t / 1e9:,.0f} GB/s ({res['layer_hbm_frac']:.1%} HBM), "
-        f"{flops / t / 1e12:.1f} TFLOP/s ({res['layer_mfma_frac']:.1%} MFMA); gate/up {stage_ms * 1e3:.1f} us = "
+        f"{flops / t / 1e12:.1f} TFLOP/s ({res['layer_mfma_frac']:.1%} MFMA, ceiling {res['mfma_ceiling']:.1%}); "
+        f"median chain {ms_median * 1e3:.1f} us/layer, cold single layer {cold_ms * 1e3:.1f} us; gate/up {stage_ms * 1e3:.1f} us = "
         f"{res['gateup_gbs']:,.0f} GB/s, {res['gateup_tflops']:.1f} TFLOP/s")
     return res
 
@@ -332,9 +360,9 @@ def prefill_roofline(pre):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--instances", type=int, default=16)
+    ap.add_argument("--steps", type=int, default=800)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--instances", type=int, default=40)
     ap.add_argument("--stage-reps", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -385,7 +413,12 @@ def main():
                    "shared_gate": True, "layer_instances": args.instances,
                    "n_active_mean": round(dec["n_active_mean"], 2),
                    "layer_algorithmic_bytes": round(dec["layer_bytes"]),
-                   "layer_hbm_frac": round(dec["layer_hbm_frac"], 4)},
+                   "layer_algorithmic_flops": round(dec["layer_flops"]),
+                   "layer_hbm_frac": round(dec["layer_hbm_frac"], 4),
+                   "layer_mfma_frac": round(dec["layer_mfma_frac"], 4),
+                   "mfma_ceiling": round(dec["mfma_ceiling"], 4),
+                   "median_chain_us_per_layer": round(dec["median_chain_us_per_layer"], 2),
+                   "cold_layer_us": round(dec["cold_layer_us"], 2)},
         "roofline": {"kernel": "routed gate/up GEMM + SwiGLU", "bound": "hbm",
                      "achieved": round(dec["gateup_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec["gateup_gbs"] / HBM_PEAK_GBS, 4),
@@ -393,13 +426,17 @@ def main():
                      "algorithmic_bytes": round(dec["gateup_bytes"])},
     }
     if not args.no_prefill:
-        pre = run_workload("qwen_prefill_skew", 4096, 4, max(4, args.steps // 40), max(2, args.warmup // 10),
+        pre = run_workload("qwen_prefill_skew", 4096, 4, max(80, args.steps // 10), max(20, args.warmup // 10),
                            max(8, args.stage_reps // 4))
         line["secondary"] = {
             "workload": "Qwen3.6-35B-A3B MoE layer forward, prefill T=4096, skewed routing",
             "value": round(pre["tokens_per_s"], 1), "unit": "tokens/s",
             "ms_per_step": round(pre["ms_per_step"], 6), "n_active_mean": round(pre["n_active_mean"], 2),
             "layer_mfma_frac": round(pre["layer_mfma_frac"], 4), "layer_hbm_frac": round(pre["layer_hbm_frac"], 4),
+            "mfma_ceiling": round(pre["mfma_ceiling"], 4), "layer_algorithmic_bytes": round(pre["layer_bytes"]),
+            "layer_algorithmic_flops": round(pre["layer_flops"]),
+            "median_chain_us_per_layer": round(pre["median_chain_us_per_layer"], 2),
+            "cold_layer_us": round(pre["cold_layer_us"], 2),
             "roofline": prefill_roofline(pre),
         }
         del pre
