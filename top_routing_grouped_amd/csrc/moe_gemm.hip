@@ -448,7 +448,11 @@ static hipError_t launch_cfg(const GemmArgs& a, int grid_x, int tf, hipStream_t 
     constexpr int SPAN = 4 * WTraits<WK>::KL;
     const bool ksplit4 = (kwg % (4 * SPAN) == 0);
     const bool ksplit2 = (kwg % (2 * SPAN) == 0);
-    if (MODE == kSmallDown && kwg % SPAN == 0) {
+    if (SMALL && kwg % SPAN == 0) {
+        // small T: 64 weight rows per workgroup, no K split (measured at
+        // decode shapes: a quarter of the workgroups of 16-row, 4-way-K
+        // tiles, so all are resident at once and the per-workgroup routing
+        // decode runs a quarter as often)
         dim3 g(grid_x, (nrows + 63) / 64, ks);
         gemm_kernel<MODE, WK, OUTBF, 1, 4, 1><<<g, 256, 0, s>>>(a);
     } else if (tf == 1 || SMALL) {
