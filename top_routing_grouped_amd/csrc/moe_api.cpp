@@ -310,11 +310,33 @@ moe::GemmArgs small_args(const moe_config& c, const Layout& L, void* ws, const m
     return a;
 }
 
+// The small-T gate/up launch does the softmax selection itself (saving the
+// routing launch) for up to kFusedSelMaxT tokens.
+bool select_fused(const moe_config& c) {
+    return small_path(c) && c.family == MOE_ROUTE_SOFTMAX_TOPK && c.n_tokens <= moe::kFusedSelMaxT &&
+           c.n_experts <= 256 && c.top_k <= 64;
+}
+
 moe_status stage_small_gateup(const moe_config& c, const Layout& L, void* ws, const void* x, const moe_weights& w,
-                              hipStream_t s) {
+                              hipStream_t s, const moe::SelParams* sel = nullptr,
+                              const moe::GateParams* gate = nullptr) {
     moe::GemmArgs a = small_args(c, L, ws, w, true);
     a.act = x;
     a.out = at<void>(ws, L.h);
+    if (sel) {
+        a.fused_sel = 1;
+        a.sel_logits = sel->logits;
+        a.sel_ksplit = sel->ksplit;
+        a.sel_ids = at<int32_t>(ws, L.ids);
+        a.sel_wts = at<float>(ws, L.wts);
+        a.sel_ids2 = sel->ids2;
+        a.sel_wts2 = sel->wts2;
+        if (gate && gate->w) {
+            a.gate_w = gate->w;
+            a.gate_x_f32 = gate->x_f32;
+            a.gate_out = gate->out;
+        }
+    }
     const int grid = (a.has_shared ? 1 : 0) + std::min(c.n_experts, c.n_tokens * c.top_k);
     HIP_TRY(moe::launch_gemm(moe::kSmallGateUp, wkind_of(c.expert_dtype), c.expert_dtype != MOE_F32, a, grid, 1, s));
     return MOE_OK;
@@ -502,15 +524,17 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
     const moe::SelParams P = sel_params(c, L, ws, weights->expert_bias, topk_ids_out, topk_weights_out);
 
     if (small_path(c)) {
-        // one stream: logits -> selection (+ shared gate logit) -> gate/up -> down -> combine
+        // one stream: logits -> selection (+ shared gate logit; inside the
+        // gate/up launch for T <= kFusedSelMaxT) -> gate/up -> down (+ combine)
         if (moe_status st = stage_logits(c, L, ws, x, weights->router, stream)) return st;
         moe::GateParams G{};
         if (has_shared && weights->shared_gate_vec) {
             G.x = x; G.w = weights->shared_gate_vec; G.D = c.d_model; G.x_f32 = c.act_dtype == MOE_F32;
             G.out = at<float>(ws, L.gate_logit);
         }
-        HIP_TRY(moe::launch_route_select_gate(P, G, ids, wts, stream));
-        if (moe_status st = stage_small_gateup(c, L, ws, x, *weights, stream)) return st;
+        const bool fuse = select_fused(c);
+        if (!fuse) HIP_TRY(moe::launch_route_select_gate(P, G, ids, wts, stream));
+        if (moe_status st = stage_small_gateup(c, L, ws, x, *weights, stream, fuse ? &P : nullptr, &G)) return st;
         if (down_combine_fused(c)) {
             moe::DownCombineArgs d{};
             d.h = at<void>(ws, L.h); d.h_ld = h_ld(c);

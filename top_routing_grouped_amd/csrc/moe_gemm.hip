@@ -26,6 +26,7 @@
 // fixed order.
 #include "moe_device.h"
 #include "moe_kernels.h"
+#include "moe_select.h"
 
 #include <type_traits>
 
@@ -157,7 +158,7 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_wave_barrier();
 }
 
-__device__ int small_tile(const GemmArgs& a, int item, int mt, int* rows_w, int* e_out) {
+__device__ int small_tile(const GemmArgs& a, const int32_t* ids, int item, int mt, int* rows_w, int* e_out) {
     __shared__ uint32_t pres_all[4][32];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (item < 0) {  // shared expert: tokens 16*mt + i
@@ -174,7 +175,7 @@ __device__ int small_tile(const GemmArgs& a, int item, int mt, int* rows_w, int*
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int p = lane + 64 * j;
-        int e = p < TK ? a.ids[p] : -1;
+        int e = p < TK ? ids[p] : -1;
         if (e < 0 || e >= a.n_experts) e = -1;
         idv[j] = e;
         if (e >= 0) atomicOr(&pres[e >> 5], 1u << (e & 31));
@@ -213,6 +214,46 @@ __device__ int small_tile(const GemmArgs& a, int item, int mt, int* rows_w, int*
     return max(0, min(16, base - 16 * mt));
 }
 
+// Softmax top-K selection of all T (<= kFusedSelMaxT) tokens inside a
+// small-T gate/up workgroup (the same selection code as the routing launch,
+// so the ids are identical): wave w takes tokens w and w + 4 into ids_l;
+// workgroup 0 also writes the routing outputs and the shared gate logits.
+// Ends with a workgroup barrier.
+__device__ void fused_select(const GemmArgs& a, int32_t* ids_l) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int T = a.n_tokens, K = a.topk;
+    SelParams P{};
+    P.logits = a.sel_logits;
+    P.ksplit = a.sel_ksplit;
+    P.T = T;
+    P.E = a.n_experts;
+    P.K = K;
+    const int tt[2] = {min(wave, T - 1), min(wave + 4, T - 1)};
+    int id[2];
+    float w[2];
+    select_softmax_lanes<4, 2>(P, tt, id, w);
+    const bool first = blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int t = wave + 4 * b;
+        if (t < T && lane < K) {
+            const int o = t * K + lane;
+            ids_l[o] = id[b];
+            if (first) {
+                a.sel_ids[o] = id[b];
+                a.sel_wts[o] = w[b];
+                if (a.sel_ids2) a.sel_ids2[o] = id[b];
+                if (a.sel_wts2) a.sel_wts2[o] = w[b];
+            }
+        }
+        if (first && a.gate_w && t < T) {
+            const float gl = wave_dot_row(a.act, a.gate_w, t, a.K, a.gate_x_f32 != 0);
+            if (lane == 0) a.gate_out[t] = gl;
+        }
+    }
+    __syncthreads();
+}
+
 // --------------------------------------------------------------- kernel
 // MODE: kRoutedGateUp | kRoutedDown | kDenseGateUp | kDenseDown | kDenseStore | kSmallGateUp | kSmallDown
 // WK: weight kind; OUTBF: output stored as bf16 (else fp32)
@@ -238,7 +279,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     const void *w0 = a.w0, *s0 = a.s0, *m0 = a.m0, *w1 = a.w1, *s1 = a.s1, *m1 = a.m1;
     if constexpr (SMALL) {
         const int item = int(blockIdx.x) - (a.has_shared ? 1 : 0);
-        count = uniform(small_tile(a, item, blockIdx.z, srows, &e));
+        const int32_t* ids = a.ids;
+        if constexpr (MODE == kSmallGateUp) {
+            __shared__ int32_t ids_l[kFusedSelMaxT * 64];
+            if (a.fused_sel) {
+                fused_select(a, ids_l);
+                ids = ids_l;
+            }
+        }
+        count = uniform(small_tile(a, ids, item, blockIdx.z, srows, &e));
         e = uniform(e);
         if (count <= 0) return;
         if (item < 0) {

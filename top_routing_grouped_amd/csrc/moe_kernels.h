@@ -51,7 +51,22 @@ struct GemmArgs {
     const float* gate_logit;  // [T] shared gate logits or null (s = 1)
     int sN, sK;               // shared item: output rows (gate/up) / reduction length (down)
     int act_ld, out_ld;       // row strides when they differ from K / N (0 = default)
+    // small-T gate/up with the softmax top-K selection folded in: every
+    // workgroup selects from the router's partial logits into LDS, and
+    // workgroup 0 writes the routing outputs and the shared gate logits
+    int fused_sel;
+    const float* sel_logits;  // [sel_ksplit][T][n_experts] partial logits
+    int sel_ksplit;
+    int32_t* sel_ids;         // [T*K] outputs (workspace)
+    float* sel_wts;
+    int32_t* sel_ids2;        // optional caller copies
+    float* sel_wts2;
+    const void* gate_w;       // shared gate vector [K] (null: no gate logits)
+    int gate_x_f32;
+    float* gate_out;          // [T]
 };
+// Largest T for which the small-T gate/up launch does the selection itself.
+constexpr int kFusedSelMaxT = 8;
 
 hipError_t launch_gemm(int mode, int wkind, bool outbf, const GemmArgs& a, int grid_x, int tf, hipStream_t s);
 // bf16 LDS-tiled variant; K % 64 == 0.  Routed modes: tiles of tiled_rows()
