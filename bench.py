@@ -357,6 +357,32 @@ def prefill_roofline(pre):
     return r
 
 
+def crossover(args):
+    """Direct (one work item per token-slot pair, each pair reading its
+    expert's weights) versus grouped (one work item per active expert)
+    execution of the routed gate/up stage at decode shape, on the same
+    routing.  Prints bytes the two would move without caches and their
+    measured launch times."""
+    for T in (1, 2, 4, 8, 16, 32):
+        spec = WORKLOADS["qwen_decode"].with_tokens(T)
+        insts = build_instances(spec, min(args.instances, 40), f"crossover T={T}")
+        for inst in insts:
+            inst.forward(None)
+        torch.cuda.synchronize()
+        grouped = time_stage(insts, moe.STAGE_GATE_UP, args.stage_reps)
+        direct = time_stage(insts, moe.STAGE_GATE_UP_DIRECT, args.stage_reps)
+        n_act = float(np.mean([inst.n_active() for inst in insts]))
+        wb = 2 * spec.d_model * spec.d_ff * BYTES_PER_PARAM[spec.expert_dtype]
+        line = {"study": "gate/up direct vs grouped", "n_tokens": T, "pairs": T * spec.top_k,
+                "n_active_mean": round(n_act, 2), "weight_bytes_grouped": round(n_act * wb),
+                "weight_bytes_direct_uncached": round(T * spec.top_k * wb),
+                "grouped_us": round(grouped * 1e3, 2), "direct_us": round(direct * 1e3, 2),
+                "direct_over_grouped": round(direct / grouped, 3)}
+        print(json.dumps(line), flush=True)
+        del insts
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,6 +395,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="profiling aid: finish with a 1 GiB device-to-device copy (known bytes for counter scaling)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="small-T study: routed gate/up with one work item per (token, slot) pair versus grouped "
+                         "by expert, T = 1..32 at decode shape; prints one JSON line per T")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="profiling aid: run one workload and print its log line only")
     args = ap.parse_args()
@@ -382,6 +411,9 @@ def main():
     torch.cuda.set_device(0)
     moe.lib()
 
+    if args.crossover:
+        crossover(args)
+        return
     if args.only == "prefill":
         run_workload("qwen_prefill_skew", 4096, min(args.instances, 4), args.steps, args.warmup, args.stage_reps)
         if args.copy_calibration:

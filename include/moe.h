@@ -191,7 +191,13 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
 typedef enum {
     MOE_STAGE_ROUTER_LOGITS = 0, /* router GEMM: x [T,D] -> fp32 logits in ws */
     MOE_STAGE_GATE_UP = 1,       /* routed gate/up GEMM + SwiGLU -> h in ws */
-    MOE_STAGE_DOWN = 2           /* routed down GEMM x alpha -> staged slot rows in ws */
+    MOE_STAGE_DOWN = 2,          /* routed down GEMM x alpha -> staged slot rows in ws */
+    MOE_STAGE_GATE_UP_DIRECT = 3 /* small T*K only (<= 256 pairs, fewer than 64 per expert):
+                                    the gate/up stage with every (token, slot) pair as its
+                                    own work item, no grouping by expert (Treebeard, "Intel
+                                    SYCL path": direct versus bucketed execution); writes
+                                    the same h as MOE_STAGE_GATE_UP.  MOE_ERR_UNSUPPORTED
+                                    otherwise. */
 } moe_stage;
 
 /* Measurement aid: re-launches one kernel stage of the last

@@ -241,3 +241,35 @@ def test_layer_deterministic_and_stream_independent(name, T):
         for u, v in zip(a, other):
             assert np.array_equal(u.view(np.uint32) if u.dtype == np.float32 else u,
                                   v.view(np.uint32) if v.dtype == np.float32 else v)
+
+
+# ------------------------------------------------------------------ direct vs grouped gate/up (measurement stage)
+@pytest.mark.parametrize("name,T", [("qwen_decode", 1), ("qwen_decode", 8), ("qwen_decode", 32), ("small_bf16", 37),
+                                    ("small_u4", 37), ("small_f32", 37)])
+def test_gate_up_direct_stage_matches_grouped(name, T):
+    """The (token, slot)-per-work-item gate/up stage writes the same h bits as
+    the grouped stage (an MFMA output column depends only on its own token)."""
+    case = _small(name, T) if name in SMALL else make_case(spec_of(name, n_tokens=T))
+    s = case.spec
+    cfg = moe.config_from_spec(s)
+    ws = moe.alloc_workspace(cfg)
+    wst = moe.weights_struct(case.w)
+    out = torch.empty_like(case.r)
+    moe.layer_forward(cfg, wst, case.x, case.r, out, None, None, ws)
+    torch.cuda.synchronize()
+    base = ws.clone()
+    moe.layer_stage(cfg, wst, case.x, moe.STAGE_GATE_UP, ws)
+    torch.cuda.synchronize()
+    grouped = ws.clone()
+    ws.copy_(base)
+    moe.layer_stage(cfg, wst, case.x, moe.STAGE_GATE_UP_DIRECT, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ws, grouped)
+
+
+def test_gate_up_direct_stage_rejects_large_t():
+    case = _small("small_bf16", 700)  # 2800 pairs over 32 experts: the grouped large-T path
+    cfg = moe.config_from_spec(case.spec)
+    ws = moe.alloc_workspace(cfg)
+    with pytest.raises(moe.MoeError):
+        moe.layer_stage(cfg, moe.weights_struct(case.w), case.x, moe.STAGE_GATE_UP_DIRECT, ws)

@@ -342,6 +342,20 @@ moe_status stage_small_gateup(const moe_config& c, const Layout& L, void* ws, co
     return MOE_OK;
 }
 
+// The same stage with one work item per (token, slot) pair (no grouping).
+moe_status stage_small_gateup_direct(const moe_config& c, const Layout& L, void* ws, const void* x,
+                                     const moe_weights& w, hipStream_t s) {
+    moe::GemmArgs a = small_args(c, L, ws, w, true);
+    a.act = x;
+    a.out = at<void>(ws, L.h);
+    a.direct_pairs = 1;
+    // the grouped launch's tile shape, so both compute each h element alike
+    a.shape_grid = (a.has_shared ? 1 : 0) + std::min(c.n_experts, c.n_tokens * c.top_k);
+    const int grid = (a.has_shared ? 1 : 0) + c.n_tokens * c.top_k;
+    HIP_TRY(moe::launch_gemm(moe::kSmallGateUp, wkind_of(c.expert_dtype), c.expert_dtype != MOE_F32, a, grid, 1, s));
+    return MOE_OK;
+}
+
 moe_status stage_small_down(const moe_config& c, const Layout& L, void* ws, const moe_weights& w, hipStream_t s) {
     moe::GemmArgs a = small_args(c, L, ws, w, false);
     a.act = at<void>(ws, L.h);
@@ -607,6 +621,9 @@ moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, co
         case MOE_STAGE_GATE_UP:
             if (small_path(c)) return stage_small_gateup(c, L, ws, x, *weights, stream);
             return stage_gateup(c, L, ws, x, *weights, pairs, tiles, nt, stream);
+        case MOE_STAGE_GATE_UP_DIRECT:
+            if (!small_path(c)) return fail(MOE_ERR_UNSUPPORTED, "the direct gate/up stage needs the small-T path");
+            return stage_small_gateup_direct(c, L, ws, x, *weights, stream);
         case MOE_STAGE_DOWN:
             if (small_path(c)) return stage_small_down(c, L, ws, *weights, stream);
             return stage_down(c, L, ws, *weights, pairs, tiles, nt, at<float>(ws, L.wts), at<void>(ws, L.slots),

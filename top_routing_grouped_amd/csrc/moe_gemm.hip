@@ -167,6 +167,15 @@ __device__ int small_tile(const GemmArgs& a, const int32_t* ids, int item, int m
         wave_lds_fence();
         return max(0, min(16, a.n_tokens - 16 * mt));
     }
+    if (a.direct_pairs) {  // item = one (token, slot) pair, no grouping
+        if (mt > 0 || item >= a.n_pairs) return 0;
+        const int e = ids[item];
+        if (e < 0 || e >= a.n_experts) return 0;
+        *e_out = e;
+        if (lane == 0) rows_w[0] = item;
+        wave_lds_fence();
+        return 1;
+    }
     uint32_t* pres = pres_all[wave];
     if (lane < 32) pres[lane] = 0;
     wave_lds_fence();
@@ -497,11 +506,13 @@ static hipError_t launch_cfg(const GemmArgs& a, int grid_x, int tf, hipStream_t 
     constexpr int SPAN = 4 * WTraits<WK>::KL;
     const bool ksplit4 = (kwg % (4 * SPAN) == 0);
     const bool ksplit2 = (kwg % (2 * SPAN) == 0);
-    if (SMALL && kwg % SPAN == 0) {
-        // small T: 64 weight rows per workgroup, no K split (measured at
-        // decode shapes: a quarter of the workgroups of 16-row, 4-way-K
-        // tiles, so all are resident at once and the per-workgroup routing
-        // decode runs a quarter as often)
+    const int shape_x = a.shape_grid > 0 ? a.shape_grid : grid_x;  // work items the tile shape is chosen for
+    if (SMALL && kwg % SPAN == 0 && (long long)shape_x * ((nrows + 63) / 64) >= 512) {
+        // small T with enough work items: 64 weight rows per workgroup, no K
+        // split (measured at T = 8: a quarter of the workgroups of 16-row,
+        // 4-way-K tiles, all resident at once, and the per-workgroup routing
+        // decode runs a quarter as often).  Fewer items (T <= 4) keep the
+        // 16-row tiles below: 64-row ones would leave ~1 workgroup per CU.
         dim3 g(grid_x, (nrows + 63) / 64, ks);
         gemm_kernel<MODE, WK, OUTBF, 1, 4, 1><<<g, 256, 0, s>>>(a);
     } else if (tf == 1 || SMALL) {

@@ -64,6 +64,8 @@ struct GemmArgs {
     const void* gate_w;       // shared gate vector [K] (null: no gate logits)
     int gate_x_f32;
     float* gate_out;          // [T]
+    int direct_pairs;         // small-T gate/up: one work item per (token, slot) pair
+    int shape_grid;           // small T: item count the tile shape is chosen for (0: grid_x)
 };
 // Largest T for which the small-T gate/up launch does the selection itself.
 constexpr int kFusedSelMaxT = 8;

@@ -30,7 +30,7 @@ _FAM = {"softmax": SOFTMAX_TOPK, "sigmoid_group": SIGMOID_GROUP_TOPK}
 # Entry points the header declares (checked by the CPU tests).
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_experts", "moe_shared_expert",
            "moe_combine", "moe_layer_forward", "moe_layer_stage", "moe_status_string", "moe_last_error")
-STAGE_ROUTER_LOGITS, STAGE_GATE_UP, STAGE_DOWN = 0, 1, 2
+STAGE_ROUTER_LOGITS, STAGE_GATE_UP, STAGE_DOWN, STAGE_GATE_UP_DIRECT = 0, 1, 2, 3
 
 
 class MoeConfig(ctypes.Structure):
