@@ -34,7 +34,14 @@ Readings where the pages are silent (each is also listed in the design doc):
     consecutive input elements, two codes per byte with the even element in
     the low nibble, scale and min in bf16;
   * the permuted pair order is stable (ascending flat pair id t*K + k inside
-    each expert).
+    each expert);
+  * RMS normalisation of the attention residual ([T] "Routing math": x is the
+    post-attention RMS-normalised hidden state; "Editable Mermaid flowchart"
+    and "Pseudocode": x = rms_norm(attention residual)) is
+    x = r / sqrt(mean_j r_j^2 + eps) * w, with eps inside the square root, an
+    optional per-feature weight w (absent: ones) applied after the division,
+    and x stored once in the activation type (bf16: round to nearest even from
+    the exact value) that every consumer of x reads.
 
 Pins: every function here is pinned by tests/test_oracle_pins.py against
 closed forms, hand-derived fixtures (tests/golden/), brute force on tiny
@@ -86,6 +93,72 @@ def widen(arr, dtype: str) -> np.ndarray:
     if dtype == "f64":
         return np.asarray(arr, dtype=np.float64)
     raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------- RMS normalisation
+def rms_norm(r: np.ndarray, weight: Optional[np.ndarray] = None, eps: float = 1e-6) -> np.ndarray:
+    """x_t = r_t / sqrt(mean_j r_t[j]^2 + eps), times weight if given ([T]
+    "Routing math": x_t is the RMS-normalised post-attention state;
+    "Pseudocode": x = rms_norm(attention residual)).  Rows are the last axis."""
+    r = np.asarray(r, dtype=np.float64)
+    ms = np.mean(r * r, axis=-1, keepdims=True)
+    x = r / np.sqrt(ms + eps)
+    if weight is not None:
+        x = x * np.asarray(weight, dtype=np.float64)
+    return x
+
+
+def _bf16_quantum(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values (8 significant bits, fp32's exponent range) at
+    the binade of v: 2^(E-7) for |v| in [2^E, 2^(E+1)), E >= -126; 2^-133 below."""
+    _, e = np.frexp(v)  # v = m 2^e, 0.5 <= |m| < 1, so E = e - 1
+    return np.ldexp(1.0, np.maximum(e, -125) - 8)
+
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value, ties to even, directly
+    from the exact value (no intermediate fp32 rounding).  Returns float64
+    holding bf16 values; magnitudes past the largest bf16 become inf."""
+    v = np.asarray(v, dtype=np.float64)
+    q = _bf16_quantum(v)
+    out = np.rint(v / q) * q  # v / q is exact (power-of-two scale); rint ties to even
+    big = np.abs(out) >= 2.0 ** 128
+    return np.where(big, np.copysign(np.inf, v), out)
+
+
+def bf16_bits(v: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) of float64 values that are bf16 values."""
+    v = np.asarray(v, dtype=np.float64)
+    f = v.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), v, equal_nan=True), "not bf16 values"
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_boundary_distance(v: np.ndarray) -> np.ndarray:
+    """Relative distance |v - m| / |v| from v to the nearest bf16 rounding
+    boundary m (a midpoint between adjacent bf16 values); inf for v = 0."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    q = _bf16_quantum(a)
+    n = np.floor(a / q)
+    d = np.abs(a - (n + 0.5) * q)  # the midpoint of the step holding a
+    # in the first step of a binade the boundary below is a quarter step down
+    # (the spacing below is half as large)
+    _, e = np.frexp(a)
+    binade_start = (n * q == np.ldexp(1.0, e - 1)) & (e - 1 > -126)
+    d = np.where(binade_start, np.minimum(d, a - (n * q - 0.25 * q)), d)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(a == 0, np.inf, d / a)
+
+
+def normed_activation(r: np.ndarray, weight: Optional[np.ndarray], eps: float, act_dtype: str) -> np.ndarray:
+    """x as the layer stores it: rms_norm rounded once to the activation type
+    ('bf16': round_bf16; 'f32': nearest fp32)."""
+    x = rms_norm(r, weight, eps)
+    if act_dtype == "bf16":
+        return round_bf16(x)
+    if act_dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    raise ValueError(act_dtype)
 
 
 # ---------------------------------------------------------------- routing

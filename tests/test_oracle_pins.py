@@ -326,3 +326,103 @@ def test_token_subset_and_given_ids_consistent():
     again = O.layer_forward(x, r, wr, banks, "softmax", 2, ids=full.route.ids)
     np.testing.assert_allclose(again.out, full.out, rtol=0, atol=1e-14)
     np.testing.assert_allclose(O.softmax_weights_for(full.z, full.route.ids), full.route.weights, rtol=1e-15)
+
+
+# ------------------------------------------------------------- RMS normalisation
+def _ev_pow(expr):
+    """Fixture expression with ** allowed (hand-derived numbers only)."""
+    if isinstance(expr, (int, float)):
+        return float(expr)
+    assert set(expr) <= set("0123456789.+-*/() "), expr
+    return float(eval(expr, {"__builtins__": {}}, {}))  # noqa: S307 - restricted alphabet
+
+
+def test_golden_rms_norm_by_hand():
+    g = _load("rms_norm_hand.json")
+    for c in g["cases"]:
+        w = None if c["weight"] is None else np.array(c["weight"], dtype=np.float64)
+        got = O.rms_norm(np.array(c["r"], dtype=np.float64), w, c["eps"])
+        want = np.vectorize(_ev_pow, otypes=[np.float64])(np.array(c["x"], dtype=object))
+        np.testing.assert_allclose(got, want, rtol=1e-15, atol=1e-15, err_msg=c["derivation"])
+
+
+def test_golden_bf16_rounding_by_hand():
+    g = _load("rms_norm_hand.json")
+    for c in g["bf16_cases"]:
+        v = np.array([_ev_pow(c["v"])])
+        with np.errstate(over="ignore"):
+            bits = O.bf16_bits(O.round_bf16(v))[0]
+        assert bits == int(c["bits"], 16), (c["v"], hex(bits), c["why"])
+
+
+@pytest.mark.parametrize("alpha", [1e-3, 0.37, 7.5, 1e4])
+def test_rms_norm_scale_invariance(alpha):
+    """rms_norm(alpha r; alpha^2 eps) = rms_norm(r; eps) for alpha > 0: the
+    mean square scales by alpha^2 and eps sits inside the square root with it."""
+    rng = np.random.default_rng(5)
+    r = rng.standard_normal((6, 96)) * rng.uniform(0.1, 30, (6, 1))
+    w = rng.standard_normal(96)
+    for eps in (0.0, 1e-6, 0.5):
+        np.testing.assert_allclose(O.rms_norm(alpha * r, w, eps * alpha ** 2), O.rms_norm(r, w, eps),
+                                   rtol=1e-12, atol=1e-14)
+
+
+def test_rms_norm_mean_square_closed_form():
+    """Unit weight: mean(x^2) = ms / (ms + eps); a weight multiplies afterwards."""
+    rng = np.random.default_rng(6)
+    r = rng.standard_normal((5, 64)) * 3
+    ms = (r * r).mean(axis=1)
+    for eps in (0.0, 1e-6, 2.0):
+        x = O.rms_norm(r, None, eps)
+        np.testing.assert_allclose((x * x).mean(axis=1), ms / (ms + eps), rtol=1e-13)
+        assert np.all(np.sign(x) == np.sign(r))
+    w = rng.uniform(0.5, 2.0, 64)
+    np.testing.assert_allclose(O.rms_norm(r, w, 1e-6) / w, O.rms_norm(r, None, 1e-6), rtol=1e-14)
+
+
+def test_round_bf16_matches_library_on_fp32_values():
+    """For values that are fp32 numbers, rounding to bf16 is what torch's
+    float32 -> bfloat16 conversion (round to nearest even) gives."""
+    rng = np.random.default_rng(7)
+    m = rng.uniform(-2, 2, 20000)
+    ex = rng.integers(-140, 120, 20000)
+    v32 = np.ldexp(m, ex).astype(np.float32)
+    # exact ties: a bf16 value plus half its spacing (even and odd neighbours)
+    base = rng.integers(0x0080, 0x7F00, 4000, dtype=np.uint32) << np.uint32(16)
+    ties = (base | np.uint32(0x8000)).view(np.float32)
+    v32 = np.concatenate([v32, ties, -ties, np.float32([0.0, 1.0, -1.0])])
+    lib = torch.from_numpy(v32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ours = O.bf16_bits(O.round_bf16(v32.astype(np.float64)))
+    assert np.array_equal(ours, lib)
+
+
+def test_round_bf16_rounds_once_from_the_exact_value():
+    """A value just above a tie rounds up even when its fp32 rounding would land
+    on the tie (rounding via fp32 first would give the even neighbour)."""
+    v = np.array([1 + 2.0 ** -8 + 2.0 ** -30, -(3 + 2.0 ** -7 + 2.0 ** -30)])
+    assert np.array_equal(v.astype(np.float32).astype(np.float64), [1 + 2.0 ** -8, -(3 + 2.0 ** -7)])
+    np.testing.assert_array_equal(O.round_bf16(v), [1 + 2.0 ** -7, -(3 + 2.0 ** -6)])
+
+
+def test_bf16_boundary_distance_brackets_the_rounding_switch():
+    """Inside the returned distance every value rounds alike; just past it the
+    rounding changes (so the distance is that of the nearest boundary)."""
+    rng = np.random.default_rng(8)
+    v = np.ldexp(rng.uniform(0.5, 1.0, 5000), rng.integers(-20, 20, 5000)) * rng.choice([-1.0, 1.0], 5000)
+    d = O.bf16_boundary_distance(v)
+    inside_lo, inside_hi = O.round_bf16(v * (1 - 0.99 * d)), O.round_bf16(v * (1 + 0.99 * d))
+    assert np.array_equal(inside_lo, inside_hi)
+    outside_lo, outside_hi = O.round_bf16(v * (1 - 1.01 * d)), O.round_bf16(v * (1 + 1.01 * d))
+    assert np.all(outside_lo != outside_hi)
+    np.testing.assert_array_equal(O.bf16_boundary_distance(np.array([1.0, 1.5, 1 - 2.0 ** -9, 0.0])),
+                                  [2.0 ** -9, 2.0 ** -8 / 1.5, 0.0, np.inf])
+
+
+def test_normed_activation_rounds_once_per_dtype():
+    rng = np.random.default_rng(9)
+    r = rng.standard_normal((3, 128)) * 5
+    x = O.rms_norm(r, None, 1e-6)
+    np.testing.assert_array_equal(O.normed_activation(r, None, 1e-6, "f32"), x.astype(np.float32).astype(np.float64))
+    b = O.normed_activation(r, None, 1e-6, "bf16")
+    assert np.all(np.abs(b - x) <= 2.0 ** -8 * np.abs(x))
+    O.bf16_bits(b)  # every element is a bf16 value
