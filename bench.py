@@ -33,13 +33,14 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from synth import WORKLOADS, make_tokens, make_weights  # noqa: E402
+from synth import WORKLOADS, make_attention_residual, make_tokens, make_weights  # noqa: E402
 from top_routing_grouped_amd import moe  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "MoE layer tokens/s, Qwen3.6 shape at T=8 and T=4096; % of HBM / MFMA roofline"
 BYTES_PER_PARAM = {"f32": 4.0, "bf16": 2.0, "u4": 0.5 + 4.0 / 64}
+NORM_EPS = 1e-6  # RMS-norm epsilon of the chained layers (the pages give none)
 
 
 def log(*a):
@@ -338,6 +339,114 @@ def run_workload(name, T, L, steps, warmup, stage_reps):
     return res
 
 
+def time_chain(spec, L, steps, warmup):
+    """A stack of L distinct layers at one token count, each starting from the
+    attention residual: layer l normalises r_l (its own RMS-norm weight) and
+    writes r_(l+1) = r_l + y_moe, which layer l+1 reads.  One workspace serves
+    every layer (calls are ordered on one stream).  Captured as one graph;
+    returns us per layer (mean over the timed replays) and the median replay."""
+    t0 = time.time()
+    base = make_weights(spec, "cuda")
+    ws_list = [base] + [clone_weights(base) for _ in range(L - 1)]
+    structs = [moe.weights_struct(w) for w in ws_list]
+    r0, _ = make_attention_residual(spec, "cuda")
+    gammas = [make_attention_residual(spec.with_tokens(1), "cuda", weight_seed=1000 * spec.workload_id + 999 + l)[1]
+              for l in range(L)]
+    bufs = [r0] + [torch.empty_like(r0) for _ in range(L)]
+    cfg = moe.config_from_spec(spec)
+    wsp = moe.alloc_workspace(cfg)
+
+    def run():
+        for l in range(L):
+            moe.layer_forward_norm(cfg, structs[l], gammas[l], NORM_EPS, bufs[l], bufs[l + 1], ws=wsp)
+
+    run()
+    torch.cuda.synchronize()
+    ref = bufs[L].clone()
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        run()
+    for _ in range(2):
+        bufs[L].fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(bufs[L].view(torch.int32), ref.view(torch.int32)):
+            raise RuntimeError("chained graph replay differs from the eager chain")
+    log(f"chain of {L} layers (T={spec.n_tokens}) built in {time.time() - t0:.1f}s")
+    for _ in range(max(1, warmup // L)):
+        g.replay()
+    torch.cuda.synchronize()
+    n = max(1, steps // L)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    evs[0].record()
+    for i in range(n):
+        g.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) / L for i in range(n))
+    total = evs[0].elapsed_time(evs[-1]) / (n * L)
+    del g, ws_list, structs, bufs
+    torch.cuda.empty_cache()
+    return total * 1e3, per[len(per) // 2] * 1e3
+
+
+def norm_bytes(spec):
+    """Algorithmic bytes of one RMS-norm launch: the fp32 residual read, x
+    written in the activation type, the fp32 weight read."""
+    T, D = spec.n_tokens, spec.d_model
+    return T * D * 4 + T * D * (4 if spec.act_dtype == "f32" else 2) + D * 4
+
+
+def time_norm(spec, reps, rotate_bytes=384 << 20):
+    """Average duration of one moe_rms_norm launch (captured graph of `reps`
+    launches over enough distinct residual buffers to exceed the last-level
+    cache), HIP events on the replay stream."""
+    r, w = make_attention_residual(spec, "cuda")
+    nbuf = max(1, min(reps, -(-rotate_bytes // r.numel() // 4)))
+    rs = [r] + [r * (1.0 + 1e-3 * i) for i in range(1, nbuf)]
+    x = torch.empty(r.shape, device="cuda", dtype=torch.float32 if spec.act_dtype == "f32" else torch.bfloat16)
+    cfg = moe.config_from_spec(spec)
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for i in range(reps):
+            moe.rms_norm(cfg, rs[i % nbuf], w, NORM_EPS, x)
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    del rs, g
+    torch.cuda.empty_cache()
+    gbs = norm_bytes(spec) / (ms / 1e3) / 1e9
+    return {"kernel": "RMS norm of the attention residual", "n_tokens": spec.n_tokens, "launch_us": round(ms * 1e3, 2),
+            "algorithmic_bytes": norm_bytes(spec), "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
+
+
+def chained_decode(args, dec_us):
+    """Entry for the 40-layer chain at decode shape with the normalisation in
+    each layer, beside the RMS-norm launch measured alone (T = 8 and 4096)."""
+    spec = WORKLOADS["qwen_decode"].with_tokens(8)
+    L = args.instances
+    us, us_med = time_chain(spec, L, args.steps, args.warmup)
+    n8 = time_norm(spec, args.stage_reps)
+    n4k = time_norm(WORKLOADS["qwen_prefill_skew"].with_tokens(4096), max(8, args.stage_reps // 4))
+    log(f"chain: {us:.1f} us/layer (median replay {us_med:.1f}) with the norm; independent layers {dec_us:.1f}; "
+        f"norm alone {n8['launch_us']:.1f} us at T=8, {n4k['launch_us']:.1f} us = {n4k['achieved']:,.0f} GB/s "
+        f"at T=4096")
+    return {"workload": f"{L} chained Qwen3.6-35B-A3B MoE layers at T=8: each normalises the attention residual "
+                        f"(RMS norm, eps {NORM_EPS:g}, per-layer weight) and feeds r + y_moe to the next",
+            "layers": L, "us_per_layer": round(us, 2), "median_replay_us_per_layer": round(us_med, 2),
+            "tokens_per_s": round(8 / (us * 1e-6), 1),
+            "independent_layers_us_per_layer": round(dec_us, 2),
+            "norm_T8": n8, "norm_T4096": n4k}
+
+
 def prefill_roofline(pre):
     """Roofline of the prefill gate/up launch, bound chosen by its algorithmic
     intensity against the chip's ridge point (bf16 MFMA peak / HBM peak)."""
@@ -398,7 +507,8 @@ def main():
     ap.add_argument("--crossover", action="store_true",
                     help="small-T study: routed gate/up with one work item per (token, slot) pair versus grouped "
                          "by expert, T = 1..32 at decode shape; prints one JSON line per T")
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+    ap.add_argument("--no-chain", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill", "chain"], default=None,
                     help="profiling aid: run one workload and print its log line only")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -413,6 +523,9 @@ def main():
 
     if args.crossover:
         crossover(args)
+        return
+    if args.only == "chain":
+        chained_decode(args, float("nan"))
         return
     if args.only == "prefill":
         run_workload("qwen_prefill_skew", 4096, min(args.instances, 4), args.steps, args.warmup, args.stage_reps)
@@ -457,6 +570,8 @@ def main():
                      "traffic": gu_traffic, "launch_us": round(dec["gateup_ms"] * 1e3, 3),
                      "algorithmic_bytes": round(dec["gateup_bytes"])},
     }
+    if not args.no_chain:
+        line["chained_decode"] = chained_decode(args, dec["ms_per_step"] * 1e3)
     if not args.no_prefill:
         pre = run_workload("qwen_prefill_skew", 4096, 4, max(80, args.steps // 10), max(20, args.warmup // 10),
                            max(8, args.stage_reps // 4))

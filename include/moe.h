@@ -187,6 +187,32 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
                              float* topk_weights_out, void* ws, size_t ws_bytes,
                              moe_stream_t stream, moe_stream_t aux_stream);
 
+/* RMS normalisation of the attention residual (Treebeard "Routing math": x_t
+ * is the post-attention, RMS-normalised hidden state; "Editable Mermaid
+ * flowchart" and "Pseudocode": x = rms_norm(attention residual) before the
+ * router).  The pages fix neither an epsilon nor a weight; this library computes
+ *   x[t, j] = residual[t, j] / sqrt(mean_j residual[t, j]^2 + eps) * norm_weight[j]
+ * residual [T, D] fp32; norm_weight [D] fp32, or NULL for ones; x [T, D]
+ * act_dtype, written once (bf16: rounded to nearest even from the fp32
+ * value).  The row's sum of squares is accumulated in fp32 in a fixed order.
+ * eps must be finite and > 0.  residual, norm_weight and x must be 16-byte
+ * aligned and x must not overlap residual.  Reads n_tokens, d_model and
+ * act_dtype of cfg. */
+moe_status moe_rms_norm(const moe_config* cfg, const float* residual, const float* norm_weight, float eps,
+                        void* x, moe_stream_t stream);
+
+/* The layer from the attention residual: x = moe_rms_norm(residual), then
+ * moe_layer_forward(x, residual) (Treebeard "Pseudocode": the layer function
+ * starts from the attention residual and returns residual + routed + shared).
+ * x_out [T, D] act_dtype receives x when non-NULL (it must not overlap
+ * residual or out); otherwise x is kept in ws.  Outputs, aliasing of out and
+ * residual, and schedules are those of moe_layer_forward; the normalisation
+ * runs first, on `stream`. */
+moe_status moe_layer_forward_norm(const moe_config* cfg, const moe_weights* weights, const float* norm_weight,
+                                  float eps, const float* residual, void* x_out, float* out,
+                                  int32_t* topk_ids_out, float* topk_weights_out, void* ws, size_t ws_bytes,
+                                  moe_stream_t stream, moe_stream_t aux_stream);
+
 /* Stages of moe_layer_forward that moe_layer_stage can re-launch. */
 typedef enum {
     MOE_STAGE_ROUTER_LOGITS = 0, /* router GEMM: x [T,D] -> fp32 logits in ws */

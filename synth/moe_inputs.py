@@ -37,6 +37,12 @@ the same seed on the same device type gives the same tensor):
     router's last column receives a per-expert offset b_e ~ N(0, var 1.5), so
     b_e acts as a logit-space offset (load skew, some experts idle).
   * residual ~ N(0,1) float32.
+  * attention residual for the entry that normalises it (make_attention_residual):
+    r_t = s_t g_t with g_t drawn as for the hidden state above (N(0,1); last
+    column 1 in the skewed workload) and s_t = 4 exp(N(0,1)) a per-token
+    magnitude (rows of very different scale); token seed 1000 * id + T + 500.
+    RMS-norm weight 1 + 0.1 N(0,1) float32, seed 1000 * id + 999 (+ a layer
+    index for chained layers).
   * sigmoid-group workload: expert_bias ~ N(0, var 0.1) float32.
 """
 from __future__ import annotations
@@ -236,3 +242,20 @@ def make_tokens(spec: LayerSpec, device="cpu", seed: Optional[int] = None):
     r = torch.randn((T, D), generator=gen, device=device, dtype=torch.float32)
     return x, r
 
+
+
+def make_attention_residual(spec: LayerSpec, device="cpu", seed: Optional[int] = None,
+                            weight_seed: Optional[int] = None):
+    """Draw an attention residual r [T, D] float32 and an RMS-norm weight [D]
+    float32 (the inputs of the layer entry that normalises r itself)."""
+    T, D = spec.n_tokens, spec.d_model
+    seed = 1000 * spec.workload_id + T + 500 if seed is None else seed
+    gen = _gen(seed, device)
+    g = torch.randn((T, D), generator=gen, device=device, dtype=torch.float32)
+    if spec.skew_var > 0:
+        g[:, D - 1] = 1.0
+    mag = 4.0 * torch.exp(torch.randn((T, 1), generator=gen, device=device, dtype=torch.float32))
+    r = (g * mag).contiguous()
+    wgen = _gen(1000 * spec.workload_id + 999 if weight_seed is None else weight_seed, device)
+    w = (1.0 + 0.1 * torch.randn((D,), generator=wgen, device=device, dtype=torch.float32)).contiguous()
+    return r, w

@@ -92,19 +92,19 @@ def _valid_topk(score, chosen, k, cand=None, eps=O.TIE_EPS):
     return all(score[e] >= kth - eps for e in chosen) and all(score[e] <= nxt + eps for e in rest)
 
 
-def valid_selection(spec: LayerSpec, z_row: np.ndarray, bias, chosen) -> bool:
-    """Whether a selection is one of the near-tied valid answers for a flagged token."""
+def valid_selection(spec: LayerSpec, z_row: np.ndarray, bias, chosen, eps: float = O.TIE_EPS) -> bool:
+    """Whether a selection is one of the near-tied valid answers (scores within eps) for a flagged token."""
     if spec.family == "softmax":
-        return _valid_topk(O.softmax(z_row[None])[0], list(chosen), spec.top_k)
+        return _valid_topk(O.softmax(z_row[None])[0], list(chosen), spec.top_k, eps=eps)
     E, G, TG = spec.n_experts, spec.n_group, spec.topk_group
     gs = E // G
     sel = O.sigmoid(z_row) + (0 if bias is None else bias)
     gsc = O.group_scores(sel[None], G)[0]
     for S in itertools.combinations(range(G), TG):
-        if not _valid_topk(gsc, list(S), TG):
+        if not _valid_topk(gsc, list(S), TG, eps=eps):
             continue
         cand = [e for g in S for e in range(g * gs, (g + 1) * gs)]
-        if _valid_topk(sel, list(chosen), spec.top_k, cand):
+        if _valid_topk(sel, list(chosen), spec.top_k, cand, eps=eps):
             return True
     return False
 

@@ -131,6 +131,36 @@ def test_null_and_workspace_errors_without_launch():
     assert L.moe_combine(None, fake, None, fake, fake, None) == moe.MOE_ERR_INVALID_ARGUMENT
 
 
+def test_rms_norm_argument_errors_without_launch():
+    L = moe.lib()
+    cfg = _cfg(n_tokens=8)
+    fake, fake2 = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 24)  # never dereferenced
+    E = moe.MOE_ERR_INVALID_ARGUMENT
+    for eps in (0.0, -1e-6, float("inf"), float("nan")):
+        assert L.moe_rms_norm(ctypes.byref(cfg), fake, None, eps, fake2, None) == E
+    assert L.moe_rms_norm(ctypes.byref(cfg), None, None, 1e-6, fake2, None) == E
+    assert L.moe_rms_norm(ctypes.byref(cfg), fake, None, 1e-6, None, None) == E
+    assert L.moe_rms_norm(ctypes.byref(cfg), ctypes.c_void_p((1 << 20) + 8), None, 1e-6, fake2, None) == E
+    assert L.moe_rms_norm(ctypes.byref(cfg), fake, ctypes.c_void_p(4100), 1e-6, fake2, None) == E
+    # x overlapping the residual rows
+    assert L.moe_rms_norm(ctypes.byref(cfg), fake, None, 1e-6, ctypes.c_void_p((1 << 20) + 256), None) == E
+    assert L.moe_rms_norm(None, fake, None, 1e-6, fake2, None) == E
+    # the layer entry: bad eps, missing residual, x_out overlapping out
+    need = moe.workspace_size(cfg)
+    w = moe.MoeWeights(4096, None, moe.MoeMatrix(4096, None, None), moe.MoeMatrix(4096, None, None),
+                       moe.MoeMatrix(4096, None, None), moe.MoeMatrix(4096, None, None),
+                       moe.MoeMatrix(4096, None, None), moe.MoeMatrix(4096, None, None))
+    ws = ctypes.c_void_p(1 << 28)
+    def call(eps=1e-6, residual=fake, x_out=None, out=fake2):
+        return L.moe_layer_forward_norm(ctypes.byref(cfg), ctypes.byref(w), None, eps, residual, x_out, out,
+                                        None, None, ws, need, None, None)
+    assert call(eps=0.0) == E
+    assert call(residual=None) == E
+    assert call(x_out=ctypes.c_void_p((1 << 24) + 64)) == E
+    assert L.moe_layer_forward_norm(ctypes.byref(cfg), ctypes.byref(w), None, 1e-6, fake, None, fake2, None, None,
+                                    ws, 16, None, None) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_zero_tokens_is_ok_without_launch():
     L = moe.lib()
     cfg = _cfg(n_tokens=0)
@@ -140,6 +170,9 @@ def test_zero_tokens_is_ok_without_launch():
     assert L.moe_combine(ctypes.byref(cfg), None, None, None, None, None) == moe.MOE_OK
     assert L.moe_layer_forward(ctypes.byref(cfg), ctypes.byref(w), None, None, None, None, None, None, 0,
                                None, None) == moe.MOE_OK
+    assert L.moe_rms_norm(ctypes.byref(cfg), None, None, 1e-6, None, None) == moe.MOE_OK
+    assert L.moe_layer_forward_norm(ctypes.byref(cfg), ctypes.byref(w), None, 1e-6, None, None, None, None, None,
+                                    None, 0, None, None) == moe.MOE_OK
 
 
 def test_status_strings():

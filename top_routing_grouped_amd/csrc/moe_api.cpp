@@ -88,7 +88,8 @@ int64_t max_tiles(int64_t n_pairs, int E, int tile_rows) {
 }
 
 struct Layout {
-    size_t chunk_base, logits, gate_logit, ids, wts, offsets, active, n_active, n_tiles, pairs, tiles, h, slots, hs, ys, total;
+    size_t chunk_base, logits, gate_logit, ids, wts, offsets, active, n_active, n_tiles, pairs, tiles, h, slots, hs, ys, xn,
+        total;
 };
 
 Layout layout(const moe_config& c) {
@@ -119,6 +120,7 @@ Layout layout(const moe_config& c) {
     L.slots = take(std::max(TK * D, T * (K + 1) * D) * hb);
     L.hs = take(T * Fs * hb);
     L.ys = take(T * D * 4);
+    L.xn = take(T * D * (c.act_dtype == MOE_F32 ? 4 : 2));  // normalised x (moe_layer_forward_norm)
     L.total = o;
     return L;
 }
@@ -191,15 +193,35 @@ moe::GemmArgs gemm_args(const moe_matrix& m0, const moe_matrix* m1, int N, int K
 template <class T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
+// RMS norm of the attention residual folded into the router-logits launch:
+// small T with bf16 activations (16-token tiles; the launch converts the
+// residual rows it reads and writes x for the later launches).
+struct NormFold {
+    const float* residual;
+    const float* w;
+    float eps;
+    void* x;
+};
+bool norm_fusable(const moe_config& c) {
+    return small_path(c) && c.act_dtype == MOE_BF16 && c.router_dtype == MOE_BF16 &&
+           !dense_tiled(c, c.router_dtype) && dense_tf(c) == 1;
+}
+
 // ---- stages (arguments already validated)
 moe_status stage_logits(const moe_config& c, const Layout& L, void* ws, const void* x, const void* router,
-                        hipStream_t s) {
+                        hipStream_t s, const NormFold* nf = nullptr) {
     const int T = c.n_tokens;
     moe_matrix rm{router, nullptr, nullptr};
     moe::GemmArgs a = gemm_args(rm, nullptr, c.n_experts, c.d_model, 1);
     a.act = x; a.n_act_rows = T; a.n_rows = T;
     a.out = at<float>(ws, L.logits);
     a.ksplit = router_ksplit(c);
+    if (nf) {
+        a.act = nf->residual;
+        a.norm_w = nf->w; a.norm_eps = nf->eps; a.norm_x = nf->x;
+        HIP_TRY(moe::launch_gemm(moe::kDenseStoreNorm, moe::kWBF16, false, a, (T + 15) / 16, 1, s));
+        return MOE_OK;
+    }
     if (dense_tiled(c, c.router_dtype)) {
         HIP_TRY(moe::launch_gemm_tiled(moe::kDenseStore, false, a, (T + moe::tiled_rows_dense() - 1) / moe::tiled_rows_dense(), s));
         return MOE_OK;
@@ -416,6 +438,100 @@ moe_status fork_join_events(hipEvent_t* fork, hipEvent_t* join) {
     return MOE_OK;
 }
 
+
+// x [T, D] act_dtype against a [T, D] fp32 tensor
+bool overlaps(const void* x, const moe_config& c, const float* t) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(t);
+    const size_t n = size_t(c.n_tokens) * c.d_model;
+    const size_t xa = n * (c.act_dtype == MOE_F32 ? 4 : 2), tb = n * 4;
+    return a < b + tb && b < a + xa;
+}
+
+moe_status check_norm(const moe_config& c, const float* residual, const float* w, float eps, const void* x) {
+    if (!(std::isfinite(eps) && eps > 0.f)) return fail(MOE_ERR_INVALID_ARGUMENT, "eps must be finite and > 0");
+    if (!residual || !x) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL tensor argument");
+    auto mis = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; };
+    if (mis(residual) || mis(x) || (w && mis(w)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "residual, norm_weight and x must be 16-byte aligned");
+    if (overlaps(x, c, residual)) return fail(MOE_ERR_INVALID_ARGUMENT, "x overlaps residual");
+    return MOE_OK;
+}
+
+moe_status layer_forward_impl(const moe_config& c, const moe_weights* weights, const void* x, const float* residual,
+                              float* out, int32_t* topk_ids_out, float* topk_weights_out, void* ws,
+                              hipStream_t stream, hipStream_t aux_stream, const NormFold* nf = nullptr) {
+    const Layout L = layout(c);
+    const bool has_shared = c.d_ff_shared > 0;
+    const bool slot_bf16 = c.expert_dtype != MOE_F32;
+    int32_t* ids = at<int32_t>(ws, L.ids);
+    float* wts = at<float>(ws, L.wts);
+    const moe::SelParams P = sel_params(c, L, ws, weights->expert_bias, topk_ids_out, topk_weights_out);
+
+    if (small_path(c)) {
+        // one stream: logits -> selection (+ shared gate logit; inside the
+        // gate/up launch for T <= kFusedSelMaxT) -> gate/up -> down (+ combine)
+        if (moe_status st = stage_logits(c, L, ws, x, weights->router, stream, nf)) return st;
+        moe::GateParams G{};
+        if (has_shared && weights->shared_gate_vec) {
+            G.x = x; G.w = weights->shared_gate_vec; G.D = c.d_model; G.x_f32 = c.act_dtype == MOE_F32;
+            G.out = at<float>(ws, L.gate_logit);
+        }
+        const bool fuse = select_fused(c);
+        if (!fuse) HIP_TRY(moe::launch_route_select_gate(P, G, ids, wts, stream));
+        if (moe_status st = stage_small_gateup(c, L, ws, x, *weights, stream, fuse ? &P : nullptr, &G)) return st;
+        if (down_combine_fused(c)) {
+            moe::DownCombineArgs d{};
+            d.h = at<void>(ws, L.h); d.h_ld = h_ld(c);
+            d.ids = ids; d.wts = wts;
+            d.w = weights->down.w; d.ws = has_shared ? weights->shared_down.w : nullptr;
+            d.gate_logit = has_shared && weights->shared_gate_vec ? at<float>(ws, L.gate_logit) : nullptr;
+            d.residual = residual; d.out = out;
+            d.T = c.n_tokens; d.K = c.top_k; d.E = c.n_experts; d.D = c.d_model; d.F = c.d_ff;
+            d.has_shared = has_shared ? 1 : 0;
+            HIP_TRY(moe::launch_down_combine(d, stream));
+            return MOE_OK;
+        }
+        if (moe_status st = stage_small_down(c, L, ws, *weights, stream)) return st;
+        HIP_TRY(moe::launch_combine(at<void>(ws, L.slots), slot_bf16, nullptr, residual, out, c.n_tokens,
+                                    c.top_k + (has_shared ? 1 : 0), c.d_model, stream));
+        return MOE_OK;
+    }
+
+    float* ys = has_shared ? at<float>(ws, L.ys) : nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    const bool fork = has_shared && aux_stream && aux_stream != stream;
+    if (fork) {
+        if (moe_status st = fork_join_events(&ev_fork, &ev_join)) return st;
+        HIP_TRY(hipEventRecord(ev_fork, stream));
+        HIP_TRY(hipStreamWaitEvent(aux_stream, ev_fork, 0));
+        if (moe_status st = stage_shared(c, L, ws, x, *weights, ys, aux_stream)) return st;
+        HIP_TRY(hipEventRecord(ev_join, aux_stream));
+    } else if (has_shared) {
+        if (moe_status st = stage_shared(c, L, ws, x, *weights, ys, stream)) return st;
+    }
+
+    const int tile_rows = routed_tile_rows(c);
+    int32_t* pairs = at<int32_t>(ws, L.pairs);
+    int4* tiles = at<int4>(ws, L.tiles);
+    int32_t* nt = at<int32_t>(ws, L.n_tiles);
+    const moe::PermParams Q = perm_params(c, ids, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.active),
+                                          at<int32_t>(ws, L.n_active), pairs, tiles, nt, tile_rows,
+                                          at<int32_t>(ws, L.chunk_base));
+    if (moe_status st = stage_logits(c, L, ws, x, weights->router, stream)) return st;
+    if (moe::route_permute_fusable(c.n_tokens, c.n_experts, c.top_k)) {
+        HIP_TRY(moe::launch_route_permute(P, ids, wts, Q, stream));
+    } else {
+        HIP_TRY(moe::launch_route_select(P, ids, wts, stream));
+        HIP_TRY(moe::launch_permute(Q, stream));
+    }
+    void* slots = at<void>(ws, L.slots);
+    if (moe_status st = stage_experts(c, L, ws, x, *weights, pairs, tiles, nt, wts, slots, slot_bf16, stream))
+        return st;
+    if (fork) HIP_TRY(hipStreamWaitEvent(stream, ev_join, 0));
+    HIP_TRY(moe::launch_combine(slots, slot_bf16, ys, residual, out, c.n_tokens, c.top_k, c.d_model, stream));
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -529,77 +645,44 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
     if (moe_status st = check_weights(*cfg, weights, true, true)) return st;
     if (moe_status st = check_ws(*cfg, ws, ws_bytes)) return st;
     (void)hipGetLastError();
-    const moe_config& c = *cfg;
-    const Layout L = layout(c);
-    const bool has_shared = c.d_ff_shared > 0;
-    const bool slot_bf16 = c.expert_dtype != MOE_F32;
-    int32_t* ids = at<int32_t>(ws, L.ids);
-    float* wts = at<float>(ws, L.wts);
-    const moe::SelParams P = sel_params(c, L, ws, weights->expert_bias, topk_ids_out, topk_weights_out);
+    return layer_forward_impl(*cfg, weights, x, residual, out, topk_ids_out, topk_weights_out, ws, stream, aux_stream);
+}
 
-    if (small_path(c)) {
-        // one stream: logits -> selection (+ shared gate logit; inside the
-        // gate/up launch for T <= kFusedSelMaxT) -> gate/up -> down (+ combine)
-        if (moe_status st = stage_logits(c, L, ws, x, weights->router, stream)) return st;
-        moe::GateParams G{};
-        if (has_shared && weights->shared_gate_vec) {
-            G.x = x; G.w = weights->shared_gate_vec; G.D = c.d_model; G.x_f32 = c.act_dtype == MOE_F32;
-            G.out = at<float>(ws, L.gate_logit);
-        }
-        const bool fuse = select_fused(c);
-        if (!fuse) HIP_TRY(moe::launch_route_select_gate(P, G, ids, wts, stream));
-        if (moe_status st = stage_small_gateup(c, L, ws, x, *weights, stream, fuse ? &P : nullptr, &G)) return st;
-        if (down_combine_fused(c)) {
-            moe::DownCombineArgs d{};
-            d.h = at<void>(ws, L.h); d.h_ld = h_ld(c);
-            d.ids = ids; d.wts = wts;
-            d.w = weights->down.w; d.ws = has_shared ? weights->shared_down.w : nullptr;
-            d.gate_logit = has_shared && weights->shared_gate_vec ? at<float>(ws, L.gate_logit) : nullptr;
-            d.residual = residual; d.out = out;
-            d.T = c.n_tokens; d.K = c.top_k; d.E = c.n_experts; d.D = c.d_model; d.F = c.d_ff;
-            d.has_shared = has_shared ? 1 : 0;
-            HIP_TRY(moe::launch_down_combine(d, stream));
-            return MOE_OK;
-        }
-        if (moe_status st = stage_small_down(c, L, ws, *weights, stream)) return st;
-        HIP_TRY(moe::launch_combine(at<void>(ws, L.slots), slot_bf16, nullptr, residual, out, c.n_tokens,
-                                    c.top_k + (has_shared ? 1 : 0), c.d_model, stream));
-        return MOE_OK;
-    }
-
-    float* ys = has_shared ? at<float>(ws, L.ys) : nullptr;
-    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-    const bool fork = has_shared && aux_stream && aux_stream != stream;
-    if (fork) {
-        if (moe_status st = fork_join_events(&ev_fork, &ev_join)) return st;
-        HIP_TRY(hipEventRecord(ev_fork, stream));
-        HIP_TRY(hipStreamWaitEvent(aux_stream, ev_fork, 0));
-        if (moe_status st = stage_shared(c, L, ws, x, *weights, ys, aux_stream)) return st;
-        HIP_TRY(hipEventRecord(ev_join, aux_stream));
-    } else if (has_shared) {
-        if (moe_status st = stage_shared(c, L, ws, x, *weights, ys, stream)) return st;
-    }
-
-    const int tile_rows = routed_tile_rows(c);
-    int32_t* pairs = at<int32_t>(ws, L.pairs);
-    int4* tiles = at<int4>(ws, L.tiles);
-    int32_t* nt = at<int32_t>(ws, L.n_tiles);
-    const moe::PermParams Q = perm_params(c, ids, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.active),
-                                          at<int32_t>(ws, L.n_active), pairs, tiles, nt, tile_rows,
-                                          at<int32_t>(ws, L.chunk_base));
-    if (moe_status st = stage_logits(c, L, ws, x, weights->router, stream)) return st;
-    if (moe::route_permute_fusable(c.n_tokens, c.n_experts, c.top_k)) {
-        HIP_TRY(moe::launch_route_permute(P, ids, wts, Q, stream));
-    } else {
-        HIP_TRY(moe::launch_route_select(P, ids, wts, stream));
-        HIP_TRY(moe::launch_permute(Q, stream));
-    }
-    void* slots = at<void>(ws, L.slots);
-    if (moe_status st = stage_experts(c, L, ws, x, *weights, pairs, tiles, nt, wts, slots, slot_bf16, stream))
-        return st;
-    if (fork) HIP_TRY(hipStreamWaitEvent(stream, ev_join, 0));
-    HIP_TRY(moe::launch_combine(slots, slot_bf16, ys, residual, out, c.n_tokens, c.top_k, c.d_model, stream));
+moe_status moe_rms_norm(const moe_config* cfg, const float* residual, const float* norm_weight, float eps, void* x,
+                        moe_stream_t stream) {
+    g_err[0] = 0;
+    if (moe_status st = check_config(cfg)) return st;
+    if (cfg->n_tokens == 0) return MOE_OK;
+    if (moe_status st = check_norm(*cfg, residual, norm_weight, eps, x)) return st;
+    (void)hipGetLastError();
+    HIP_TRY(moe::launch_rms_norm(residual, norm_weight, eps, cfg->n_tokens, cfg->d_model, x,
+                                 cfg->act_dtype != MOE_F32, stream));
     return MOE_OK;
+}
+
+moe_status moe_layer_forward_norm(const moe_config* cfg, const moe_weights* weights, const float* norm_weight,
+                                  float eps, const float* residual, void* x_out, float* out, int32_t* topk_ids_out,
+                                  float* topk_weights_out, void* ws, size_t ws_bytes, moe_stream_t stream,
+                                  moe_stream_t aux_stream) {
+    g_err[0] = 0;
+    if (moe_status st = check_config(cfg)) return st;
+    if (cfg->n_tokens == 0) return MOE_OK;
+    if (!residual || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL tensor argument");
+    if (!weights || !weights->router) return fail(MOE_ERR_INVALID_ARGUMENT, "router weights are NULL");
+    if (moe_status st = check_weights(*cfg, weights, true, true)) return st;
+    if (moe_status st = check_ws(*cfg, ws, ws_bytes)) return st;
+    const moe_config& c = *cfg;
+    void* x = x_out ? x_out : at<void>(ws, layout(c).xn);
+    if (moe_status st = check_norm(c, residual, norm_weight, eps, x)) return st;
+    if (x_out && overlaps(x_out, c, out)) return fail(MOE_ERR_INVALID_ARGUMENT, "x_out overlaps out");
+    (void)hipGetLastError();
+    if (norm_fusable(c)) {
+        const NormFold nf{residual, norm_weight, eps, x};
+        return layer_forward_impl(c, weights, x, residual, out, topk_ids_out, topk_weights_out, ws, stream,
+                                  aux_stream, &nf);
+    }
+    HIP_TRY(moe::launch_rms_norm(residual, norm_weight, eps, c.n_tokens, c.d_model, x, c.act_dtype != MOE_F32, stream));
+    return layer_forward_impl(c, weights, x, residual, out, topk_ids_out, topk_weights_out, ws, stream, aux_stream);
 }
 
 moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, const void* x, moe_stage stage,

@@ -130,6 +130,32 @@ __device__ __forceinline__ uint64_t sel_key(float score, int idx) {
 __device__ __forceinline__ int key_index(uint64_t key) { return int(0xffffffffu - uint32_t(key)); }
 __device__ __forceinline__ float key_score(uint64_t key) { return from_orderable(uint32_t(key >> 32)); }
 
+// ------------------------------------------------------------ RMS norm pieces
+// Shared by every kernel that normalises the attention residual, so that all
+// of them produce the same bits: lane l of a wave sums the squares of the
+// row's float4 blocks l, l + 64, l + 128, ... in that order, then wave_sum.
+__device__ __forceinline__ float sum_sq4(float4 v, float s) {
+    s = fmaf(v.x, v.x, s);
+    s = fmaf(v.y, v.y, s);
+    s = fmaf(v.z, v.z, s);
+    return fmaf(v.w, v.w, s);
+}
+__device__ __forceinline__ float rms_inv_from_sum(float sum_sq, int D, float eps) {
+    return 1.0f / sqrtf(sum_sq / float(D) + eps);
+}
+// 1 / rms of a D-element fp32 row (D % 4 == 0); every lane gets the value.
+__device__ __forceinline__ float wave_row_rms_inv(const float* row, int D, float eps, int lane) {
+    const float4* r4 = reinterpret_cast<const float4*>(row);
+    float s = 0.f;
+    for (int i = lane; i < D / 4; i += kWave) s = sum_sq4(r4[i], s);
+    return rms_inv_from_sum(wave_sum(s), D, eps);
+}
+// x = (r * inv) * w, or r * inv without a weight
+__device__ __forceinline__ float norm_scale(float r, float inv, const float* w, float wv) {
+    const float v = r * inv;
+    return w ? v * wv : v;
+}
+
 __device__ __forceinline__ float sigmoidf_(float v) { return 1.0f / (1.0f + __expf(-v)); }
 
 // A value every lane of the wave holds alike, moved to a scalar register so

@@ -132,6 +132,35 @@ __device__ __forceinline__ void load_x(Frag<WK == kWF32>& f, const void* rowp, i
     }
 }
 
+// Activation chunk straight from an fp32 attention-residual row: x = (r * inv)
+// * w rounded to bf16 (the same arithmetic as the RMS-norm kernel, so the
+// same bits); xo, when not null, receives the converted x row.
+__device__ __forceinline__ void load_x_norm(Frag<false>& f, const float* rowp, const float* w, float inv, int kc,
+                                            int q, uint16_t* xo) {
+    if (!rowp) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f.v[j] = as_bf16x8(make_uint4(0, 0, 0, 0));
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int k = kofs<kWBF16>(kc, q, j);
+        const float4 a = *reinterpret_cast<const float4*>(rowp + k);
+        const float4 b = *reinterpret_cast<const float4*>(rowp + k + 4);
+        float4 ga = float4{0.f, 0.f, 0.f, 0.f}, gb = ga;
+        if (w) {
+            ga = *reinterpret_cast<const float4*>(w + k);
+            gb = *reinterpret_cast<const float4*>(w + k + 4);
+        }
+        const u32x4 p = {pack_bf16x2(norm_scale(a.x, inv, w, ga.x), norm_scale(a.y, inv, w, ga.y)),
+                         pack_bf16x2(norm_scale(a.z, inv, w, ga.z), norm_scale(a.w, inv, w, ga.w)),
+                         pack_bf16x2(norm_scale(b.x, inv, w, gb.x), norm_scale(b.y, inv, w, gb.y)),
+                         pack_bf16x2(norm_scale(b.z, inv, w, gb.z), norm_scale(b.w, inv, w, gb.w))};
+        f.v[j] = as_bf16x8(p);
+        if (xo) *reinterpret_cast<u32x4*>(xo + k) = p;
+    }
+}
+
 template <bool F32>
 __device__ __forceinline__ void mma_chunk(f32x4& acc, const Frag<F32>& a, const Frag<F32>& b) {
 #pragma unroll
@@ -265,6 +294,7 @@ __device__ void fused_select(const GemmArgs& a, int32_t* ids_l) {
 
 // --------------------------------------------------------------- kernel
 // MODE: kRoutedGateUp | kRoutedDown | kDenseGateUp | kDenseDown | kDenseStore | kSmallGateUp | kSmallDown
+//       | kDenseStoreNorm
 // WK: weight kind; OUTBF: output stored as bf16 (else fp32)
 // TF: 16-token fragments per tile; WN x WKS waves = 4 (rows x K split)
 template <int MODE, int WK, bool OUTBF, int TF, int WN, int WKS>
@@ -273,6 +303,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     constexpr bool SMALL = (MODE == kSmallGateUp || MODE == kSmallDown);
     constexpr bool DUAL = (MODE == kRoutedGateUp || MODE == kDenseGateUp || MODE == kSmallGateUp);
     constexpr bool ROUTED = (MODE == kRoutedGateUp || MODE == kRoutedDown);
+    constexpr bool NORM = (MODE == kDenseStoreNorm);
+    constexpr bool STORE = (MODE == kDenseStore || NORM);
+    static_assert(!NORM || (TF == 1 && WK == kWBF16), "the folded RMS norm takes bf16 16-row tiles");
     constexpr int KL = WTraits<WK>::KL;
     constexpr int SPAN = 4 * KL;
     constexpr int BM = 16 * TF;
@@ -326,8 +359,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     const int q = lane >> 4;
     const int r = lane & 15;
     // dense store may split K over blockIdx.z (partial sums to separate planes)
-    const int ksub = (MODE == kDenseStore) ? K / max(a.ksplit, 1) : K;
-    const int kbase = (MODE == kDenseStore) ? int(blockIdx.z) * ksub : 0;
+    const int ksub = STORE ? K / max(a.ksplit, 1) : K;
+    const int kbase = STORE ? int(blockIdx.z) * ksub : 0;
     const int wrow0 = blockIdx.y * (16 * WN) + 16 * wn;
     const bool rows_ok = wrow0 < N;
 
@@ -350,7 +383,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                 arow = begin + i;
             }
             if (arow >= 0 && arow < a.n_act_rows)
-                p = F32 ? static_cast<const void*>(static_cast<const float*>(a.act) + size_t(arow) * act_ld)
+                p = (F32 || NORM) ? static_cast<const void*>(static_cast<const float*>(a.act) + size_t(arow) * act_ld)
                         : static_cast<const void*>(static_cast<const uint16_t*>(a.act) + size_t(arow) * act_ld);
         }
         xrow[j] = p;
@@ -362,11 +395,46 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < TF; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (rows_ok) {
-        const size_t wrow = size_t(e) * N + wrow0 + r;
-        const int kper = ksub / WKS;
-        const int kbeg = kbase + wk * kper;
-        const int nchunks = kper / SPAN;
+    // folded RMS norm (router logits from the attention residual): the first
+    // chunk's weights are requested before the residual rows are read for the
+    // tokens' 1/rms, so the HBM and L2 round trips overlap.  Then this lane's
+    // token scale, and (row block 0, first wave column) where the converted x
+    // goes.
+    const size_t wrow = size_t(e) * N + wrow0 + r;
+    const int kper = ksub / WKS;
+    const int kbeg = kbase + wk * kper;
+    const int nchunks = kper / SPAN;
+    [[maybe_unused]] Frag<F32> w_first;
+    [[maybe_unused]] float x_inv = 0.f;
+    [[maybe_unused]] uint16_t* x_dst = nullptr;
+    if constexpr (NORM) {
+        __shared__ float s_inv[16];
+        if (rows_ok && nchunks > 0) load_w<WK>(w_first, w0, s0, m0, wrow, K, kbeg, q);
+        for (int i = wave; i < count; i += 4) {
+            const float v =
+                wave_row_rms_inv(static_cast<const float*>(a.act) + size_t(begin + i) * act_ld, K, a.norm_eps, lane);
+            if (lane == 0) s_inv[i] = v;
+        }
+        __syncthreads();
+        if (r < count) {
+            x_inv = s_inv[r];
+            if (blockIdx.y == 0 && wn == 0) x_dst = static_cast<uint16_t*>(a.norm_x) + size_t(begin + r) * K;
+        }
+    }
+
+    if constexpr (NORM) {
+        if (rows_ok) {
+            for (int c = 0; c < nchunks; ++c) {
+                Frag<F32> wa, xb;
+                if (c == 0)
+                    wa = w_first;
+                else
+                    load_w<WK>(wa, w0, s0, m0, wrow, K, kbeg + c * SPAN, q);
+                load_x_norm(xb, static_cast<const float*>(xrow[0]), a.norm_w, x_inv, kbeg + c * SPAN, q, x_dst);
+                mma_chunk<F32>(acc[0][0], wa, xb);
+            }
+        }
+    } else if (rows_ok) {
         // U = 2 chunks per trip, all loads before any MFMA: a runtime-count
         // loop with MFMAs (convergent) is not unrolled by the compiler, so
         // without this a wave waits a full memory round trip per chunk.
@@ -498,9 +566,11 @@ template <int MODE, int WK, bool OUTBF>
 static hipError_t launch_cfg(const GemmArgs& a, int grid_x, int tf, hipStream_t s) {
     // waves split the workgroup's K range 4, 2 or 1 ways (rows 16, 32, 64)
     constexpr bool SMALL = (MODE == kSmallGateUp || MODE == kSmallDown);
-    int ks = (MODE == kDenseStore && a.ksplit > 1) ? a.ksplit : 1;
+    constexpr bool STORE = (MODE == kDenseStore || MODE == kDenseStoreNorm);
+    if (MODE == kDenseStoreNorm && tf != 1) return hipErrorInvalidValue;
+    int ks = (STORE && a.ksplit > 1) ? a.ksplit : 1;
     if (SMALL) ks = (a.n_tokens + 15) / 16;  // grid.z = 16-token m-tiles (an expert holds <= T pairs)
-    const int kwg = (MODE == kDenseStore) ? a.K / ks : (SMALL && a.has_shared ? gcd_k(a) : a.K);
+    const int kwg = STORE ? a.K / ks : (SMALL && a.has_shared ? gcd_k(a) : a.K);
     if constexpr (SMALL) tf = 1;
     const int nrows = (MODE == kSmallGateUp && a.has_shared && a.sN > a.N) ? a.sN : a.N;
     constexpr int SPAN = 4 * WTraits<WK>::KL;
@@ -526,7 +596,7 @@ static hipError_t launch_cfg(const GemmArgs& a, int grid_x, int tf, hipStream_t 
             dim3 g(grid_x, (nrows + 63) / 64, ks);
             gemm_kernel<MODE, WK, OUTBF, 1, 4, 1><<<g, 256, 0, s>>>(a);
         }
-    } else if constexpr (!SMALL) {
+    } else if constexpr (!SMALL && MODE != kDenseStoreNorm) {
         if (ksplit4) {
             dim3 g(grid_x, (nrows + 15) / 16, ks);
             gemm_kernel<MODE, WK, OUTBF, 4, 1, 4><<<g, 256, 0, s>>>(a);
@@ -559,6 +629,9 @@ hipError_t launch_gemm(int mode, int wkind, bool outbf, const GemmArgs& a, int g
         default:
             // router logits: bf16 or fp32 weights, fp32 output
             return dispatch_wk<kDenseStore>(a, wkind == kWF32 ? kWF32 : kWBF16, false, grid_x, tf, s);
+        case kDenseStoreNorm:
+            if (wkind != kWBF16) return hipErrorInvalidValue;
+            return launch_cfg<kDenseStoreNorm, kWBF16, false>(a, grid_x, tf, s);
     }
 }
 

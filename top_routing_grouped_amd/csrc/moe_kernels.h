@@ -18,7 +18,8 @@ enum {
     kDenseDown = 3,     // all T rows; sigmoid(gate logit) * . (or 1) -> out[t]
     kDenseStore = 4,    // all T rows; plain fp32 store (router logits)
     kSmallGateUp = 5,   // small T*K: tile derived from topk ids in-kernel; shared expert as item 0
-    kSmallDown = 6      // small T*K: same tiles; writes slot rows t*(K+1)+k, shared to slot K
+    kSmallDown = 6,     // small T*K: same tiles; writes slot rows t*(K+1)+k, shared to slot K
+    kDenseStoreNorm = 7 // router logits from the fp32 attention residual, RMS norm folded in (bf16, 16-row tiles)
 };
 
 struct GemmArgs {
@@ -66,6 +67,11 @@ struct GemmArgs {
     float* gate_out;          // [T]
     int direct_pairs;         // small-T gate/up: one work item per (token, slot) pair
     int shape_grid;           // small T: item count the tile shape is chosen for (0: grid_x)
+    // kDenseStoreNorm: act is the fp32 residual [n_rows][K]; x = (r * (1/rms)) * norm_w
+    // is rounded to bf16 on the fly, and the row-block-0 workgroups write it to norm_x
+    const float* norm_w;      // [K] or null (ones)
+    float norm_eps;
+    void* norm_x;             // [n_rows][K] bf16
 };
 // Largest T for which the small-T gate/up launch does the selection itself.
 constexpr int kFusedSelMaxT = 8;
@@ -120,5 +126,10 @@ hipError_t launch_down_combine(const DownCombineArgs& a, hipStream_t s);
 hipError_t launch_combine(const void* slots, bool slots_bf16, const float* shared, const float* residual,
                           float* out, int T, int K, int D, hipStream_t s);
 // small T: the slot rows hold K routed slots + the shared expert (K+1 per token)
+
+// x[t, :] = r[t, :] / sqrt(mean(r[t, :]^2) + eps) * w (w may be NULL: ones);
+// x bf16 (out_bf16) or fp32.  D % 4 == 0; r, w, x 16-byte aligned.
+hipError_t launch_rms_norm(const float* r, const float* w, float eps, int T, int D, void* x, bool out_bf16,
+                           hipStream_t s);
 
 }  // namespace moe
