@@ -143,12 +143,41 @@ __device__ __forceinline__ float sum_sq4(float4 v, float s) {
 __device__ __forceinline__ float rms_inv_from_sum(float sum_sq, int D, float eps) {
     return 1.0f / sqrtf(sum_sq / float(D) + eps);
 }
+// Sums of squares of NR fp32 rows of D elements (D % 4 == 0; a null row reads
+// as zeros), reduced over the wave.  The loads go out in batches of 8 float4
+// per lane and row, all of a batch before any of its sums; blocks past the
+// row end read as zero, and adding +0 leaves a sum of squares unchanged, so
+// each row's sum is the same sequence of operations as summing its blocks
+// lane, lane + 64, ... one at a time.
+template <int NR>
+__device__ __forceinline__ void wave_rows_sum_sq(const float* const (&rows)[NR], int D, int lane, float (&s)[NR]) {
+    constexpr int B = 8;
+    const int n4 = D / 4;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) s[r] = 0.f;
+    for (int base = 0; base < n4; base += kWave * B) {
+        float4 v[NR][B];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                const int i = base + lane + kWave * j;
+                v[r][j] = (rows[r] && i < n4) ? reinterpret_cast<const float4*>(rows[r])[i] : float4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int j = 0; j < B; ++j) s[r] = sum_sq4(v[r][j], s[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) s[r] = wave_sum(s[r]);
+}
 // 1 / rms of a D-element fp32 row (D % 4 == 0); every lane gets the value.
 __device__ __forceinline__ float wave_row_rms_inv(const float* row, int D, float eps, int lane) {
-    const float4* r4 = reinterpret_cast<const float4*>(row);
-    float s = 0.f;
-    for (int i = lane; i < D / 4; i += kWave) s = sum_sq4(r4[i], s);
-    return rms_inv_from_sum(wave_sum(s), D, eps);
+    const float* rows[1] = {row};
+    float s[1];
+    wave_rows_sum_sq<1>(rows, D, lane, s);
+    return rms_inv_from_sum(s[0], D, eps);
 }
 // x = (r * inv) * w, or r * inv without a weight
 __device__ __forceinline__ float norm_scale(float r, float inv, const float* w, float wv) {

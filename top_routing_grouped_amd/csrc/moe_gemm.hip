@@ -410,10 +410,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     if constexpr (NORM) {
         __shared__ float s_inv[16];
         if (rows_ok && nchunks > 0) load_w<WK>(w_first, w0, s0, m0, wrow, K, kbeg, q);
-        for (int i = wave; i < count; i += 4) {
-            const float v =
-                wave_row_rms_inv(static_cast<const float*>(a.act) + size_t(begin + i) * act_ld, K, a.norm_eps, lane);
-            if (lane == 0) s_inv[i] = v;
+        // rows wave and wave + 4 together (both rows' loads in flight at once)
+        for (int i = wave; i < count; i += 8) {
+            const float* rows[2] = {static_cast<const float*>(a.act) + size_t(begin + i) * act_ld,
+                                    i + 4 < count ? static_cast<const float*>(a.act) + size_t(begin + i + 4) * act_ld
+                                                  : nullptr};
+            float ss[2];
+            wave_rows_sum_sq<2>(rows, K, lane, ss);
+            if (lane == 0) {
+                s_inv[i] = rms_inv_from_sum(ss[0], K, a.norm_eps);
+                if (i + 4 < count) s_inv[i + 4] = rms_inv_from_sum(ss[1], K, a.norm_eps);
+            }
         }
         __syncthreads();
         if (r < count) {
