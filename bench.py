@@ -33,7 +33,7 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from synth import WORKLOADS, make_attention_residual, make_tokens, make_weights  # noqa: E402
+from synth import WORKLOAD_TOKENS, WORKLOADS, make_attention_residual, make_tokens, make_weights  # noqa: E402
 from top_routing_grouped_amd import moe  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
@@ -423,9 +423,12 @@ def time_norm(spec, reps, rotate_bytes=384 << 20):
     del rs, g
     torch.cuda.empty_cache()
     gbs = norm_bytes(spec) / (ms / 1e3) / 1e9
-    return {"kernel": "RMS norm of the attention residual", "n_tokens": spec.n_tokens, "launch_us": round(ms * 1e3, 2),
-            "algorithmic_bytes": norm_bytes(spec), "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
+    rec = {"kernel": "RMS norm of the attention residual", "n_tokens": spec.n_tokens, "launch_us": round(ms * 1e3, 2),
+           "algorithmic_bytes": norm_bytes(spec), "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
+    if spec.n_tokens == 4096:
+        rec["traffic"] = traffic_record("rms_norm", "qwen_T4096", norm_bytes(spec))
+    return rec
 
 
 def chained_decode(args, dec_us):
@@ -492,6 +495,37 @@ def crossover(args):
         torch.cuda.empty_cache()
 
 
+def all_configs(args):
+    """One JSON line per workload and token count of the parity
+    configurations, with the same protocol as the headline: chained graph
+    over distinct layer instances (40 up to T = 512, 4 beyond), actual
+    n_active, algorithmic bytes and flops, both roofline fractions, the
+    attainable MFMA ceiling, the routed gate/up launch alone."""
+    for name, Ts in WORKLOAD_TOKENS.items():
+        for T in Ts:
+            big = T > 512
+            L = min(args.instances, 4) if big else args.instances
+            steps = max(80, args.steps // 10) if big else args.steps
+            warmup = max(20, args.warmup // 10) if big else args.warmup
+            res = run_workload(name, T, L, steps, warmup, max(8, args.stage_reps // 4) if big else args.stage_reps)
+            spec = res["spec"]
+            print(json.dumps({
+                "workload": name, "n_tokens": T, "d_model": spec.d_model, "n_experts": spec.n_experts,
+                "top_k": spec.top_k, "d_ff": spec.d_ff, "d_ff_shared": spec.d_ff_shared, "routing": spec.family,
+                "expert_dtype": spec.expert_dtype, "layer_instances": L,
+                "us_per_layer": round(res["ms_per_step"] * 1e3, 2), "tokens_per_s": round(res["tokens_per_s"], 1),
+                "median_chain_us_per_layer": round(res["median_chain_us_per_layer"], 2),
+                "cold_layer_us": round(res["cold_layer_us"], 2), "n_active_mean": round(res["n_active_mean"], 2),
+                "layer_algorithmic_bytes": round(res["layer_bytes"]),
+                "layer_algorithmic_flops": round(res["layer_flops"]),
+                "layer_hbm_frac": round(res["layer_hbm_frac"], 4), "layer_mfma_frac": round(res["layer_mfma_frac"], 4),
+                "mfma_ceiling": round(res["mfma_ceiling"], 4), "gateup_us": round(res["gateup_ms"] * 1e3, 2),
+                "gateup_hbm_frac": round(res["gateup_gbs"] / HBM_PEAK_GBS, 4),
+                "gateup_mfma_frac": round(res["gateup_tflops"] / BF16_PEAK_TFLOPS, 4)}), flush=True)
+            del res
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -508,6 +542,10 @@ def main():
                     help="small-T study: routed gate/up with one work item per (token, slot) pair versus grouped "
                          "by expert, T = 1..32 at decode shape; prints one JSON line per T")
     ap.add_argument("--no-chain", action="store_true")
+    ap.add_argument("--configs", action="store_true",
+                    help="one JSON line per parity configuration (every workload and token count)")
+    ap.add_argument("--workload", default=None, help="with --tokens: run this one workload (profiling aid)")
+    ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--only", choices=["decode", "prefill", "chain"], default=None,
                     help="profiling aid: run one workload and print its log line only")
     args = ap.parse_args()
@@ -524,8 +562,19 @@ def main():
     if args.crossover:
         crossover(args)
         return
+    if args.configs:
+        all_configs(args)
+        return
+    if args.workload:
+        T = args.tokens or WORKLOADS[args.workload].n_tokens
+        big = T > 512
+        run_workload(args.workload, T, min(args.instances, 4) if big else args.instances, args.steps, args.warmup,
+                     args.stage_reps)
+        return
     if args.only == "chain":
         chained_decode(args, float("nan"))
+        if args.copy_calibration:
+            copy_calibration()
         return
     if args.only == "prefill":
         run_workload("qwen_prefill_skew", 4096, min(args.instances, 4), args.steps, args.warmup, args.stage_reps)

@@ -86,7 +86,8 @@ typedef struct {
     moe_dtype act_dtype;    /* x: MOE_F32 or MOE_BF16 */
     moe_dtype router_dtype; /* router and shared gate vector: same as act_dtype */
     moe_dtype expert_dtype; /* routed and shared banks: MOE_F32 (with F32 activations),
-                               MOE_BF16 or MOE_U4_AFFINE_G64 (with BF16 activations) */
+                               MOE_BF16 or MOE_U4_AFFINE_G64 (with BF16 activations;
+                               d_model, d_ff, d_ff_shared <= 4096) */
 } moe_config;
 
 /* One weight matrix or bank.  For MOE_F32/MOE_BF16 only `w` is used

@@ -54,11 +54,13 @@ bool dense_tiled(const moe_config& c, moe_dtype d) { return c.n_tokens >= 128 &&
 // extra work item of the routed launches.
 bool small_path(const moe_config& c) { return !routed_large(c) && (int64_t)c.n_tokens * c.top_k <= 256; }
 int h_ld(const moe_config& c) { return std::max(c.d_ff, c.d_ff_shared); }
-// Small path with bf16 weights: the down projection and the combine are one
-// launch (each workgroup owns a slice of output features for every token).
+// Small path with bf16 or 4-bit weights: the down projection and the combine
+// are one launch (each workgroup owns a slice of output features for every
+// token).
 bool down_combine_fused(const moe_config& c) {
-    return small_path(c) && c.expert_dtype == MOE_BF16 &&
-           moe::down_combine_supported(c.n_tokens, c.top_k, c.d_model, c.d_ff, c.d_ff_shared);
+    return small_path(c) && (c.expert_dtype == MOE_BF16 || c.expert_dtype == MOE_U4_AFFINE_G64) &&
+           moe::down_combine_supported(c.n_tokens, c.top_k, c.d_model, c.d_ff, c.d_ff_shared,
+                                       c.expert_dtype == MOE_U4_AFFINE_G64);
 }
 
 // Router logits: for small T, K is split over up to 8 workgroups (partial
@@ -150,6 +152,11 @@ moe_status check_config(const moe_config* c) {
     if (c->router_dtype != c->act_dtype) return fail(MOE_ERR_UNSUPPORTED, "router_dtype must equal act_dtype");
     if (f32 ? c->expert_dtype != MOE_F32 : (c->expert_dtype != MOE_BF16 && c->expert_dtype != MOE_U4_AFFINE_G64))
         return fail(MOE_ERR_UNSUPPORTED, "expert_dtype must be F32 with F32 activations, BF16 or U4_AFFINE_G64 with BF16");
+    if (c->expert_dtype == MOE_U4_AFFINE_G64 &&
+        (c->d_model > 64 * moe::kU4MaxGroups || c->d_ff > 64 * moe::kU4MaxGroups ||
+         c->d_ff_shared > 64 * moe::kU4MaxGroups))
+        return fail(MOE_ERR_UNSUPPORTED, "4-bit weights: d_model, d_ff and d_ff_shared must be <= %d",
+                    64 * moe::kU4MaxGroups);
     const int span = kspan_of(c->expert_dtype);
     if (c->d_model % span || c->d_ff % span || c->d_ff_shared % span)
         return fail(MOE_ERR_UNSUPPORTED, "d_model, d_ff, d_ff_shared must be multiples of %d for this dtype", span);
@@ -488,6 +495,11 @@ moe_status layer_forward_impl(const moe_config& c, const moe_weights* weights, c
             d.residual = residual; d.out = out;
             d.T = c.n_tokens; d.K = c.top_k; d.E = c.n_experts; d.D = c.d_model; d.F = c.d_ff;
             d.has_shared = has_shared ? 1 : 0;
+            if (c.expert_dtype == MOE_U4_AFFINE_G64) {
+                d.u4 = 1;
+                d.w_scale = weights->down.scale; d.w_min = weights->down.min;
+                if (has_shared) { d.ws_scale = weights->shared_down.scale; d.ws_min = weights->shared_down.min; }
+            }
             HIP_TRY(moe::launch_down_combine(d, stream));
             return MOE_OK;
         }

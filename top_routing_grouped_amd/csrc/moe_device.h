@@ -22,7 +22,19 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     __bf16 b = static_cast<__bf16>(f);
     return uint32_t(__builtin_bit_cast(uint16_t, b));
 }
+// Two floats -> packed bf16 (lo in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 (converting the halves one at a time costs a shift and an
+// or more per pair).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+// The same rounding with the halves converted one at a time: more instructions,
+// but neither float waits in a register for the other (the 4-bit
+// dequantisation of the down projections keeps 5 waves per SIMD this way,
+// 4 with pack_bf16x2).
+__device__ __forceinline__ uint32_t pack_bf16x2_split(float lo, float hi) {
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 

@@ -1,4 +1,5 @@
-// Down projection fused with the combine, for small token counts (Treebeard,
+// Down projection fused with the combine, for small token counts, bf16 or
+// 4-bit affine group-64 weights (Treebeard,
 // "How Treebeard routes Qwen3.6 MoE tokens", "Routed expert computation" and
 // "Shared expert computation", last block):
 //   out[t, :] = residual[t, :] + sum_{k ascending} alpha[t, k] * (W_down[e_tk] h[t*K + k])
@@ -44,8 +45,30 @@ __device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float acc)
     return dot2(a3, b3, dot2(a2, b2, dot2(a1, b1, dot2(a0, b0, acc))));
 }
 
-// J: 16-byte loads per lane per unit (F = 64 J)
-template <int J>
+// 4-bit weights: piece j of lane s covers reduction elements 256 j + 32 s ..
+// +31 (16 bytes of codes, inside one group of 64); the same 32 h elements are
+// 4 loads of 16 bytes.  Each weight is dequantised to bf16 (w = scale * q +
+// min, rounded to nearest even, as in the MFMA path) and dotted with h in
+// pairs.
+__device__ __forceinline__ float dot_u4_piece(const u32x4& c, float s, float m, const u32x4 (&h)[4], float acc) {
+    const uint32_t words[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t even = words[i] & 0x0f0f0f0fu, odd = (words[i] >> 4) & 0x0f0f0f0fu;
+        const uint32_t h0 = h[i].x, h1 = h[i].y, h2 = h[i].z, h3 = h[i].w;
+        const uint32_t hp[4] = {h0, h1, h2, h3};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t wp = pack_bf16x2(fmaf(s, float((even >> (8 * b)) & 0xffu), m),
+                                            fmaf(s, float((odd >> (8 * b)) & 0xffu), m));
+            acc = dot2(wp, hp[b], acc);
+        }
+    }
+    return acc;
+}
+
+// J: 16-byte weight loads per lane per unit (bf16: F = 64 J; U4: F = 256 J)
+template <int J, bool U4>
 __global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombineArgs a) {
     __shared__ float part[kDcWaves][kDcMaxT][kDcR];
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
@@ -76,7 +99,7 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombine
     const uint16_t* wb = static_cast<const uint16_t*>(a.w);
     const uint16_t* wsb = static_cast<const uint16_t*>(a.ws);
     const uint16_t* hb = static_cast<const uint16_t*>(a.h);
-    const int F = 64 * J;
+    const int F = U4 ? 256 * J : 64 * J;
 
     // unit u: token u / KS, slot u % KS (slot K: the shared expert).  Buffer
     // loads: the unit's row-slice and h row are scalar bases, a lane's byte
@@ -84,6 +107,33 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombine
     // load destinations (address arithmetic on VGPRs made the compiler wait
     // for the loads in flight before reusing their registers).
     const uint32_t w_off = uint32_t((r * F + 8 * s) * 2), h_off = uint32_t(16 * s);
+    // 4-bit: lane offsets of the codes, the group scale/min and the h pieces
+    const uint32_t c_off = uint32_t(r * (F / 2) + 16 * s), g_off = uint32_t((r * (F / 64) + s / 2) * 2),
+                   hq_off = uint32_t(64 * s);
+    const uint8_t* cb = static_cast<const uint8_t*>(a.w);
+    const uint8_t* csb = static_cast<const uint8_t*>(a.ws);
+    auto load_u4 = [&](int u, u32x4 (&cr)[J], uint32_t (&sm)[J], u32x4 (&hr)[J][4]) __attribute__((always_inline)) {
+        const int t = u / KS, k = u - t * KS;
+        const int e = __builtin_amdgcn_readlane(u_e, u - ub);
+        const size_t rowi = e >= 0 ? size_t(e) * a.D + d0 : size_t(d0);
+        const uint8_t* crow = (e >= 0 ? cb : csb) + rowi * (F / 2);
+        const uint16_t* srow = static_cast<const uint16_t*>(e >= 0 ? a.w_scale : a.ws_scale) + rowi * (F / 64);
+        const uint16_t* mrow = static_cast<const uint16_t*>(e >= 0 ? a.w_min : a.ws_min) + rowi * (F / 64);
+        const size_t hrow = k < K ? size_t(t) * K + k : size_t(TK) + t;
+        const auto rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(crow), 0, kDcR * F / 2, kRsrcWord3);
+        const auto rsc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(srow), 0, kDcR * F / 32, kRsrcWord3);
+        const auto rmn = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(mrow), 0, kDcR * F / 32, kRsrcWord3);
+        const auto rh = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(hb + hrow * a.h_ld), 0, F * 2, kRsrcWord3);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            cr[j] = __builtin_amdgcn_raw_buffer_load_b128(rc, c_off + 128 * j, 0, 0);
+            const uint32_t sv = __builtin_amdgcn_raw_buffer_load_b16(rsc, g_off + 8 * j, 0, 0);
+            const uint32_t mv = __builtin_amdgcn_raw_buffer_load_b16(rmn, g_off + 8 * j, 0, 0);
+            sm[j] = sv | (mv << 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hr[j][i] = __builtin_amdgcn_raw_buffer_load_b128(rh, hq_off + 512 * j + 16 * i, 0, 0);
+        }
+    };
     auto load = [&](int u, u32x4 (&wr)[J], u32x4 (&hr)[J]) __attribute__((always_inline)) {
         const int t = u / KS, k = u - t * KS;
         const int e = __builtin_amdgcn_readlane(u_e, u - ub);
@@ -125,7 +175,35 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombine
         acc = fmaf(unit_scale(u), p0 + p1, acc);
     };
 
-    if (ub < ue) {
+    auto use_u4 = [&](int u, const u32x4 (&cr)[J], const uint32_t (&sm)[J], const u32x4 (&hr)[J][4])
+                      __attribute__((always_inline)) {
+        const int t = u / KS;
+        if (t != cur_t) {
+            flush();
+            cur_t = t;
+        }
+        float p = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; ++j) p = dot_u4_piece(cr[j], bf16_lo(sm[j]), bf16_hi(sm[j]), hr[j], p);
+        acc = fmaf(unit_scale(u), p, acc);
+    };
+
+    if constexpr (U4) {
+        if (ub < ue) {
+            u32x4 ca[J], cn[J], ha[J][4], hn[J][4];
+            uint32_t sa[J], sn[J];
+            load_u4(ub, ca, sa, ha);
+            int u = ub;
+            for (; u + 2 <= ue; u += 2) {
+                load_u4(u + 1, cn, sn, hn);
+                use_u4(u, ca, sa, ha);
+                load_u4(min(u + 2, ue - 1), ca, sa, ha);
+                use_u4(u + 1, cn, sn, hn);
+            }
+            if (u < ue) use_u4(u, ca, sa, ha);
+            flush();
+        }
+    } else if (ub < ue) {
         u32x4 wa[J], ha[J], wn[J], hn[J];
         load(ub, wa, ha);
         int u = ub;
@@ -155,22 +233,34 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombine
 
 }  // namespace
 
-bool down_combine_supported(int T, int K, int D, int F, int Fs) {
+bool down_combine_supported(int T, int K, int D, int F, int Fs, bool u4) {
     // a wave's units (T * (K + 1) / 8 of them) must fit its 64 lanes
     if (T <= 0 || T > kDcMaxT || D % kDcR || T * (K + 1) > 64 * kDcWaves) return false;
     if (Fs != 0 && Fs != F) return false;
+    if (u4) return F == 256 || F == 512 || F == 768 || F == 1024;
     return F == 128 || F == 256 || F == 512 || F == 768 || F == 1024;
 }
 
 hipError_t launch_down_combine(const DownCombineArgs& a, hipStream_t s) {
-    if (!down_combine_supported(a.T, a.K, a.D, a.F, a.has_shared ? a.F : 0)) return hipErrorInvalidValue;
+    const bool u4 = a.u4 != 0;
+    if (!down_combine_supported(a.T, a.K, a.D, a.F, a.has_shared ? a.F : 0, u4)) return hipErrorInvalidValue;
+    if (u4 && (!a.w_scale || !a.w_min || (a.has_shared && (!a.ws_scale || !a.ws_min)))) return hipErrorInvalidValue;
     const dim3 g(unsigned(a.D / kDcR)), b(kDcWaves * 64);
+    if (u4) {
+        switch (a.F / 256) {
+            case 1: down_combine_kernel<1, true><<<g, b, 0, s>>>(a); break;
+            case 2: down_combine_kernel<2, true><<<g, b, 0, s>>>(a); break;
+            case 3: down_combine_kernel<3, true><<<g, b, 0, s>>>(a); break;
+            default: down_combine_kernel<4, true><<<g, b, 0, s>>>(a); break;
+        }
+        return hipGetLastError();
+    }
     switch (a.F / 64) {
-        case 2: down_combine_kernel<2><<<g, b, 0, s>>>(a); break;
-        case 4: down_combine_kernel<4><<<g, b, 0, s>>>(a); break;
-        case 8: down_combine_kernel<8><<<g, b, 0, s>>>(a); break;
-        case 12: down_combine_kernel<12><<<g, b, 0, s>>>(a); break;
-        default: down_combine_kernel<16><<<g, b, 0, s>>>(a); break;
+        case 2: down_combine_kernel<2, false><<<g, b, 0, s>>>(a); break;
+        case 4: down_combine_kernel<4, false><<<g, b, 0, s>>>(a); break;
+        case 8: down_combine_kernel<8, false><<<g, b, 0, s>>>(a); break;
+        case 12: down_combine_kernel<12, false><<<g, b, 0, s>>>(a); break;
+        default: down_combine_kernel<16, false><<<g, b, 0, s>>>(a); break;
     }
     return hipGetLastError();
 }

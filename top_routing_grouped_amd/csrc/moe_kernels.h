@@ -75,6 +75,9 @@ struct GemmArgs {
 };
 // Largest T for which the small-T gate/up launch does the selection itself.
 constexpr int kFusedSelMaxT = 8;
+// 4-bit weights: largest count of 64-element groups in a GEMM workgroup's K
+// range (reduction lengths up to 4096), the size of the LDS scale staging.
+constexpr int kU4MaxGroups = 64;
 
 hipError_t launch_gemm(int mode, int wkind, bool outbf, const GemmArgs& a, int grid_x, int tf, hipStream_t s);
 // bf16 LDS-tiled variant; K % 64 == 0.  Routed modes: tiles of tiled_rows()
@@ -120,8 +123,15 @@ struct DownCombineArgs {
     const float* residual;    // [T][D]
     float* out;               // [T][D]
     int T, K, E, D, F, has_shared;
+    // 4-bit affine group-64 banks (u4 != 0): w / ws hold the codes [.., D, F/2];
+    // scale and min bf16 [.., D, F/64]
+    int u4;
+    const void* w_scale;
+    const void* w_min;
+    const void* ws_scale;
+    const void* ws_min;
 };
-bool down_combine_supported(int T, int K, int D, int F, int Fs);
+bool down_combine_supported(int T, int K, int D, int F, int Fs, bool u4);
 hipError_t launch_down_combine(const DownCombineArgs& a, hipStream_t s);
 hipError_t launch_combine(const void* slots, bool slots_bf16, const float* shared, const float* residual,
                           float* out, int T, int K, int D, hipStream_t s);
