@@ -1,0 +1,73 @@
+"""GPU parity at the edges of what the library accepts, against the fp64 oracle:
+the largest expert count and top-k (E = 1024, K = 32, both routing families,
+every schedule from the small-T path to the tiled large-T path), top-1
+routing, K = E (every expert selected: a dense softmax mixture), and a router
+that ties every expert, so that every token takes experts 0..K-1 (the lowest
+index wins, [T] "Routing math" reading R1) and K experts each receive all T
+pairs (one expert spanning many GEMM tiles)."""
+import numpy as np
+import pytest
+
+from tests.gpu_harness import TOL, check_layer, check_route, make_case, run_layer, spec_of
+
+pytestmark = pytest.mark.gpu
+
+SMALL_DIMS = dict(d_model=256, d_ff=128, d_ff_shared=128)
+
+
+def _sample(T, seed=0, n=48):
+    if T <= 64:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, n - 2, replace=False)]))
+
+
+def _layer_vs_oracle(case):
+    out, ids, wts = run_layer(case)
+    z, rt = case.oracle_route()
+    flagged = check_route(case, ids, wts, z, rt)
+    err = check_layer(case, out, ids, tokens=_sample(case.spec.n_tokens))
+    return ids, wts, flagged, err
+
+
+@pytest.mark.parametrize("family,T", [("softmax", 3), ("softmax", 200), ("softmax", 2048),
+                                      ("sigmoid_group", 3), ("sigmoid_group", 200)])
+def test_layer_max_experts_and_top_k(family, T):
+    if family == "softmax":
+        spec = spec_of("qwen_decode", n_tokens=T, n_experts=1024, top_k=32, **SMALL_DIMS)
+    else:
+        spec = spec_of("sigmoid_group", n_tokens=T, n_experts=1024, n_group=16, topk_group=4, top_k=32,
+                       **SMALL_DIMS)
+    ids, _, flagged, err = _layer_vs_oracle(make_case(spec))
+    assert ids.min() >= 0 and ids.max() < 1024
+    print(f"{family} E=1024 K=32 T={T}: {flagged} near-tie tokens, y_moe normwise error {err:.2e}")
+
+
+@pytest.mark.parametrize("T", [1, 37, 1000])
+def test_layer_top1(T):
+    spec = spec_of("qwen_decode", n_tokens=T, n_experts=64, top_k=1, **SMALL_DIMS)
+    _, wts, _, err = _layer_vs_oracle(make_case(spec))
+    np.testing.assert_allclose(wts, 1.0, rtol=1e-6)  # one selected expert carries the whole weight
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("T", [5, 300])
+def test_layer_every_expert_selected(T):
+    spec = spec_of("qwen_decode", n_tokens=T, n_experts=16, top_k=16, **SMALL_DIMS)
+    ids, wts, _, _ = _layer_vs_oracle(make_case(spec))
+    assert (np.sort(ids, axis=1) == np.arange(16)[None]).all()
+    np.testing.assert_allclose(wts.sum(axis=1), 1.0, rtol=1e-5)
+
+
+@pytest.mark.parametrize("dtype,T", [("bf16", 37), ("bf16", 700), ("bf16", 5000), ("u4", 37), ("u4", 700)])
+def test_layer_all_tied_router_hot_experts(dtype, T):
+    base = "qwen_decode" if dtype == "bf16" else "qwen_u4"
+    spec = spec_of(base, n_tokens=T, n_experts=32, top_k=4, **SMALL_DIMS)
+    case = make_case(spec, cache_key=("tied", dtype, T))
+    case.w.router.zero_()
+    case.wr64[:] = 0.0
+    out, ids, wts = run_layer(case)
+    assert (ids == np.arange(4)[None]).all()  # all logits equal: the lowest indices win
+    np.testing.assert_allclose(wts, 0.25, rtol=1e-6)
+    err = check_layer(case, out, ids, tokens=_sample(T))
+    print(f"{dtype} T={T}: experts 0..3 with {T} pairs each, y_moe normwise error {err:.2e}")
