@@ -148,7 +148,8 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids,
  * slot_out [T, K, D] fp32.  Inputs are the permute outputs above (only the
  * first n_active entries of active_experts are read) and the flat weights
  * [T*K] fp32.  Only active experts' weights are read, each once per tile of
- * up to 16 (small T) or 64 (large T) of its pairs.  The SwiGLU intermediate
+ * up to 16 of its pairs (small T), 128 (bf16 weights, experts averaging >= 16
+ * pairs) or 64 (4-bit and fp32 weights, >= 64 pairs).  The SwiGLU intermediate
  * is rounded to bf16 for bf16/u4 weights and kept fp32 for fp32 weights. */
 moe_status moe_experts(const moe_config* cfg, const void* x, const moe_weights* weights,
                        const int32_t* expert_offsets, const int32_t* active_experts,
@@ -175,7 +176,8 @@ moe_status moe_combine(const moe_config* cfg, const float* slot_out, const float
  * topk_ids_out [T, K] and topk_weights_out [T, K] receive the routing when
  * non-NULL.  Internally the routed slot rows are staged in bf16 for bf16/u4
  * weights.  Schedules:
- *   T*K <= 256 (and experts averaging < 64 pairs): a single stream; the
+ *   T*K <= 256 (and experts averaging < 16 pairs for bf16 weights, < 64
+ *     otherwise): a single stream; the
  *     shared expert is one more work item of the routed gate/up and down
  *     launches, its sigmoid gate logit is computed with the routing, and each
  *     GEMM workgroup finds its expert and pairs from the routing ids itself

@@ -25,7 +25,7 @@ SMALL = {
     # d_ff 256: the fused down + combine launch with 4-bit weights at small T
     "small_u4_f256": ("qwen_u4", dict(d_model=256, n_experts=32, top_k=4, d_ff=256, d_ff_shared=256)),
 }
-SMALL_T = [1, 37, 301, 700]
+SMALL_T = [1, 37, 100, 301, 700]  # 100: bf16 experts average < 16 pairs above the small path (16-token tiles)
 
 FULL = [("tiny_f32", 4), ("qwen_decode", 1), ("qwen_decode", 8), ("qwen_decode", 32),
         ("qwen_prefill_skew", 4096), ("sigmoid_group", 2048), ("qwen_u4", 1), ("qwen_u4", 64), ("qwen_u4", 512)]

@@ -659,12 +659,15 @@ static hipError_t launch_cfg(const GemmArgs& a, int grid_x, int tf, hipStream_t 
     const bool ksplit4 = (kwg % (4 * SPAN) == 0);
     const bool ksplit2 = (kwg % (2 * SPAN) == 0);
     const int shape_x = a.shape_grid > 0 ? a.shape_grid : grid_x;  // work items the tile shape is chosen for
-    if (SMALL && kwg % SPAN == 0 && (long long)shape_x * ((nrows + 63) / 64) >= 512) {
-        // small T with enough work items: 64 weight rows per workgroup, no K
-        // split (measured at T = 8: a quarter of the workgroups of 16-row,
-        // 4-way-K tiles, all resident at once, and the per-workgroup routing
-        // decode runs a quarter as often).  Fewer items (T <= 4) keep the
-        // 16-row tiles below: 64-row ones would leave ~1 workgroup per CU.
+    const bool routed16 = (MODE == kRoutedGateUp || MODE == kRoutedDown) && tf == 1;
+    if ((SMALL || routed16) && kwg % SPAN == 0 && (long long)shape_x * ((nrows + 63) / 64) >= 512) {
+        // enough work items: 64 weight rows per workgroup, no K split
+        // (measured at T = 8: a quarter of the workgroups of 16-row, 4-way-K
+        // tiles, all resident at once, and the per-workgroup routing decode
+        // runs a quarter as often; routed 16-token tiles at medium T: 4-bit
+        // T = 512 layer 252 -> 220 us, bf16 T = 256 386 -> 357 us).  Fewer
+        // items (T <= 4) keep the 16-row tiles below: 64-row ones would leave
+        // ~1 workgroup per CU.
         dim3 g(grid_x, (nrows + 63) / 64, ks);
         gemm_kernel<MODE, WK, OUTBF, 1, 4, 1><<<g, 256, 0, s>>>(a);
     } else if (tf == 1 || SMALL) {

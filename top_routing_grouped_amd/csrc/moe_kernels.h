@@ -81,7 +81,7 @@ constexpr int kU4MaxGroups = 64;
 
 hipError_t launch_gemm(int mode, int wkind, bool outbf, const GemmArgs& a, int grid_x, int tf, hipStream_t s);
 // bf16 LDS-tiled variant; K % 64 == 0.  Routed modes: tiles of tiled_rows()
-// pairs (256 weight rows x 256 tokens per workgroup); dense modes: token
+// pairs (256 weight rows x 128 tokens per workgroup); dense modes: token
 // tiles of tiled_rows_dense() (128 x 128).
 hipError_t launch_gemm_tiled(int mode, bool outbf, const GemmArgs& a, int grid_x, hipStream_t s);
 int tiled_rows();
