@@ -561,21 +561,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                     for (int i = 0; i < 4; ++i) dst[((m * TF + j) * 4 + i) * 64 + lane] = acc[m][j][i];
         }
         __syncthreads();
-        if (wk > 0) return;
+        if (wk == 0) {
 #pragma unroll
-        for (int s = 1; s < WKS; ++s) {
-            const float* src = red + ((s - 1) * WN + wn) * NACC * 64;
+            for (int s = 1; s < WKS; ++s) {
+                const float* src = red + ((s - 1) * WN + wn) * NACC * 64;
 #pragma unroll
-            for (int m = 0; m < NM; ++m)
+                for (int m = 0; m < NM; ++m)
 #pragma unroll
-                for (int j = 0; j < TF; ++j)
+                    for (int j = 0; j < TF; ++j)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[m][j][i] += src[((m * TF + j) * 4 + i) * 64 + lane];
+                        for (int i = 0; i < 4; ++i) acc[m][j][i] += src[((m * TF + j) * 4 + i) * 64 + lane];
+            }
         }
     }
-    if (!rows_ok) return;
-
-    // ---- epilogue: lane holds rows wrow0 + 4q + (0..3) of token column j*16 + r
+    // ---- epilogue (waves of the first K part): lane holds rows wrow0 + 4q +
+    // (0..3) of token column j*16 + r.  (A guarded block rather than early
+    // returns: the compiler allocates 4-bit gate/up launches 118 registers
+    // this way instead of 152, one more wave per SIMD.)
+    if (!rows_ok || wk != 0) return;
     const int f0 = wrow0 + 4 * q;
 #pragma unroll
     for (int j = 0; j < TF; ++j) {
