@@ -220,7 +220,9 @@ moe_status moe_layer_forward_norm(const moe_config* cfg, const moe_weights* weig
 typedef enum {
     MOE_STAGE_ROUTER_LOGITS = 0, /* router GEMM: x [T,D] -> fp32 logits in ws */
     MOE_STAGE_GATE_UP = 1,       /* routed gate/up GEMM + SwiGLU -> h in ws */
-    MOE_STAGE_DOWN = 2,          /* routed down GEMM x alpha -> staged slot rows in ws */
+    MOE_STAGE_DOWN = 2,          /* routed down GEMM x alpha -> staged slot rows in ws (small T
+                                    with bf16/4-bit weights: the down projection fused with the
+                                    combine, writing a [T, D] scratch in ws) */
     MOE_STAGE_GATE_UP_DIRECT = 3 /* small T*K only (<= 256 pairs, fewer than 64 per expert):
                                     the gate/up stage with every (token, slot) pair as its
                                     own work item, no grouping by expert (Treebeard, "Intel

@@ -275,3 +275,27 @@ def test_gate_up_direct_stage_rejects_large_t():
     ws = moe.alloc_workspace(cfg)
     with pytest.raises(moe.MoeError):
         moe.layer_stage(cfg, moe.weights_struct(case.w), case.x, moe.STAGE_GATE_UP_DIRECT, ws)
+
+
+@pytest.mark.parametrize("name,T", [("qwen_decode", 8), ("qwen_u4", 64), ("small_bf16", 301)])
+def test_layer_stages_leave_caller_outputs_alone(name, T):
+    """Re-launching each stage of the last forward (the kernels the layer ran:
+    at small T the fused down + combine) succeeds, touches none of the
+    caller's buffers, and a forward afterwards reproduces the first bits."""
+    case = _small(name, T) if name in SMALL else make_case(spec_of(name, n_tokens=T))
+    cfg = moe.config_from_spec(case.spec)
+    ws = moe.alloc_workspace(cfg)
+    wst = moe.weights_struct(case.w)
+    out = torch.empty_like(case.r)
+    r = case.r.clone()
+    moe.layer_forward(cfg, wst, case.x, r, out, None, None, ws)
+    torch.cuda.synchronize()
+    first = out.clone()
+    for stage in (moe.STAGE_ROUTER_LOGITS, moe.STAGE_GATE_UP, moe.STAGE_DOWN):
+        moe.layer_stage(cfg, wst, case.x, stage, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), first.view(torch.int32))
+    assert torch.equal(r.view(torch.int32), case.r.view(torch.int32))
+    moe.layer_forward(cfg, wst, case.x, r, out, None, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), first.view(torch.int32))

@@ -400,6 +400,26 @@ moe_status stage_small_down(const moe_config& c, const Layout& L, void* ws, cons
     return MOE_OK;
 }
 
+// The small-T down projection fused with the combine (bf16 or 4-bit banks).
+moe::DownCombineArgs down_combine_args(const moe_config& c, const Layout& L, void* ws, const moe_weights& w,
+                                       const float* residual, float* out) {
+    const bool has_shared = c.d_ff_shared > 0;
+    moe::DownCombineArgs d{};
+    d.h = at<void>(ws, L.h); d.h_ld = h_ld(c);
+    d.ids = at<int32_t>(ws, L.ids); d.wts = at<float>(ws, L.wts);
+    d.w = w.down.w; d.ws = has_shared ? w.shared_down.w : nullptr;
+    d.gate_logit = has_shared && w.shared_gate_vec ? at<float>(ws, L.gate_logit) : nullptr;
+    d.residual = residual; d.out = out;
+    d.T = c.n_tokens; d.K = c.top_k; d.E = c.n_experts; d.D = c.d_model; d.F = c.d_ff;
+    d.has_shared = has_shared ? 1 : 0;
+    if (c.expert_dtype == MOE_U4_AFFINE_G64) {
+        d.u4 = 1;
+        d.w_scale = w.down.scale; d.w_min = w.down.min;
+        if (has_shared) { d.ws_scale = w.shared_down.scale; d.ws_min = w.shared_down.min; }
+    }
+    return d;
+}
+
 moe_status stage_experts(const moe_config& c, const Layout& L, void* ws, const void* x, const moe_weights& w,
                          const int32_t* pairs, const int4* tiles, const int32_t* n_tiles, const float* wts,
                          void* slot_out, bool slot_bf16, hipStream_t s) {
@@ -493,20 +513,7 @@ moe_status layer_forward_impl(const moe_config& c, const moe_weights* weights, c
         if (!fuse) HIP_TRY(moe::launch_route_select_gate(P, G, ids, wts, stream));
         if (moe_status st = stage_small_gateup(c, L, ws, x, *weights, stream, fuse ? &P : nullptr, &G)) return st;
         if (down_combine_fused(c)) {
-            moe::DownCombineArgs d{};
-            d.h = at<void>(ws, L.h); d.h_ld = h_ld(c);
-            d.ids = ids; d.wts = wts;
-            d.w = weights->down.w; d.ws = has_shared ? weights->shared_down.w : nullptr;
-            d.gate_logit = has_shared && weights->shared_gate_vec ? at<float>(ws, L.gate_logit) : nullptr;
-            d.residual = residual; d.out = out;
-            d.T = c.n_tokens; d.K = c.top_k; d.E = c.n_experts; d.D = c.d_model; d.F = c.d_ff;
-            d.has_shared = has_shared ? 1 : 0;
-            if (c.expert_dtype == MOE_U4_AFFINE_G64) {
-                d.u4 = 1;
-                d.w_scale = weights->down.scale; d.w_min = weights->down.min;
-                if (has_shared) { d.ws_scale = weights->shared_down.scale; d.ws_min = weights->shared_down.min; }
-            }
-            HIP_TRY(moe::launch_down_combine(d, stream));
+            HIP_TRY(moe::launch_down_combine(down_combine_args(c, L, ws, *weights, residual, out), stream));
             return MOE_OK;
         }
         if (moe_status st = stage_small_down(c, L, ws, *weights, stream)) return st;
@@ -726,6 +733,13 @@ moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, co
             if (!small_path(c)) return fail(MOE_ERR_UNSUPPORTED, "the direct gate/up stage needs the small-T path");
             return stage_small_gateup_direct(c, L, ws, x, *weights, stream);
         case MOE_STAGE_DOWN:
+            if (down_combine_fused(c)) {
+                // the layer's own launch, writing into the workspace (y_shared region,
+                // [T, D] fp32, also standing in for the residual)
+                float* y = at<float>(ws, L.ys);
+                HIP_TRY(moe::launch_down_combine(down_combine_args(c, L, ws, *weights, y, y), stream));
+                return MOE_OK;
+            }
             if (small_path(c)) return stage_small_down(c, L, ws, *weights, stream);
             return stage_down(c, L, ws, *weights, pairs, tiles, nt, at<float>(ws, L.wts), at<void>(ws, L.slots),
                               c.expert_dtype != MOE_F32, stream);
