@@ -397,8 +397,18 @@ __device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
     asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
     return v;
 }
+__device__ __forceinline__ uint32_t ds_read4(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
 __device__ __forceinline__ void lgkm_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void tie(uint32_t& v) { asm volatile("" : "+v"(v)); }
+// 4 bytes per lane from a buffer straight into LDS at dst + 4 * lane
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(dst), 4, voff, 0, 0, 0);
+}
 constexpr uint32_t kDropOffset = 0x80000000u;  // past every buffer: the store is dropped
 
 template <int MODE, bool OUTBF, class C>
@@ -413,13 +423,15 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
     constexpr int BJ = BT / 8 / NW;         // 8-row B blocks per wave per step
     constexpr int kDmaPerStep = AJ + BJ;
     constexpr int kStores = DUAL ? FT * FM / 2 : FT * FM;
-    constexpr int kPrefetch = DUAL ? BJ : 2 * FT;
+    constexpr int kPrefetch = DUAL ? 1 : 2 * FT;
     static_assert(MODE == kRoutedGateUp || MODE == kRoutedDown, "routed modes");
     static_assert(AJ * 8 * NW == BW && BJ * 8 * NW == BT, "whole 8-row blocks per wave");
     static_assert(!DUAL || (NW / 2) * AJ * 8 == BW / 2, "a wave's A rows lie in the gate or the up half");
     static_assert(6 + kStores + kPrefetch + kDmaPerStep < 64, "vmcnt range");
     __shared__ __attribute__((aligned(16))) uint16_t lds[NST][STAGE];
     __shared__ int4 items[kPersistMaxItems];
+    // gate/up: pair ids of the item after next, 64 per wave (one DMA per item)
+    __shared__ uint32_t pair_ids[DUAL ? NW * 64 : 1];
 
     const int N = a.N, K = a.K, nk = K / BK;
     const int nrb = (N + ROWS - 1) / ROWS;
@@ -470,6 +482,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
                                                         uint32_t(size_t(a.n_act_rows) * K * 2), kRsrcWord3);
     const auto rs_out = __builtin_amdgcn_make_buffer_rsrc(
         a.out, 0, uint32_t(size_t(a.n_pairs) * N * (OUTBF ? 2 : 4)), kRsrcWord3);
+    const auto rs_pairs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.pairs), 0,
+                                                            uint32_t(a.n_pairs) * 4u, kRsrcWord3);
     // this wave's weight rows of an item (gate/up: gate or up half by wave)
     auto w_rsrc = [&](int4 it) __attribute__((always_inline)) {
         const int r0 = it.w * ROWS;
@@ -566,13 +580,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
     // count of operations in flight
     int4 cur = item_at(0);
     uint32_t xo_cur[BJ], xo_nxt[BJ];
-    int pn[BJ];
     int ep_cur[FT], ep_nxt[FT];
     float es_cur[FT];
+    {
+        const int4 n1 = item_at(min(1, n_mine - 1));
 #pragma unroll
-    for (int j = 0; j < BJ; ++j) {
-        const int v = DUAL ? a.pairs[pair_index(cur, brow[j])] : cur.y + brow[j];
-        xo_cur[j] = x_offset(j, v, brow[j] < cur.z);
+        for (int j = 0; j < BJ; ++j) {
+            const int v = DUAL ? a.pairs[pair_index(cur, brow[j])] : cur.y + brow[j];
+            xo_cur[j] = x_offset(j, v, brow[j] < cur.z);
+            const int v1 = DUAL ? a.pairs[pair_index(n1, brow[j])] : n1.y + brow[j];
+            xo_nxt[j] = x_offset(j, v1, brow[j] < n1.z);
+        }
     }
     if constexpr (!DUAL) {
 #pragma unroll
@@ -589,17 +607,25 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, rs_out, kDropOffset + 16u * i, 0, 0);
     }
     int g = 0;  // global K step: LDS stage g % 3
-    // the next item's token-row offsets are formed at step kx, after a wait
-    // that covers the item-top prefetch (K steps >= 4); with 2 K steps at step 0
-    const int kx = nk >= 4 ? 2 : 0;
 
+    // Token-row offsets are formed one item ahead of their first DMA: the
+    // pair ids of the item after next go into LDS by DMA at an item's top
+    // and are turned into offsets right after the wait that ends its K loop
+    // (which leaves only that loop's newest DMA in flight, so they have
+    // landed; the wave reads only what it loaded itself).  Plain loads there
+    // cost a full memory round trip per item: the compiler drained the
+    // memory counter ahead of each item's K loop when that loop used them,
+    // and at the K loop's end otherwise (its wait model does not count the
+    // LDS DMA).
     for (int m = 0; m < n_mine; ++m) {
         const int4 nxt = item_at(min(m + 1, n_mine - 1));
         const auto rw_nxt = w_rsrc(nxt);
-        // item-top prefetch, kPrefetch loads: the next item's token rows
-        // (gate/up) or store rows (down), and this item's routing weights
-#pragma unroll
-        for (int jj = 0; jj < BJ; ++jj) pn[jj] = DUAL ? a.pairs[pair_index(nxt, brow[jj])] : 0;
+        // item-top prefetch, kPrefetch loads: the pair ids of the item after
+        // next (gate/up: its token rows) or the next item's store rows
+        // (down), and this item's routing weights
+        const int4 nx2 = item_at(min(m + 2, n_mine - 1));
+        if constexpr (DUAL)  // lane l: the pair id of the wave's row l mod 8 BJ (past the end: zero)
+            dma4(rs_pairs, &pair_ids[wave * 64], uint32_t(nx2.y + wave * 8 * BJ + (lane & (8 * BJ - 1))) * 4u);
         if constexpr (!DUAL) {
 #pragma unroll
             for (int jj = 0; jj < FT; ++jj) {
@@ -616,17 +642,16 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
 
         auto run = [&](auto nf_c) __attribute__((always_inline)) {
             auto step = [&](int kt) __attribute__((always_inline)) {
-                if (kt == kx) {
-                    if (nk < 4) vm_wait_lgkm0<0>();
-#pragma unroll
-                    for (int jj = 0; jj < BJ; ++jj)
-                        xo_nxt[jj] = x_offset(jj, DUAL ? pn[jj] : nxt.y + brow[jj], brow[jj] < nxt.z);
-                }
+                // one DMA call with its operands selected element by element:
+                // two calls on the two arrays were merged by the compiler into
+                // one call on a selected array address, which put both arrays
+                // in scratch memory
                 const int st = (g + 2) % NST;
-                if (kt + 2 < nk)
-                    dma(st, rw_cur, xo_cur, kt + 2);
-                else
-                    dma(st, rw_nxt, xo_nxt, kt + 2 - nk);
+                const bool same = kt + 2 < nk;
+                uint32_t xo_s[BJ];
+#pragma unroll
+                for (int jj = 0; jj < BJ; ++jj) xo_s[jj] = same ? xo_cur[jj] : xo_nxt[jj];
+                dma(st, same ? rw_cur : rw_nxt, xo_s, same ? kt + 2 : kt + 2 - nk);
                 compute(g % NST, nf_c);
                 ++g;
             };
@@ -657,6 +682,22 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
         // exactly the two newest steps' DMA may be in flight here; everything
         // older (the prefetch) is complete
         vm_wait_lgkm0<2 * kDmaPerStep>();
+        uint32_t xo_nn[BJ];
+        if constexpr (DUAL) {
+            uint32_t pid[BJ];
+#pragma unroll
+            for (int jj = 0; jj < BJ; ++jj)
+                pid[jj] = ds_read4(lds_byte_addr(&pair_ids[wave * 64]) + 4u * uint32_t(brow[jj] - wave * 8 * BJ));
+            lgkm_wait_all();
+#pragma unroll
+            for (int jj = 0; jj < BJ; ++jj) {
+                tie(pid[jj]);
+                xo_nn[jj] = x_offset(jj, int(pid[jj]), brow[jj] < nx2.z);
+            }
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < BJ; ++jj) xo_nn[jj] = x_offset(jj, nx2.y + brow[jj], brow[jj] < nx2.z);
+        }
 
         // ---- stores: kStores buffer stores per wave, masked ones dropped
         const int begin = cur.y, count = cur.z, row_blk = cur.w;
@@ -704,7 +745,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
         cur = nxt;
         rw_cur = rw_nxt;
 #pragma unroll
-        for (int j = 0; j < BJ; ++j) xo_cur[j] = xo_nxt[j];
+        for (int j = 0; j < BJ; ++j) {
+            xo_cur[j] = xo_nxt[j];
+            xo_nxt[j] = xo_nn[j];
+        }
         if constexpr (!DUAL) {
 #pragma unroll
             for (int j = 0; j < FT; ++j) ep_cur[j] = ep_nxt[j];
