@@ -71,3 +71,17 @@ def test_layer_all_tied_router_hot_experts(dtype, T):
     np.testing.assert_allclose(wts, 0.25, rtol=1e-6)
     err = check_layer(case, out, ids, tokens=_sample(T))
     print(f"{dtype} T={T}: experts 0..3 with {T} pairs each, y_moe normwise error {err:.2e}")
+
+
+@pytest.mark.parametrize("dtype,F", [("bf16", 128), ("bf16", 256), ("bf16", 768), ("bf16", 1024),
+                                     ("u4", 256), ("u4", 768), ("u4", 1024)])
+@pytest.mark.parametrize("T", [3, 16])
+def test_layer_fused_down_combine_every_d_ff(dtype, F, T):
+    """Each d_ff the fused small-T down + combine launch takes (bf16: 128 ..
+    1024; 4-bit: multiples of 256) against the oracle, with one and with
+    several units per wave (T = 16, K = 4 and the shared expert: 80 units,
+    the 4-bit launch's three-units-in-flight schedule)."""
+    base = "qwen_decode" if dtype == "bf16" else "qwen_u4"
+    spec = spec_of(base, n_tokens=T, d_model=256, n_experts=32, top_k=4, d_ff=F, d_ff_shared=F)
+    _, _, _, err = _layer_vs_oracle(make_case(spec))
+    print(f"{dtype} d_ff={F} T={T}: y_moe normwise error {err:.2e}")

@@ -16,9 +16,13 @@
 // 16-byte load instruction reads R whole 128-byte lines.  The waves split the
 // list of units evenly; a wave's partial sum for a token goes to LDS when the
 // token changes and the workgroup adds the waves' partials in wave order.
-// Two units' loads are in flight per wave while the previous one is used.
+// The loads of the next one or two units are in flight per wave while a unit
+// is used.
 #include "moe_device.h"
 #include "moe_kernels.h"
+
+#include <type_traits>
+#include <utility>
 
 namespace moe {
 
@@ -67,8 +71,19 @@ __device__ __forceinline__ float dot_u4_piece(const u32x4& c, float s, float m, 
     return acc;
 }
 
-// J: 16-byte weight loads per lane per unit (bf16: F = 64 J; U4: F = 256 J)
-template <int J, bool U4>
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// J: 16-byte weight loads per lane per unit (bf16: F = 64 J; U4: F = 256 J);
+// NB: units whose loads are in flight per wave
+template <int J, bool U4, int NB>
 __global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombineArgs a) {
     __shared__ float part[kDcWaves][kDcMaxT][kDcR];
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
@@ -188,34 +203,43 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombine
         acc = fmaf(unit_scale(u), p, acc);
     };
 
+    // NB units in flight: NB register slots used in rotation (unrolled, so
+    // every slot index is a constant).  Slot i holds unit u + i at the top of
+    // the loop; step i issues the loads of unit u + i + NB - 1 (clamped: past
+    // the end they re-read the last unit, unused) into the slot that step i - 1
+    // used, then uses unit u + i.
     if constexpr (U4) {
         if (ub < ue) {
-            u32x4 ca[J], cn[J], ha[J][4], hn[J][4];
-            uint32_t sa[J], sn[J];
-            load_u4(ub, ca, sa, ha);
+            u32x4 cq[NB][J], hq[NB][J][4];
+            uint32_t sq[NB][J];
+            static_for<NB - 1>([&](auto ic) { load_u4(min(ub + ic(), ue - 1), cq[ic()], sq[ic()], hq[ic()]); });
             int u = ub;
-            for (; u + 2 <= ue; u += 2) {
-                load_u4(u + 1, cn, sn, hn);
-                use_u4(u, ca, sa, ha);
-                load_u4(min(u + 2, ue - 1), ca, sa, ha);
-                use_u4(u + 1, cn, sn, hn);
+            for (; u + NB <= ue; u += NB) {
+                static_for<NB>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value, nx = (i + NB - 1) % NB;
+                    load_u4(min(u + i + NB - 1, ue - 1), cq[nx], sq[nx], hq[nx]);
+                    use_u4(u + i, cq[i], sq[i], hq[i]);
+                });
             }
-            if (u < ue) use_u4(u, ca, sa, ha);
+            static_for<NB - 1>([&](auto ic) {
+                if (u + ic() < ue) use_u4(u + ic(), cq[ic()], sq[ic()], hq[ic()]);
+            });
             flush();
         }
     } else if (ub < ue) {
-        u32x4 wa[J], ha[J], wn[J], hn[J];
-        load(ub, wa, ha);
+        u32x4 wq[NB][J], hq[NB][J];
+        static_for<NB - 1>([&](auto ic) { load(min(ub + ic(), ue - 1), wq[ic()], hq[ic()]); });
         int u = ub;
-        // two units in flight: the loads of u + 1 (clamped: past the end they
-        // re-read the last unit, unused) are issued before unit u is used
-        for (; u + 2 <= ue; u += 2) {
-            load(u + 1, wn, hn);
-            use(u, wa, ha);
-            load(min(u + 2, ue - 1), wa, ha);
-            use(u + 1, wn, hn);
+        for (; u + NB <= ue; u += NB) {
+            static_for<NB>([&](auto ic) {
+                constexpr int i = decltype(ic)::value, nx = (i + NB - 1) % NB;
+                load(min(u + i + NB - 1, ue - 1), wq[nx], hq[nx]);
+                use(u + i, wq[i], hq[i]);
+            });
         }
-        if (u < ue) use(u, wa, ha);
+        static_for<NB - 1>([&](auto ic) {
+            if (u + ic() < ue) use(u + ic(), wq[ic()], hq[ic()]);
+        });
         flush();
     }
     __syncthreads();
@@ -230,6 +254,15 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombine
         a.out[o] = a.residual[o] + v;
     }
 }
+
+// Units in flight per wave.  Measured at Qwen3.6 shape (d_ff 512): a third
+// unit in flight takes 4-bit T = 64 (40 units per wave) from 145 to 141 us per
+// layer, but costs bf16 layers 1-1.5 us at T = 1, 8 and 32, and 4-bit layers
+// with one or two units per wave about 1 us (its prologue loads the same unit
+// twice).  So three for 4-bit banks whose units fit the registers of two waves
+// per SIMD (5 J 16-byte loads per lane per unit, J <= 3) when a wave has at
+// least 8 units, two otherwise.
+constexpr int kDcDeepUnits = 8;
 
 }  // namespace
 
@@ -247,20 +280,30 @@ hipError_t launch_down_combine(const DownCombineArgs& a, hipStream_t s) {
     if (u4 && (!a.w_scale || !a.w_min || (a.has_shared && (!a.ws_scale || !a.ws_min)))) return hipErrorInvalidValue;
     const dim3 g(unsigned(a.D / kDcR)), b(kDcWaves * 64);
     if (u4) {
+        const bool deep = a.T * (a.K + (a.has_shared ? 1 : 0)) >= kDcDeepUnits * kDcWaves;
         switch (a.F / 256) {
-            case 1: down_combine_kernel<1, true><<<g, b, 0, s>>>(a); break;
-            case 2: down_combine_kernel<2, true><<<g, b, 0, s>>>(a); break;
-            case 3: down_combine_kernel<3, true><<<g, b, 0, s>>>(a); break;
-            default: down_combine_kernel<4, true><<<g, b, 0, s>>>(a); break;
+            case 1:
+                if (deep) down_combine_kernel<1, true, 3><<<g, b, 0, s>>>(a);
+                else down_combine_kernel<1, true, 2><<<g, b, 0, s>>>(a);
+                break;
+            case 2:
+                if (deep) down_combine_kernel<2, true, 3><<<g, b, 0, s>>>(a);
+                else down_combine_kernel<2, true, 2><<<g, b, 0, s>>>(a);
+                break;
+            case 3:
+                if (deep) down_combine_kernel<3, true, 3><<<g, b, 0, s>>>(a);
+                else down_combine_kernel<3, true, 2><<<g, b, 0, s>>>(a);
+                break;
+            default: down_combine_kernel<4, true, 2><<<g, b, 0, s>>>(a); break;
         }
         return hipGetLastError();
     }
     switch (a.F / 64) {
-        case 2: down_combine_kernel<2, false><<<g, b, 0, s>>>(a); break;
-        case 4: down_combine_kernel<4, false><<<g, b, 0, s>>>(a); break;
-        case 8: down_combine_kernel<8, false><<<g, b, 0, s>>>(a); break;
-        case 12: down_combine_kernel<12, false><<<g, b, 0, s>>>(a); break;
-        default: down_combine_kernel<16, false><<<g, b, 0, s>>>(a); break;
+        case 2: down_combine_kernel<2, false, 2><<<g, b, 0, s>>>(a); break;
+        case 4: down_combine_kernel<4, false, 2><<<g, b, 0, s>>>(a); break;
+        case 8: down_combine_kernel<8, false, 2><<<g, b, 0, s>>>(a); break;
+        case 12: down_combine_kernel<12, false, 2><<<g, b, 0, s>>>(a); break;
+        default: down_combine_kernel<16, false, 2><<<g, b, 0, s>>>(a); break;
     }
     return hipGetLastError();
 }
