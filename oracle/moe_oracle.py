@@ -57,7 +57,13 @@ from typing import Optional
 import numpy as np
 
 CLAMP = 2.0 ** -14  # smallest normal fp16, the renormalisation floor ([T] "Routing math")
-TIE_EPS = 1e-4  # near-tie threshold for flagging tokens
+# Near-tie threshold.  A token is flagged when the gap at the selection
+# boundary (k-th against (k+1)-th score, and for the group family the
+# kept/dropped group scores) is below it: the selected set itself is then not
+# fixed at fp32 precision of the logits.  Separately, order_ties marks a gap
+# below it between two adjacent selected slots: the set is fixed, but the two
+# slots (ordered by descending score) can be ranked either way.
+TIE_EPS = 1e-4
 
 
 # ---------------------------------------------------------------- widening
@@ -192,8 +198,17 @@ def _rank_desc(score: np.ndarray) -> np.ndarray:
 class Route:
     ids: np.ndarray  # [T, K] int32, slots by descending selection score
     weights: np.ndarray  # [T, K] float64 routing weights alpha
-    flags: np.ndarray  # [T] bool near-tie
+    flags: np.ndarray  # [T] bool near-tie at the selection boundary
     score: np.ndarray  # [T, E] float64 selection score (p, or sigmoid + bias)
+    order_ties: Optional[np.ndarray] = None  # [T] bool near-tie between adjacent selected slots
+
+
+def order_ties(score: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """[T] bool: some two adjacent selected slots' scores differ by < TIE_EPS."""
+    s = np.take_along_axis(score, ids.astype(np.int64), axis=1)
+    if s.shape[1] < 2:
+        return np.zeros(s.shape[0], dtype=bool)
+    return (s[:, :-1] - s[:, 1:]).min(axis=1) < TIE_EPS
 
 
 def softmax_topk(z: np.ndarray, k: int) -> Route:
@@ -213,7 +228,7 @@ def softmax_topk(z: np.ndarray, k: int) -> Route:
         w[t] = p[t, sel] / denom
         if k < E:
             flags[t] = (p[t, order[k - 1]] - p[t, order[k]]) < TIE_EPS
-    return Route(ids, w, flags, p)
+    return Route(ids, w, flags, p, order_ties(p, ids))
 
 
 def softmax_weights_for(z: np.ndarray, ids: np.ndarray) -> np.ndarray:
@@ -264,7 +279,7 @@ def sigmoid_group_topk(z: np.ndarray, bias: Optional[np.ndarray], k: int, n_grou
         if k < len(cand):
             f |= (sel[t, corder[k - 1]] - sel[t, corder[k]]) < TIE_EPS
         flags[t] = f
-    return Route(ids, w, flags, sel)
+    return Route(ids, w, flags, sel, order_ties(sel, ids))
 
 
 def sigmoid_weights_for(z: np.ndarray, ids: np.ndarray, routed_scaling: float) -> np.ndarray:
@@ -406,7 +421,8 @@ def layer_forward(x: np.ndarray, residual: np.ndarray, w_router: np.ndarray, ban
     r = route(z, family, k, bias, n_group, topk_group, routed_scaling)
     if ids is not None:
         ids_t = np.asarray(ids)[tokens]
-        r = Route(ids_t.astype(np.int32), weights_for(z, ids_t, family, routed_scaling), r.flags, r.score)
+        r = Route(ids_t.astype(np.int32), weights_for(z, ids_t, family, routed_scaling), r.flags, r.score,
+                  order_ties(r.score, ids_t))
     local = np.arange(tokens.size)
     slots = routed_slots(x[tokens], r.ids, r.weights, banks, local)
     ys = shared_expert(x[tokens], banks)

@@ -85,3 +85,18 @@ def test_layer_fused_down_combine_every_d_ff(dtype, F, T):
     spec = spec_of(base, n_tokens=T, d_model=256, n_experts=32, top_k=4, d_ff=F, d_ff_shared=F)
     _, _, _, err = _layer_vs_oracle(make_case(spec))
     print(f"{dtype} d_ff={F} T={T}: y_moe normwise error {err:.2e}")
+
+
+def test_layer_max_tokens_qwen_prefill():
+    """T = 32768 at Qwen3.6 shape with skewed routing (262144 pairs): the
+    routed down projection has 8 row blocks x more than 2048 token tiles of
+    128 pairs, more items than the persistent launch's per-workgroup table
+    holds (8 XCDs x 32 workgroups x 64), so it runs the non-persistent tiled
+    kernel; every token's routing against the oracle, the layer output on
+    sampled tokens."""
+    T = 32768
+    case = make_case(spec_of("qwen_prefill_skew", n_tokens=T))
+    s = case.spec
+    assert 8 * (s.n_tokens * s.top_k // 128) >= 8 * 32 * 64  # down items: past the persistent table
+    ids, wts, flagged, err = _layer_vs_oracle(case)
+    print(f"qwen_prefill_skew T={T}: {flagged} near-tie tokens, y_moe normwise error {err:.2e}")

@@ -170,6 +170,29 @@ def test_all_tie_softmax():
     assert rt.flags.all()
 
 
+def test_order_tie_between_selected_slots():
+    """Two selected experts that tie mark the token's slot order as not fixed
+    (order_ties) without flagging its selected set, whose boundary is wide;
+    neither mark when every gap is wide."""
+    E = 16
+    tied = np.full((1, E), -3.0)
+    tied[0, :3] = [4.0, 2.0, 2.0]
+    wide = tied.copy()
+    wide[0, 1] = 2.5
+    rt = O.softmax_topk(np.concatenate([tied, wide]), 3)
+    np.testing.assert_array_equal(rt.ids, [[0, 1, 2], [0, 1, 2]])
+    assert rt.flags.tolist() == [False, False]
+    assert rt.order_ties.tolist() == [True, False]
+    # sigmoid group family: 2 groups of 8, both kept; experts 0 and 9 tie
+    z = np.full((2, E), -4.0)
+    z[:, 0], z[:, 9], z[:, 5] = 3.0, 3.0, 1.0
+    z[1, 9] = 2.0
+    rs = O.sigmoid_group_topk(z, None, 3, 2, 2, 1.0)
+    np.testing.assert_array_equal(rs.ids, [[0, 9, 5], [0, 9, 5]])
+    assert rs.flags.tolist() == [False, False]
+    assert rs.order_ties.tolist() == [True, False]
+
+
 def _brute_group(z, b, K, G, tg, scale):
     E = z.size
     gs = E // G
