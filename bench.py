@@ -621,6 +621,12 @@ def main():
     }
     if not args.no_chain:
         line["chained_decode"] = chained_decode(args, dec["ms_per_step"] * 1e3)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(dec["insts"][0], args.cpu_seconds)
+    # the decode instances (40 layer copies, about 60 GB) are released before
+    # the prefill workload is built
+    del dec
+    torch.cuda.empty_cache()
     if not args.no_prefill:
         pre = run_workload("qwen_prefill_skew", 4096, 4, max(80, args.steps // 10), max(20, args.warmup // 10),
                            max(8, args.stage_reps // 4))
@@ -636,8 +642,6 @@ def main():
             "roofline": prefill_roofline(pre),
         }
         del pre
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(dec["insts"][0], args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
