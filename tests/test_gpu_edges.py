@@ -100,3 +100,26 @@ def test_layer_max_tokens_qwen_prefill():
     assert 8 * (s.n_tokens * s.top_k // 128) >= 8 * 32 * 64  # down items: past the persistent table
     ids, wts, flagged, err = _layer_vs_oracle(case)
     print(f"qwen_prefill_skew T={T}: {flagged} near-tie tokens, y_moe normwise error {err:.2e}")
+
+
+@pytest.mark.parametrize("G,TG,K,bias,T", [
+    (1, 1, 8, True, 5), (1, 1, 8, True, 300),  # one group: plain sigmoid top-k of score + bias
+    (8, 8, 8, True, 37),  # every group kept
+    (8, 1, 8, True, 37),  # one group kept: all K experts of the best group (groups of 8)
+    (32, 4, 6, True, 37),  # groups of 2: a group's score is the sum of its two experts
+    (8, 4, 8, False, 37), (8, 4, 8, False, 1000),  # no expert_bias, routed_scaling 1
+])
+def test_layer_sigmoid_group_degenerate(G, TG, K, bias, T):
+    """The group top-k family at its degenerate settings, 64 experts, against
+    the oracle (small-T and, at T = 300 / 1000, the medium and tiled paths)."""
+    spec = spec_of("sigmoid_group", n_tokens=T, n_experts=64, n_group=G, topk_group=TG, top_k=K,
+                   bias_var=0.1 if bias else 0.0, routed_scaling=2.5 if bias else 1.0, **SMALL_DIMS)
+    case = make_case(spec, cache_key=("sigmoid_degenerate", G, TG, K, bias))
+    if not bias:  # the NULL expert_bias pointer (the generator draws zeros)
+        case.w.expert_bias = None
+        case.bias64 = None
+    ids, wts, flagged, err = _layer_vs_oracle(case)
+    assert err <= TOL["bf16"]
+    if TG == 1:  # every token's experts lie in one group
+        assert (ids // (64 // G) == ids[:, :1] // (64 // G)).all()
+    print(f"G={G} TG={TG} K={K} bias={bias} T={T}: {flagged} near-tie tokens, y_moe normwise error {err:.2e}")

@@ -344,8 +344,9 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_tiled_kernel(GemmArg
 // first K steps, and the pair ids and routing weights of its stores.  Here
 // one workgroup per CU walks its XCD's run of items (the same weight-
 // stationary order) and hides all of that behind the previous item: the
-// item list is decoded into LDS once, the next item's token rows and store
-// targets are loaded while the current item's K loop runs, and its first two
+// item list is decoded into LDS once, the pair ids that locate token rows
+// (gate/up, two items ahead) and the next item's store targets (down) are
+// loaded while the current item's K loop runs, and the next item's first two
 // K steps are loaded during the current item's last two.  Loads are buffer
 // loads from scalar bases (the weight block, the token matrix) with fixed
 // per-lane offsets, so switching items changes no VGPR address, and the
