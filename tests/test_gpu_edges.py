@@ -123,3 +123,23 @@ def test_layer_sigmoid_group_degenerate(G, TG, K, bias, T):
     if TG == 1:  # every token's experts lie in one group
         assert (ids // (64 // G) == ids[:, :1] // (64 // G)).all()
     print(f"G={G} TG={TG} K={K} bias={bias} T={T}: {flagged} near-tie tokens, y_moe normwise error {err:.2e}")
+
+
+# Token counts on both sides of every switch of the schedule at E=32, K=4:
+# selection folded into the gate/up launch (T <= 8), dense 64-token tiles
+# (T >= 64), the small-T path (T*K <= 256), the tiled router and shared expert
+# (T >= 128), the tiled routed GEMMs (bf16: T*K >= 16 E; 4-bit: >= 64 E) and the
+# chunked permute (T*K >= 4096).
+BOUNDARY_T = [8, 9, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1023, 1024]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "u4"])
+@pytest.mark.parametrize("T", BOUNDARY_T)
+def test_layer_schedule_boundaries(dtype, T):
+    base = "qwen_decode" if dtype == "bf16" else "qwen_u4"
+    spec = spec_of(base, n_tokens=T, d_model=256, n_experts=32, top_k=4, d_ff=128, d_ff_shared=128)
+    case = make_case(spec, cache_key=("boundaries", dtype))
+    out, ids, wts = run_layer(case)
+    z, rt = case.oracle_route()
+    check_route(case, ids, wts, z, rt)
+    check_layer(case, out, ids)
