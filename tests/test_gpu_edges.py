@@ -133,11 +133,12 @@ def test_layer_sigmoid_group_degenerate(G, TG, K, bias, T):
 BOUNDARY_T = [8, 9, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1023, 1024]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "u4"])
+@pytest.mark.parametrize("dtype", ["bf16", "u4", "sigmoid"])
 @pytest.mark.parametrize("T", BOUNDARY_T)
 def test_layer_schedule_boundaries(dtype, T):
-    base = "qwen_decode" if dtype == "bf16" else "qwen_u4"
-    spec = spec_of(base, n_tokens=T, d_model=256, n_experts=32, top_k=4, d_ff=128, d_ff_shared=128)
+    base = {"bf16": "qwen_decode", "u4": "qwen_u4", "sigmoid": "sigmoid_group"}[dtype]
+    extra = dict(n_group=4, topk_group=2) if dtype == "sigmoid" else {}
+    spec = spec_of(base, n_tokens=T, d_model=256, n_experts=32, top_k=4, d_ff=128, d_ff_shared=128, **extra)
     case = make_case(spec, cache_key=("boundaries", dtype))
     out, ids, wts = run_layer(case)
     z, rt = case.oracle_route()
