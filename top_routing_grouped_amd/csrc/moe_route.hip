@@ -12,9 +12,11 @@
 //   contiguous experts scored by the sum of their two best sel, the best
 //   topk_group groups kept, top-K of sel inside them,
 //   alpha = routed_scaling * s_I / max(sum s_I, 2^-14)  (bias excluded).
-// Selection is K rounds of a wave-wide maximum over 64-bit keys
-// (score bits << 32 | ~index), which breaks ties toward the lower index and
-// leaves slot k holding the k-th best expert.
+// Selection is K rounds of a wave-wide maximum, ties toward the lower expert
+// index, leaving slot k with the k-th best expert: for the softmax family
+// over 32-bit order-preserving score keys, the winner being the lowest lane
+// that offers the maximum (lanes hold ascending expert ids); for the group
+// family over 64-bit keys (score bits << 32 | ~index).
 #include "moe_kernels.h"
 #include "moe_select.h"
 

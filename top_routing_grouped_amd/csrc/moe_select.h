@@ -10,8 +10,10 @@
 //     groups of E/n_group contiguous experts scored by the sum of their two
 //     best sel, the best topk_group groups kept, top-K of sel inside them,
 //     alpha = routed_scaling * s_I / max(sum s_I, 2^-14)  (bias excluded).
-// K rounds of a wave-wide maximum over 64-bit keys (score bits << 32 |
-// ~index) break ties toward the lower index and put the k-th best in slot k.
+// K rounds of a wave-wide maximum break ties toward the lower index and put
+// the k-th best in slot k: 32-bit order-preserving score keys plus one ballot
+// for the lowest offering lane in the softmax family (select_softmax_lanes),
+// 64-bit keys (score bits << 32 | ~index) in the group family (select_token).
 //
 // Permute (Treebeard, "Intel SYCL path", steps 1-4): count the pairs per
 // expert, offsets by exclusive scan, active-expert list, stable scatter of
