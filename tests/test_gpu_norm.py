@@ -167,13 +167,12 @@ LAYER_CASES = [("small_bf16", 1), ("small_bf16", 37), ("small_bf16", 301), ("sma
                ("qwen_prefill_skew", 4096)]
 
 
-@pytest.mark.parametrize("name,T", LAYER_CASES)
-def test_layer_forward_norm_matches_oracle(name, T):
-    spec = _spec(name, T)
-    case = make_case(spec)
-    r, w = make_attention_residual(spec, "cuda")
-    r = _special_rows(r, huge=False)
-    out, ids, wts, x = run_layer_norm(case, r, w)
+def check_layer_from_residual(case, r, w, out, ids, wts, x, tag):
+    """The layer entry's x, routing and output against the oracle run from
+    residual r (see the module docstring for the rounding-band allowances)."""
+    spec = case.spec
+    T = spec.n_tokens
+    name = tag
     r64, w64 = widen_tensor(r), widen_tensor(w)
     delta = check_normed_x(x, r64, w64, EPS, spec.act_dtype)
     x_or = O.normed_activation(r64, w64, EPS, spec.act_dtype)
@@ -202,8 +201,49 @@ def test_layer_forward_norm_matches_oracle(name, T):
     err = check_layer(ocase, out, ids, tokens=toks)
     print(f"{name} T={T}: y_moe normwise error {err:.2e} (gate {TOL[spec.expert_dtype]}); "
           f"{int((dz > 0).sum())} sampled tokens with x inside a rounding band")
+    return err
+
+
+@pytest.mark.parametrize("name,T", LAYER_CASES)
+def test_layer_forward_norm_matches_oracle(name, T):
+    spec = _spec(name, T)
+    case = make_case(spec)
+    r, w = make_attention_residual(spec, "cuda")
+    r = _special_rows(r, huge=False)
+    out, ids, wts, x = run_layer_norm(case, r, w)
+    check_layer_from_residual(case, r, w, out, ids, wts, x, name)
     if T >= 2:  # the zero row: x = 0, every projection 0, out = residual + y(0) = 0
         assert np.all(out[0] == 0.0)
+
+
+@pytest.mark.parametrize("name,T", [("small_bf16", 37), ("small_u4", 8), ("small_sigmoid", 301),
+                                    ("qwen_decode", 8)])
+def test_chained_layers_match_oracle_layer_by_layer(name, T):
+    """Three layers chained as a decoder stack runs them: one workspace, the
+    output written over the residual it was computed from, each layer with its
+    own RMS-norm weight.  Each layer is checked against the oracle run from
+    the residual the GPU fed it (the previous layer's GPU output)."""
+    spec = _spec(name, T)
+    case = make_case(spec)
+    cfg = moe.config_from_spec(spec)
+    ws = moe.alloc_workspace(cfg)
+    wstruct = moe.weights_struct(case.w)
+    res, _ = make_attention_residual(spec, "cuda")
+    ids = torch.empty((T, spec.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, spec.top_k), dtype=torch.float32, device="cuda")
+    x = torch.empty((T, spec.d_model), device="cuda",
+                    dtype=torch.float32 if spec.act_dtype == "f32" else torch.bfloat16)
+    stream, aux = torch.cuda.Stream(), torch.cuda.Stream()
+    for layer in range(3):
+        _, nw = make_attention_residual(spec, "cuda", weight_seed=4242 + layer)
+        r_in = res.clone()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            moe.layer_forward_norm(cfg, wstruct, nw, EPS, res, res, x_out=x, ids_out=ids, weights_out=wts,
+                                   ws=ws, stream=stream, aux_stream=aux)
+        torch.cuda.synchronize()
+        check_layer_from_residual(case, r_in, nw, res.cpu().numpy(), ids.cpu().numpy(), wts.cpu().numpy(), x,
+                                  f"{name} layer {layer}")
 
 
 @pytest.mark.parametrize("name,T", [("qwen_decode", 1), ("qwen_decode", 8), ("qwen_decode", 32), ("small_bf16", 37),
