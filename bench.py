@@ -103,9 +103,12 @@ def layer_flops(spec):
 
 
 def shared_in_routed_launch(spec):
-    """Small T*K: the library runs the shared expert inside the routed launches."""
+    """Small T*K: the library runs the shared expert inside the routed launches
+    (its small-T path: T*K <= 256 pairs and fewer than 16 pairs per expert on
+    average for bf16 banks, 64 for 4-bit and fp32 banks)."""
     T, K, E = spec.n_tokens, spec.top_k, spec.n_experts
-    return T * K <= 256 and T * K < 64 * E and spec.d_ff_shared > 0
+    per_expert = 16 if spec.expert_dtype == "bf16" else 64
+    return T * K <= 256 and T * K < per_expert * E and spec.d_ff_shared > 0
 
 
 def gateup_bytes(spec, n_active):
