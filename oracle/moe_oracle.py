@@ -22,7 +22,7 @@ Sources (page titles and sections; the pages print no code we follow):
        expert_bias, n_group, topk_group, routed_scaling), tier table
        ("4-bit affine, group 64").
 
-Readings where the pages are silent (each is also listed in the design doc):
+Readings where the pages are silent:
   * selection ties go to the lowest expert index (groups: lowest group
     index); slots are ordered by descending score;
   * the sigmoid family uses the same max(sum, 2^-14) guard as the softmax
