@@ -46,8 +46,12 @@ Readings where the pages are silent:
 Pins: every function here is pinned by tests/test_oracle_pins.py against
 closed forms, hand-derived fixtures (tests/golden/), brute force on tiny
 inputs, invariants the pages state, and library routines for the special
-cases that reduce to them.  The numeric value of a full layer at model shape
-has no printed worked example on the pages; it rests on those pins.
+cases that reduce to them.  That includes the weights of given selections
+(softmax_weights_for, sigmoid_weights_for) and the layer run on given ids in
+both routing families (hand-derived values in tests/golden/), and the lazy,
+per-expert widening of the banks in oracle/inputs.py (equal to the eager
+widening).  The numeric value of a full layer at model shape has no printed
+worked example on the pages; it rests on those pins.
 """
 from __future__ import annotations
 
@@ -60,9 +64,7 @@ CLAMP = 2.0 ** -14  # smallest normal fp16, the renormalisation floor ([T] "Rout
 # Near-tie threshold.  A token is flagged when the gap at the selection
 # boundary (k-th against (k+1)-th score, and for the group family the
 # kept/dropped group scores) is below it: the selected set itself is then not
-# fixed at fp32 precision of the logits.  Separately, order_ties marks a gap
-# below it between two adjacent selected slots: the set is fixed, but the two
-# slots (ordered by descending score) can be ranked either way.
+# fixed at fp32 precision of the logits.
 TIE_EPS = 1e-4
 
 
@@ -200,15 +202,6 @@ class Route:
     weights: np.ndarray  # [T, K] float64 routing weights alpha
     flags: np.ndarray  # [T] bool near-tie at the selection boundary
     score: np.ndarray  # [T, E] float64 selection score (p, or sigmoid + bias)
-    order_ties: Optional[np.ndarray] = None  # [T] bool near-tie between adjacent selected slots
-
-
-def order_ties(score: np.ndarray, ids: np.ndarray) -> np.ndarray:
-    """[T] bool: some two adjacent selected slots' scores differ by < TIE_EPS."""
-    s = np.take_along_axis(score, ids.astype(np.int64), axis=1)
-    if s.shape[1] < 2:
-        return np.zeros(s.shape[0], dtype=bool)
-    return (s[:, :-1] - s[:, 1:]).min(axis=1) < TIE_EPS
 
 
 def softmax_topk(z: np.ndarray, k: int) -> Route:
@@ -228,7 +221,7 @@ def softmax_topk(z: np.ndarray, k: int) -> Route:
         w[t] = p[t, sel] / denom
         if k < E:
             flags[t] = (p[t, order[k - 1]] - p[t, order[k]]) < TIE_EPS
-    return Route(ids, w, flags, p, order_ties(p, ids))
+    return Route(ids, w, flags, p)
 
 
 def softmax_weights_for(z: np.ndarray, ids: np.ndarray) -> np.ndarray:
@@ -279,10 +272,14 @@ def sigmoid_group_topk(z: np.ndarray, bias: Optional[np.ndarray], k: int, n_grou
         if k < len(cand):
             f |= (sel[t, corder[k - 1]] - sel[t, corder[k]]) < TIE_EPS
         flags[t] = f
-    return Route(ids, w, flags, sel, order_ties(sel, ids))
+    return Route(ids, w, flags, sel)
 
 
 def sigmoid_weights_for(z: np.ndarray, ids: np.ndarray, routed_scaling: float) -> np.ndarray:
+    """Weights of given (possibly non-oracle) selections in the sigmoid group
+    family ([E] "Sigmoid group top-k", steps 4-5): the raw sigmoid scores of
+    the selected experts (bias excluded), renormalised with the 2^-14 floor,
+    times routed_scaling."""
     s = np.take_along_axis(sigmoid(z), ids.astype(np.int64), axis=1)
     return routed_scaling * s / np.maximum(s.sum(axis=1, keepdims=True), CLAMP)
 
@@ -421,8 +418,7 @@ def layer_forward(x: np.ndarray, residual: np.ndarray, w_router: np.ndarray, ban
     r = route(z, family, k, bias, n_group, topk_group, routed_scaling)
     if ids is not None:
         ids_t = np.asarray(ids)[tokens]
-        r = Route(ids_t.astype(np.int32), weights_for(z, ids_t, family, routed_scaling), r.flags, r.score,
-                  order_ties(r.score, ids_t))
+        r = Route(ids_t.astype(np.int32), weights_for(z, ids_t, family, routed_scaling), r.flags, r.score)
     local = np.arange(tokens.size)
     slots = routed_slots(x[tokens], r.ids, r.weights, banks, local)
     ys = shared_expert(x[tokens], banks)
@@ -430,33 +426,38 @@ def layer_forward(x: np.ndarray, residual: np.ndarray, w_router: np.ndarray, ban
     return LayerResult(out, out - residual[tokens], slots, ys, r, z, tokens)
 
 
-def layer_forward_loop(x: np.ndarray, residual: np.ndarray, w_router: np.ndarray, banks: Banks,
-                       family: str, k: int, bias=None, n_group=1, topk_group=1,
-                       routed_scaling=1.0) -> np.ndarray:
-    """The same layer as a per-token, per-slot loop of matrix-vector products
-    (the conceptual loop of [T] "Pseudocode"); an independent formulation of
-    layer_forward's grouped matmuls, for small inputs."""
+def layer_forward_dense(x: np.ndarray, residual: np.ndarray, w_router: np.ndarray, banks: Banks,
+                        family: str, k: int, bias=None, n_group=1, topk_group=1,
+                        routed_scaling=1.0) -> np.ndarray:
+    """The same layer as a dense mixture over all E experts: every expert runs
+    on every token, and a [T, E] weight matrix that is zero off each token's
+    selection contracts their outputs ([T] "Routing math": the routing weights
+    of unselected experts are zero; "Routed expert computation": y_routed is
+    the weighted sum of expert outputs; "Shared expert computation": the gated
+    shared branch and the residual sum).  It shares neither the gathering by
+    expert nor the (token, slot) write-back with layer_forward, and costs E/K
+    times its expert work: for small inputs."""
     T, D = x.shape
-    out = np.zeros_like(residual)
+    E = w_router.shape[0]
+    z = x @ w_router.T
+    rt = route(z, family, k, bias, n_group, topk_group, routed_scaling)
+    A = np.zeros((T, E))
     for t in range(T):
-        xt = x[t]
-        zt = np.array([np.dot(w_router[e], xt) for e in range(w_router.shape[0])])
-        rt = route(zt[None, :], family, k, bias, n_group, topk_group, routed_scaling)
-        routed = np.zeros(D)
-        for slot in range(k):
-            wg, wu, wd = banks.expert(int(rt.ids[0, slot]))
-            g = np.array([np.dot(wg[f], xt) for f in range(wg.shape[0])])
-            u = np.array([np.dot(wu[f], xt) for f in range(wu.shape[0])])
-            h = np.array([gi / (1.0 + np.exp(-gi)) * ui for gi, ui in zip(g, u)])
-            e_out = np.array([np.dot(wd[d], h) for d in range(D)])
-            routed = routed + rt.weights[0, slot] * e_out
-        shared = np.zeros(D)
-        if banks.shared_gate is not None:
-            g = banks.shared_gate @ xt
-            u = banks.shared_up @ xt
-            h = g / (1.0 + np.exp(-g)) * u
-            shared = banks.shared_down @ h
-            if banks.shared_gate_vec is not None:
-                shared = shared / (1.0 + np.exp(-np.dot(banks.shared_gate_vec, xt)))
-        out[t] = residual[t] + (routed + shared)
-    return out
+        A[t, rt.ids[t]] = rt.weights[t]
+    mats = [banks.expert(e) for e in range(E)]
+    Wg = np.stack([m[0] for m in mats])  # [E, F, D]
+    Wu = np.stack([m[1] for m in mats])
+    Wd = np.stack([m[2] for m in mats])  # [E, D, F]
+    G = np.einsum("td,efd->tef", x, Wg)
+    U = np.einsum("td,efd->tef", x, Wu)
+    H = G / (1.0 + np.exp(-G)) * U
+    Y = np.einsum("tef,edf->ted", H, Wd)  # every expert's output for every token
+    y_routed = np.einsum("te,ted->td", A, Y)
+    y_shared = np.zeros((T, D))
+    if banks.shared_gate is not None:
+        gs = x @ banks.shared_gate.T
+        us = x @ banks.shared_up.T
+        y_shared = (gs / (1.0 + np.exp(-gs)) * us) @ banks.shared_down.T
+        if banks.shared_gate_vec is not None:
+            y_shared = y_shared / (1.0 + np.exp(-(x @ banks.shared_gate_vec)))[:, None]
+    return residual + (y_routed + y_shared)

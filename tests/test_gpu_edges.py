@@ -8,25 +8,20 @@ pairs (one expert spanning many GEMM tiles)."""
 import numpy as np
 import pytest
 
-from tests.gpu_harness import TOL, check_layer, check_route, make_case, run_layer, spec_of
+from tests.gpu_harness import TOL, check_layer, check_route, compare_tokens, make_case, run_layer, spec_of
 
 pytestmark = pytest.mark.gpu
 
 SMALL_DIMS = dict(d_model=256, d_ff=128, d_ff_shared=128)
 
 
-def _sample(T, seed=0, n=48):
-    if T <= 64:
-        return np.arange(T)
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, n - 2, replace=False)]))
-
-
 def _layer_vs_oracle(case):
     out, ids, wts = run_layer(case)
     z, rt = case.oracle_route()
-    flagged = check_route(case, ids, wts, z, rt)
-    err = check_layer(case, out, ids, tokens=_sample(case.spec.n_tokens))
+    flagged, _ = check_route(case, ids, wts, z, rt)
+    toks = compare_tokens(case, ids)
+    err = check_layer(case, out, ids, tokens=toks)
+    print(f"layer output compared on {toks.size} of {case.spec.n_tokens} tokens")
     return ids, wts, flagged, err
 
 
@@ -69,7 +64,7 @@ def test_layer_all_tied_router_hot_experts(dtype, T):
     out, ids, wts = run_layer(case)
     assert (ids == np.arange(4)[None]).all()  # all logits equal: the lowest indices win
     np.testing.assert_allclose(wts, 0.25, rtol=1e-6)
-    err = check_layer(case, out, ids, tokens=_sample(T))
+    err = check_layer(case, out, ids, tokens=compare_tokens(case, ids))
     print(f"{dtype} T={T}: experts 0..3 with {T} pairs each, y_moe normwise error {err:.2e}")
 
 
@@ -93,7 +88,8 @@ def test_layer_max_tokens_qwen_prefill():
     128 pairs, more items than the persistent launch's per-workgroup table
     holds (8 XCDs x 32 workgroups x 64), so it runs the non-persistent tiled
     kernel; every token's routing against the oracle, the layer output on
-    sampled tokens."""
+    the first and last pair of every 128-pair token tile of every active
+    expert (so every GEMM work item) plus random tokens."""
     T = 32768
     case = make_case(spec_of("qwen_prefill_skew", n_tokens=T))
     s = case.spec

@@ -28,7 +28,8 @@ import torch
 from oracle import moe_oracle as O
 from oracle.inputs import to_numpy, widen_tensor
 from synth import make_attention_residual
-from tests.gpu_harness import (TOL, check_layer, make_case, normwise_err, spec_of, valid_selection, WEIGHT_RTOL)
+from tests.gpu_harness import (TOL, check_layer, compare_tokens, logit_error_bound, make_case, normwise_err,
+                               score_interval, spec_of, valid_selection, _order_consistent, WEIGHT_RTOL)
 from top_routing_grouped_amd import moe
 
 pytestmark = pytest.mark.gpu
@@ -155,13 +156,6 @@ def run_layer_norm(case, r, w, eps=EPS, x_out=True, aux=True, out_alias=False):
     return out.cpu().numpy(), ids.cpu().numpy(), wts.cpu().numpy(), x
 
 
-def _sample(T, seed=0, n=48):
-    if T <= 64:
-        return np.arange(T)
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, n - 3, replace=False)]))
-
-
 LAYER_CASES = [("small_bf16", 1), ("small_bf16", 37), ("small_bf16", 301), ("small_f32", 37), ("small_f32", 700),
                ("small_u4", 37), ("small_sigmoid", 37), ("qwen_decode", 8), ("qwen_decode", 32),
                ("qwen_prefill_skew", 4096)]
@@ -180,16 +174,22 @@ def check_layer_from_residual(case, r, w, out, ids, wts, x, tag):
 
     # routing: ids exact on tokens away from near-ties; weights within the
     # change that the x band can make
-    toks = _sample(T)
+    toks = compare_tokens(ocase, ids)
     z = O.router_logits(x_or[toks], case.wr64)
     rt = O.route(z, spec.family, spec.top_k, case.bias64, spec.n_group, spec.topk_group, spec.routed_scaling)
     dz = delta[toks] @ np.abs(case.wr64).max(axis=0)
     wtol = WEIGHT_RTOL + 2.0 * dz * (1 + 1e-3)
     g_ids, g_wts = ids[toks], wts[toks]
     differ = (g_ids != rt.ids).any(axis=1)
-    strict = ~rt.flags & ~rt.order_ties & (dz == 0)
-    assert not (differ & strict).any(), f"tokens {toks[differ & strict][:5]} differ with no near-tie or x band"
-    for i in np.flatnonzero(differ):
+    strict = ~rt.flags & (dz == 0)
+    # away from near-ties and x bands: the set exact, the slot order one that
+    # fp32 logit error can give
+    dzb = logit_error_bound(spec, x_or[toks], case.wr64)
+    for i in np.flatnonzero(differ & strict):
+        assert sorted(g_ids[i]) == sorted(rt.ids[i]), f"token {toks[i]}: {g_ids[i]} vs {rt.ids[i]}, no near-tie"
+        lo, hi = score_interval(spec, z[i], dzb[i], case.bias64)
+        assert _order_consistent(lo, hi, g_ids[i]), f"token {toks[i]}: slot order {g_ids[i]} vs {rt.ids[i]}"
+    for i in np.flatnonzero(differ & ~strict):
         # a score moves by at most p * (e^(2 dz) - 1) (softmax) or dz / 4 per
         # sigmoid, twice that for a group score
         widen = 2.1 * dz[i] * rt.score[i].max() if spec.family == "softmax" else 0.5 * dz[i]
@@ -199,8 +199,8 @@ def check_layer_from_residual(case, r, w, out, ids, wts, x, tag):
     rel = np.abs(g_wts - rt.weights) / np.abs(rt.weights)
     assert np.all(rel[same].max(axis=1, initial=0) <= wtol[same]), f"weights rel err {rel[same].max():.3e}"
     err = check_layer(ocase, out, ids, tokens=toks)
-    print(f"{name} T={T}: y_moe normwise error {err:.2e} (gate {TOL[spec.expert_dtype]}); "
-          f"{int((dz > 0).sum())} sampled tokens with x inside a rounding band")
+    print(f"{name} T={T}: y_moe normwise error {err:.2e} (gate {TOL[spec.expert_dtype]}) over {toks.size} tokens; "
+          f"{int((dz > 0).sum())} with x inside a rounding band, {int((differ & strict).sum())} order-relaxed")
     return err
 
 

@@ -65,9 +65,9 @@ def test_golden_softmax_layer_by_hand():
     np.testing.assert_array_equal(res.route.ids, np.array(g["expected_ids"]))
     np.testing.assert_allclose(res.route.weights, _arr(g["expected_weights"]), rtol=0, atol=1e-15)
     np.testing.assert_allclose(res.out, _arr(g["expected_out"]), rtol=0, atol=1e-12)
-    # the per-token loop formulation reproduces the same hand values
-    loop = O.layer_forward_loop(x, r, _arr(g["router"]), banks, "softmax", g["shape"]["K"])
-    np.testing.assert_allclose(loop, _arr(g["expected_out"]), rtol=0, atol=1e-12)
+    # the dense-mixture formulation reproduces the same hand values
+    dense = O.layer_forward_dense(x, r, _arr(g["router"]), banks, "softmax", g["shape"]["K"])
+    np.testing.assert_allclose(dense, _arr(g["expected_out"]), rtol=0, atol=1e-12)
 
 
 def test_golden_sigmoid_group_by_hand():
@@ -85,6 +85,103 @@ def test_golden_sigmoid_group_by_hand():
     members = np.arange(kept * 2, kept * 2 + 2)
     alt = members[np.argsort(-sel[0, members], kind="stable")][: sh["K"]]
     assert list(alt) == g["top1_group_rule_ids_token0"] != list(rt.ids[0])
+
+
+def _sigmoid_layer_fixture():
+    g = _load("sigmoid_group_layer_hand.json")
+    sh = g["shape"]
+    banks = O.Banks(_arr(g["gate"]), _arr(g["up"]), _arr(g["down"]), _arr(g["shared_gate"]), _arr(g["shared_up"]),
+                    _arr(g["shared_down"]), None)
+    args = dict(bias=_arr(g["expert_bias"]), n_group=sh["n_group"], topk_group=sh["topk_group"],
+                routed_scaling=sh["routed_scaling"])
+    return g, sh, banks, args
+
+
+def test_golden_sigmoid_group_layer_by_hand():
+    g, sh, banks, args = _sigmoid_layer_fixture()
+    x, r, wr = _arr(g["x"]), _arr(g["residual"]), _arr(g["router"])
+    res = O.layer_forward(x, r, wr, banks, "sigmoid_group", sh["K"], **args)
+    np.testing.assert_array_equal(res.route.ids, np.array(g["expected_ids"]))
+    np.testing.assert_allclose(res.route.weights, _arr(g["expected_weights"]), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(res.out, _arr(g["expected_out"]), rtol=0, atol=1e-12)
+    dense = O.layer_forward_dense(x, r, wr, banks, "sigmoid_group", sh["K"], **args)
+    np.testing.assert_allclose(dense, _arr(g["expected_out"]), rtol=0, atol=1e-12)
+
+
+def test_golden_sigmoid_group_layer_given_ids_by_hand():
+    """The layer on given selections (one token's set is not the rule's
+    choice, the other's slots are swapped): weights from the raw sigmoid
+    scores of the given set times routed_scaling, outputs by hand."""
+    g, sh, banks, args = _sigmoid_layer_fixture()
+    x, r, wr = _arr(g["x"]), _arr(g["residual"]), _arr(g["router"])
+    given = np.array(g["given_ids"])
+    res = O.layer_forward(x, r, wr, banks, "sigmoid_group", sh["K"], ids=given, **args)
+    np.testing.assert_array_equal(res.route.ids, given)
+    np.testing.assert_allclose(res.route.weights, _arr(g["given_weights"]), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(res.out, _arr(g["given_out"]), rtol=0, atol=1e-12)
+    z = O.router_logits(x, wr)
+    np.testing.assert_allclose(O.sigmoid_weights_for(z, given, sh["routed_scaling"]), _arr(g["given_weights"]),
+                               rtol=0, atol=1e-15)
+    # negative controls: the biased score, or no routed_scaling, give other weights
+    s_sel = np.take_along_axis(O.sigmoid(z), given, axis=1)
+    b_sel = args["bias"][given]
+    by_sel = 2.5 * (s_sel + b_sel) / (s_sel + b_sel).sum(axis=1, keepdims=True)
+    unscaled = s_sel / s_sel.sum(axis=1, keepdims=True)
+    for wrong in (by_sel, unscaled):
+        assert np.abs(wrong - _arr(g["given_weights"])).max() > 0.05
+
+
+def test_sigmoid_weights_for_equals_the_rule_on_its_own_selection():
+    rng = np.random.default_rng(31)
+    for E, G, tg, K, scale in [(128, 8, 4, 8, 2.5), (32, 4, 2, 4, 1.0), (16, 1, 1, 3, 0.7)]:
+        z = rng.standard_normal((60, E)) * 1.5
+        b = rng.standard_normal(E) * 0.3
+        rt = O.sigmoid_group_topk(z, b, K, G, tg, scale)
+        np.testing.assert_allclose(O.sigmoid_weights_for(z, rt.ids, scale), rt.weights, rtol=1e-15, atol=0)
+        np.testing.assert_allclose(O.weights_for(z, rt.ids, "sigmoid_group", scale), rt.weights, rtol=1e-15, atol=0)
+        # slot order follows the given ids
+        rev = rt.ids[:, ::-1]
+        np.testing.assert_allclose(O.sigmoid_weights_for(z, rev, scale), rt.weights[:, ::-1], rtol=1e-15, atol=0)
+
+
+def test_sigmoid_given_ids_layer_reproduces_the_unforced_layer():
+    rng = np.random.default_rng(32)
+    x, r, wr, banks = _rand_layer(rng, 10, 32, 16, 4, 16, 16, gated=False)
+    kw = dict(bias=rng.standard_normal(16) * 0.3, n_group=4, topk_group=2, routed_scaling=2.5)
+    full = O.layer_forward(x, r, wr, banks, "sigmoid_group", 4, **kw)
+    again = O.layer_forward(x, r, wr, banks, "sigmoid_group", 4, ids=full.route.ids, **kw)
+    np.testing.assert_array_equal(again.route.ids, full.route.ids)
+    np.testing.assert_allclose(again.route.weights, full.route.weights, rtol=1e-15, atol=0)
+    np.testing.assert_allclose(again.out, full.out, rtol=0, atol=1e-14)
+    # swapped slot order: the same sum up to fp64 rounding
+    swapped = O.layer_forward(x, r, wr, banks, "sigmoid_group", 4, ids=full.route.ids[:, ::-1], **kw)
+    np.testing.assert_allclose(swapped.out, full.out, rtol=0, atol=1e-13)
+    sub = np.array([7, 2])
+    part = O.layer_forward(x, r, wr, banks, "sigmoid_group", 4, tokens=sub, ids=full.route.ids, **kw)
+    np.testing.assert_allclose(part.out, full.out[sub], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "u4", "f32"])
+def test_lazy_banks_equal_eager_widening(dtype):
+    """The per-expert (lazy) widening the full-shape tests use returns exactly
+    the eager widening's slice for every expert and matrix; bf16 also equals
+    torch's own bf16 -> float64 conversion."""
+    import dataclasses
+    from oracle.inputs import banks_from
+    from synth import WORKLOADS, make_weights
+    base = {"bf16": "qwen_decode", "u4": "qwen_u4", "f32": "tiny_f32"}[dtype]
+    spec = dataclasses.replace(WORKLOADS[base], d_model=128, n_experts=16, d_ff=64, d_ff_shared=64, top_k=4)
+    w = make_weights(spec)
+    eager, lazy = banks_from(w), banks_from(w, lazy=True)
+    assert callable(lazy.gate) and not callable(eager.gate)
+    for e in range(spec.n_experts):
+        for a, b in zip(eager.expert(e), lazy.expert(e)):
+            np.testing.assert_array_equal(a, b)
+    if dtype == "bf16":
+        np.testing.assert_array_equal(eager.gate, w.gate.w.double().numpy())
+        np.testing.assert_array_equal(lazy.expert(5)[2], w.down.w[5].double().numpy())
+    for name in ("shared_gate", "shared_up", "shared_down"):
+        np.testing.assert_array_equal(getattr(eager, name), getattr(lazy, name))
 
 
 def test_golden_u4_dequant_by_hand():
@@ -168,29 +265,6 @@ def test_all_tie_softmax():
     np.testing.assert_array_equal(rt.ids, np.tile(np.arange(8), (3, 1)))
     np.testing.assert_array_equal(rt.weights, np.full((3, 8), 1 / 8))
     assert rt.flags.all()
-
-
-def test_order_tie_between_selected_slots():
-    """Two selected experts that tie mark the token's slot order as not fixed
-    (order_ties) without flagging its selected set, whose boundary is wide;
-    neither mark when every gap is wide."""
-    E = 16
-    tied = np.full((1, E), -3.0)
-    tied[0, :3] = [4.0, 2.0, 2.0]
-    wide = tied.copy()
-    wide[0, 1] = 2.5
-    rt = O.softmax_topk(np.concatenate([tied, wide]), 3)
-    np.testing.assert_array_equal(rt.ids, [[0, 1, 2], [0, 1, 2]])
-    assert rt.flags.tolist() == [False, False]
-    assert rt.order_ties.tolist() == [True, False]
-    # sigmoid group family: 2 groups of 8, both kept; experts 0 and 9 tie
-    z = np.full((2, E), -4.0)
-    z[:, 0], z[:, 9], z[:, 5] = 3.0, 3.0, 1.0
-    z[1, 9] = 2.0
-    rs = O.sigmoid_group_topk(z, None, 3, 2, 2, 1.0)
-    np.testing.assert_array_equal(rs.ids, [[0, 9, 5], [0, 9, 5]])
-    assert rs.flags.tolist() == [False, False]
-    assert rs.order_ties.tolist() == [True, False]
 
 
 def _brute_group(z, b, K, G, tg, scale):
@@ -328,14 +402,14 @@ def test_zero_gate_vector_halves_shared_expert():
     np.testing.assert_array_equal(ys, 0.5 * O.shared_expert(x, banks))
 
 
-def test_grouped_and_loop_formulations_agree():
+def test_grouped_and_dense_formulations_agree():
     rng = np.random.default_rng(24)
     x, r, wr, banks = _rand_layer(rng, 9, 64, 16, 4, 32, 32)
     for fam, kw in [("softmax", {}), ("sigmoid_group",
                                        dict(bias=rng.standard_normal(16) * 0.3, n_group=4, topk_group=2,
                                             routed_scaling=2.5))]:
         a = O.layer_forward(x, r, wr, banks, fam, 4, **kw).out
-        b = O.layer_forward_loop(x, r, wr, banks, fam, 4, **kw)
+        b = O.layer_forward_dense(x, r, wr, banks, fam, 4, **kw)
         np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
 
 
