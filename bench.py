@@ -139,11 +139,31 @@ def build_instances(spec, L, log_prefix):
     return insts
 
 
-def time_layer(insts, steps, warmup):
-    """ms per layer forward.  The L instances' forwards are captured in order
-    into one graph (a chain of L layers, as a decoder stack would launch
-    them) plus one single-layer graph per instance for a remainder, so that
-    exactly `steps` forwards run in the timed region."""
+def chain_length(steps, L):
+    """Layers per captured chain: the largest divisor of `steps` not above L,
+    so that exactly `steps` forwards run as whole chains."""
+    return max(d for d in range(1, min(L, steps) + 1) if steps % d == 0)
+
+
+def capture_chain(insts, aux, cap):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for inst in insts:
+            inst.forward(aux)
+    return g
+
+
+def time_layer(insts, steps, warmup, protocol_chains=20):
+    """Per-layer time of the layer forward, measured two ways.
+
+    Timed region: exactly `steps` forwards, run as whole captured chains of
+    Lc = chain_length(steps, L) distinct instances (a decoder stack's launch
+    pattern) after at least 5 warm-up chains (or `warmup` forwards, whichever
+    is more), bracketed by synchronisation and HIP events.  Protocol
+    measurement (outside the timed region): `protocol_chains` replays of the
+    chain of all L instances, each timed alone; the median is reported.
+    Replays of both graphs are first checked bit for bit against the eager
+    forwards."""
     aux = torch.cuda.Stream()
     # eager warm-up (creates the library's fork/join events), then capture
     for inst in insts:
@@ -151,54 +171,55 @@ def time_layer(insts, steps, warmup):
     torch.cuda.synchronize()
     ref_out = [inst.out.clone() for inst in insts]
     cap = torch.cuda.Stream()
-    for inst in insts:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
-            inst.forward(aux)
-        inst.graph = g
-    chain = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(chain, stream=cap):
-        for inst in insts:
-            inst.forward(aux)
+    L = len(insts)
+    Lc = chain_length(steps, L)
+    full = capture_chain(insts, aux, cap)
+    part = full if Lc == L else capture_chain(insts[:Lc], aux, cap)
+    for inst in insts:  # single-layer graphs for the isolated and cold latencies
+        inst.graph = capture_chain([inst], aux, cap)
     torch.cuda.synchronize()
-    # captured forwards must reproduce the eager results bit for bit, replay after replay
-    for rep in range(3):
+    for g, n in ((full, L), (part, Lc), (full, L)):
         for inst in insts:
             inst.out.fill_(float("nan"))
-        (chain if rep % 2 else insts[0].graph).replay()
+        g.replay()
         torch.cuda.synchronize()
-        check = insts if rep % 2 else insts[:1]
-        for inst, ref in zip(check, ref_out):
+        for inst, ref in zip(insts[:n], ref_out):
             if not torch.equal(inst.out.view(torch.int32), ref.view(torch.int32)):
                 raise RuntimeError("graph replay differs from the eager forward")
-    L = len(insts)
-    for i in range(max(1, warmup // L)):
-        chain.replay()
+    for _ in range(max(5, -(-warmup // Lc))):
+        part.replay()
     torch.cuda.synchronize()
-    n_chain = steps // L
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_chain + 2)]
+    n_chain = steps // Lc
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(n_chain):
+        part.replay()
+    end.record()
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end) / steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(protocol_chains + 1)]
     evs[0].record()
-    for c in range(n_chain):
-        chain.replay()
+    for c in range(protocol_chains):
+        full.replay()
         evs[c + 1].record()
-    for i in range(steps % L):
-        insts[i].graph.replay()
-    evs[-1].record()
     torch.cuda.synchronize()
-    total = evs[0].elapsed_time(evs[-1]) / steps
-    per_chain = sorted(evs[c].elapsed_time(evs[c + 1]) / L for c in range(n_chain))
-    median = per_chain[len(per_chain) // 2] if per_chain else total
-    return total, median
+    per_chain = sorted(evs[c].elapsed_time(evs[c + 1]) / L for c in range(protocol_chains))
+    return {"ms": total, "chain_layers": Lc, "chains_timed": n_chain,
+            "median_ms": per_chain[len(per_chain) // 2], "protocol_chains": protocol_chains, "protocol_layers": L}
 
 
-def cold_layer_ms(insts, reps=10, flush_bytes=512 << 20):
-    """Single-layer latency after writing a 512 MB buffer (evicts the
-    last-level cache): median over `reps` instances' single-layer graphs."""
-    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+def single_layer_ms(insts, reps=10, flush_bytes=0):
+    """Latency of one layer launched alone (its single-layer graph) after the
+    GPU has drained: median over `reps` instances.  With flush_bytes, a buffer
+    of that size is written first (it evicts the last-level cache, leaves its
+    lines dirty, and replaces the TLB entries of the weights)."""
+    flush = torch.empty(max(flush_bytes, 4) // 4, dtype=torch.float32, device="cuda")
     times = []
     for i in range(reps):
         inst = insts[i % len(insts)]
-        flush.fill_(float(i))
+        if flush_bytes:
+            flush.fill_(float(i))
+        torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         inst.graph.replay()
@@ -253,22 +274,52 @@ def traffic_record(kernel_key, workload, launch_bytes):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(inst, seconds):
-    """The fp64 oracle (as it stands) on the host cores: full layer over
-    instance 0's tokens, repeated for about `seconds`."""
-    from oracle import moe_oracle as O
-    from oracle.inputs import banks_from, widen_tensor
+def host_description():
+    """CPU model, the BLAS library NumPy uses, and the thread count the oracle
+    runs with: the cores this process may run on (its affinity mask), capped
+    by OMP_NUM_THREADS when that is set (the CPU share of a shared host)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        cores = min(cores, int(omp))
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
     except Exception:  # pragma: no cover
-        cores = 1
+        pass
+    return {"cpu_model": model, "blas": blas, "cores": cores}
+
+
+def cpu_baseline(inst, seconds):
+    """The fp64 oracle (as it stands) on the host cores: full layer forwards
+    over instance 0's tokens, repeated for about `seconds` (at least once),
+    with BLAS limited to the cores host_description() reports."""
+    from oracle import moe_oracle as O
+    from oracle.inputs import banks_from, widen_tensor
+    host = host_description()
     spec = inst.spec
     host_w = clone_weights_to_host(inst.w)
     banks = banks_from(host_w, lazy=True)
     x64, r64 = widen_tensor(inst.x), widen_tensor(inst.r)
     wr = widen_tensor(host_w.router)
     bias = None if host_w.expert_bias is None else widen_tensor(host_w.expert_bias)
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=host["cores"], user_api="blas")
+    except Exception:  # pragma: no cover
+        limiter = None
     reps, t0 = 0, time.time()
     while True:
         O.layer_forward(x64, r64, wr, banks, spec.family, spec.top_k, bias, spec.n_group, spec.topk_group,
@@ -277,7 +328,10 @@ def cpu_baseline(inst, seconds):
         if time.time() - t0 >= seconds:
             break
     dt = time.time() - t0
-    return {"value": reps * spec.n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    if limiter is not None:
+        limiter.unregister()
+    return {"value": reps * spec.n_tokens / dt, "unit": "tokens/s", "cores": host["cores"], "kind": "oracle",
+            "cpu_model": host["cpu_model"], "blas": host["blas"],
             "sample": f"{reps} full layer forwards of the same workload (T={spec.n_tokens}) in float64 NumPy, "
                       f"{dt:.1f} s wall clock; weights widened from bf16 per expert inside each call"}
 
@@ -313,8 +367,10 @@ def copy_calibration(nbytes=1 << 30):
 def run_workload(name, T, L, steps, warmup, stage_reps):
     spec = WORKLOADS[name].with_tokens(T)
     insts = build_instances(spec, L, f"{name} T={T}")
-    ms, ms_median = time_layer(insts, steps, warmup)
-    cold_ms = cold_layer_ms(insts)
+    tl = time_layer(insts, steps, warmup)
+    ms, ms_median = tl["ms"], tl["median_ms"]
+    alone_ms = single_layer_ms(insts)
+    cold_ms = single_layer_ms(insts, flush_bytes=512 << 20)
     n_act = [inst.n_active() for inst in insts]
     mean_act = float(np.mean(n_act))
     byts = float(np.mean([layer_bytes(spec, a) for a in n_act]))
@@ -328,6 +384,7 @@ def run_workload(name, T, L, steps, warmup, stage_reps):
     res = {
         "spec": spec, "insts": insts, "ms_per_step": ms, "tokens_per_s": T / t,
         "median_chain_us_per_layer": ms_median * 1e3, "cold_layer_us": cold_ms * 1e3,
+        "alone_layer_us": alone_ms * 1e3, "timing": tl,
         "mfma_ceiling": t_mfma / max(t_hbm, t_mfma),
         "n_active_mean": mean_act, "layer_bytes": byts, "layer_flops": flops,
         "layer_hbm_frac": byts / t / (HBM_PEAK_GBS * 1e9), "layer_mfma_frac": flops / t / (BF16_PEAK_TFLOPS * 1e12),
@@ -337,7 +394,9 @@ def run_workload(name, T, L, steps, warmup, stage_reps):
     log(f"{name} T={T}: {ms * 1e3:.1f} us/layer, {T / t:,.0f} tok/s, n_active {mean_act:.1f}, "
         f"layer {byts / t / 1e9:,.0f} GB/s ({res['layer_hbm_frac']:.1%} HBM), "
         f"{flops / t / 1e12:.1f} TFLOP/s ({res['layer_mfma_frac']:.1%} MFMA, ceiling {res['mfma_ceiling']:.1%}); "
-        f"median chain {ms_median * 1e3:.1f} us/layer, cold single layer {cold_ms * 1e3:.1f} us; gate/up {stage_ms * 1e3:.1f} us = "
+        f"{tl['chains_timed']} chains of {tl['chain_layers']} timed; median of {tl['protocol_chains']} chains of "
+        f"{tl['protocol_layers']} {ms_median * 1e3:.1f} us/layer; single layer alone {alone_ms * 1e3:.1f} us, "
+        f"after a cache flush {cold_ms * 1e3:.1f} us; gate/up {stage_ms * 1e3:.1f} us = "
         f"{res['gateup_gbs']:,.0f} GB/s, {res['gateup_tflops']:.1f} TFLOP/s")
     return res
 
@@ -614,9 +673,15 @@ def main():
                    "layer_hbm_frac": round(dec["layer_hbm_frac"], 4),
                    "layer_mfma_frac": round(dec["layer_mfma_frac"], 4),
                    "mfma_ceiling": round(dec["mfma_ceiling"], 4),
+                   "timed_chain_layers": dec["timing"]["chain_layers"],
+                   "timed_chains": dec["timing"]["chains_timed"],
                    "median_chain_us_per_layer": round(dec["median_chain_us_per_layer"], 2),
+                   "median_over": f"{dec['timing']['protocol_chains']} chains of {dec['timing']['protocol_layers']} "
+                                  f"layers, outside the timed region",
+                   "alone_layer_us": round(dec["alone_layer_us"], 2),
                    "cold_layer_us": round(dec["cold_layer_us"], 2)},
-        "roofline": {"kernel": "routed gate/up GEMM + SwiGLU", "bound": "hbm",
+        "roofline": {"kernel": "routed gate/up GEMM + SwiGLU (selection folded in, as the layer launches it)",
+                     "bound": "hbm",
                      "achieved": round(dec["gateup_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec["gateup_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": gu_traffic, "launch_us": round(dec["gateup_ms"] * 1e3, 3),
@@ -640,10 +705,14 @@ def main():
             "layer_mfma_frac": round(pre["layer_mfma_frac"], 4), "layer_hbm_frac": round(pre["layer_hbm_frac"], 4),
             "mfma_ceiling": round(pre["mfma_ceiling"], 4), "layer_algorithmic_bytes": round(pre["layer_bytes"]),
             "layer_algorithmic_flops": round(pre["layer_flops"]),
+            "timed_chain_layers": pre["timing"]["chain_layers"], "timed_chains": pre["timing"]["chains_timed"],
             "median_chain_us_per_layer": round(pre["median_chain_us_per_layer"], 2),
+            "alone_layer_us": round(pre["alone_layer_us"], 2),
             "cold_layer_us": round(pre["cold_layer_us"], 2),
             "roofline": prefill_roofline(pre),
         }
+        if not args.no_cpu_baseline:
+            line["secondary"]["cpu_baseline"] = cpu_baseline(pre["insts"][0], args.cpu_seconds)
         del pre
     print(json.dumps(line), flush=True)
 

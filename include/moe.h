@@ -219,7 +219,9 @@ moe_status moe_layer_forward_norm(const moe_config* cfg, const moe_weights* weig
 /* Stages of moe_layer_forward that moe_layer_stage can re-launch. */
 typedef enum {
     MOE_STAGE_ROUTER_LOGITS = 0, /* router GEMM: x [T,D] -> fp32 logits in ws */
-    MOE_STAGE_GATE_UP = 1,       /* routed gate/up GEMM + SwiGLU -> h in ws */
+    MOE_STAGE_GATE_UP = 1,       /* routed gate/up GEMM + SwiGLU -> h in ws (where the layer
+                                    folds the selection into this launch, so does the stage:
+                                    it selects again from the router logits in ws) */
     MOE_STAGE_DOWN = 2,          /* routed down GEMM x alpha -> staged slot rows in ws (small T
                                     with bf16/4-bit weights: the down projection fused with the
                                     combine, writing a [T, D] scratch in ws) */

@@ -727,7 +727,18 @@ moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, co
     switch (stage) {
         case MOE_STAGE_ROUTER_LOGITS: return stage_logits(c, L, ws, x, weights->router, stream);
         case MOE_STAGE_GATE_UP:
-            if (small_path(c)) return stage_small_gateup(c, L, ws, x, *weights, stream);
+            if (small_path(c)) {
+                if (!select_fused(c)) return stage_small_gateup(c, L, ws, x, *weights, stream);
+                // the launch the layer runs: selection (and the shared gate
+                // logit) from the router logits in ws, then gate/up
+                const moe::SelParams P = sel_params(c, L, ws, weights->expert_bias);
+                moe::GateParams G{};
+                if (c.d_ff_shared > 0 && weights->shared_gate_vec) {
+                    G.x = x; G.w = weights->shared_gate_vec; G.D = c.d_model; G.x_f32 = c.act_dtype == MOE_F32;
+                    G.out = at<float>(ws, L.gate_logit);
+                }
+                return stage_small_gateup(c, L, ws, x, *weights, stream, &P, &G);
+            }
             return stage_gateup(c, L, ws, x, *weights, pairs, tiles, nt, stream);
         case MOE_STAGE_GATE_UP_DIRECT:
             if (!small_path(c)) return fail(MOE_ERR_UNSUPPORTED, "the direct gate/up stage needs the small-T path");
