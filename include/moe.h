@@ -216,6 +216,22 @@ moe_status moe_layer_forward_norm(const moe_config* cfg, const moe_weights* weig
                                   int32_t* topk_ids_out, float* topk_weights_out, void* ws, size_t ws_bytes,
                                   moe_stream_t stream, moe_stream_t aux_stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, outputs and results as moe_layer_forward,
+ * without the workspace and the aux stream: everything runs on `stream`.
+ * Scratch memory is a 32 MiB array inside the library, one per device (held
+ * until the process ends); a layer whose moe_workspace_size exceeds 32 MiB
+ * (at Qwen3.6 shape: bf16 weights beyond T = 256) returns
+ * MOE_ERR_WORKSPACE_TOO_SMALL and launches nothing.  The call allocates
+ * nothing: no hipMalloc, hipFree, event or stream creation.  Every call on a
+ * device shares that device's array, so calls that overlap on one device
+ * (different streams, or different host threads) race: order them on one
+ * stream. */
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, const moe_weights* weights, const void* x,
+                                     const float* residual, float* out, int32_t* topk_ids_out,
+                                     float* topk_weights_out, moe_stream_t stream);
+
 /* Stages of moe_layer_forward that moe_layer_stage can re-launch. */
 typedef enum {
     MOE_STAGE_ROUTER_LOGITS = 0, /* router GEMM: x [T,D] -> fp32 logits in ws */

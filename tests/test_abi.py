@@ -161,6 +161,31 @@ def test_rms_norm_argument_errors_without_launch():
                                     ws, 16, None, None) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_noalloc_entry_host_checks_without_launch():
+    """The allocation-free layer entry rejects bad arguments and layers whose
+    scratch need exceeds its 32 MiB array before any HIP call."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(4096)  # never dereferenced
+    w = moe.MoeWeights(4096, None, moe.MoeMatrix(4096, None, None), moe.MoeMatrix(4096, None, None),
+                       moe.MoeMatrix(4096, None, None), moe.MoeMatrix(4096, None, None),
+                       moe.MoeMatrix(4096, None, None), moe.MoeMatrix(4096, None, None))
+    big = moe.make_config(512, 2048, 256, 8, 512, 512)
+    assert moe.workspace_size(big) > 32 << 20
+    assert L.moe_layer_forward_noalloc(ctypes.byref(big), ctypes.byref(w), fake, fake, fake, None, None, None) == \
+        moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert b"32" in L.moe_last_error() or b"33554432" in L.moe_last_error()
+    small = moe.make_config(8, 2048, 256, 8, 512, 512)
+    assert L.moe_layer_forward_noalloc(ctypes.byref(small), ctypes.byref(w), None, fake, fake, None, None, None) == \
+        moe.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_layer_forward_noalloc(ctypes.byref(small), None, fake, fake, fake, None, None, None) == \
+        moe.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_layer_forward_noalloc(None, ctypes.byref(w), fake, fake, fake, None, None, None) == \
+        moe.MOE_ERR_INVALID_ARGUMENT
+    zero = moe.make_config(0, 2048, 256, 8, 512, 512)
+    assert L.moe_layer_forward_noalloc(ctypes.byref(zero), ctypes.byref(w), None, None, None, None, None, None) == \
+        moe.MOE_OK
+
+
 def test_zero_tokens_is_ok_without_launch():
     L = moe.lib()
     cfg = _cfg(n_tokens=0)

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -557,6 +558,32 @@ moe_status layer_forward_impl(const moe_config& c, const moe_weights* weights, c
     return MOE_OK;
 }
 
+// Scratch memory of moe_layer_forward_noalloc, for callers that cannot
+// allocate: one array per device, held by the loaded library until the
+// process ends.  Its name denotes a host-side stand-in in host code; host
+// code uses only the device address that hipGetSymbolAddress returns for the
+// current device (kept per device in g_scratch_ptr).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDev] = {};
+
+// Device address of this device's scratch array (looked up once per device,
+// with that device current).
+moe_status scratch_ptr(void** out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDev) return fail(MOE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p || reinterpret_cast<uintptr_t>(p) % 256)
+            return fail(MOE_ERR_HIP, "scratch array address %p is not 256-byte aligned", p);
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -671,6 +698,27 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
     if (moe_status st = check_ws(*cfg, ws, ws_bytes)) return st;
     (void)hipGetLastError();
     return layer_forward_impl(*cfg, weights, x, residual, out, topk_ids_out, topk_weights_out, ws, stream, aux_stream);
+}
+
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, const moe_weights* weights, const void* x,
+                                     const float* residual, float* out, int32_t* topk_ids_out,
+                                     float* topk_weights_out, moe_stream_t stream) {
+    g_err[0] = 0;
+    if (moe_status st = check_config(cfg)) return st;
+    if (cfg->n_tokens == 0) return MOE_OK;
+    if (!x || !residual || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL tensor argument");
+    if (!weights || !weights->router) return fail(MOE_ERR_INVALID_ARGUMENT, "router weights are NULL");
+    if (moe_status st = check_weights(*cfg, weights, true, true)) return st;
+    const size_t need = layout(*cfg).total;
+    if (need > kScratchBytes)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
+                    "this layer needs %zu bytes of scratch; the allocation-free entry has %zu (use "
+                    "moe_layer_forward with a workspace)", need, kScratchBytes);
+    void* ws = nullptr;
+    if (moe_status st = scratch_ptr(&ws)) return st;
+    (void)hipGetLastError();
+    // one stream: no fork/join events are created
+    return layer_forward_impl(*cfg, weights, x, residual, out, topk_ids_out, topk_weights_out, ws, stream, nullptr);
 }
 
 moe_status moe_rms_norm(const moe_config* cfg, const float* residual, const float* norm_weight, float eps, void* x,

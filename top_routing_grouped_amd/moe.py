@@ -29,8 +29,8 @@ _FAM = {"softmax": SOFTMAX_TOPK, "sigmoid_group": SIGMOID_GROUP_TOPK}
 
 # Entry points the header declares (checked by the CPU tests).
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_experts", "moe_shared_expert",
-           "moe_combine", "moe_layer_forward", "moe_rms_norm", "moe_layer_forward_norm", "moe_layer_stage",
-           "moe_status_string", "moe_last_error")
+           "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_rms_norm", "moe_layer_forward_norm",
+           "moe_layer_stage", "moe_status_string", "moe_last_error")
 STAGE_ROUTER_LOGITS, STAGE_GATE_UP, STAGE_DOWN, STAGE_GATE_UP_DIRECT = 0, 1, 2, 3
 
 
@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "moe_shared_expert": [cfg, P, wts, P, P, S, P],
             "moe_combine": [cfg, P, P, P, P, P],
             "moe_layer_forward": [cfg, wts, P, P, P, P, P, P, S, P, P],
+            "moe_layer_forward_noalloc": [cfg, wts, P, P, P, P, P, P],
             "moe_rms_norm": [cfg, P, P, ctypes.c_float, P, P],
             "moe_layer_forward_norm": [cfg, wts, P, ctypes.c_float, P, P, P, P, P, P, S, P, P],
             "moe_layer_stage": [cfg, wts, P, I32, P, S, P],
@@ -183,6 +184,12 @@ def layer_forward(cfg, wstruct: MoeWeights, x, residual, out, ids_out=None, weig
                                    _ptr(ids_out), _ptr(weights_out), _ptr(ws), 0 if ws is None else ws.numel(),
                                    _stream(stream), None if aux_stream is None else _stream(aux_stream)),
            "moe_layer_forward")
+
+
+def layer_forward_noalloc(cfg, wstruct: MoeWeights, x, residual, out, ids_out=None, weights_out=None, stream=None):
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(cfg), ctypes.byref(wstruct), _ptr(x), _ptr(residual),
+                                           _ptr(out), _ptr(ids_out), _ptr(weights_out), _stream(stream)),
+           "moe_layer_forward_noalloc")
 
 
 def rms_norm(cfg, residual, norm_weight, eps: float, x, stream=None):
