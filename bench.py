@@ -76,10 +76,14 @@ class Instance:
         self.ids = torch.empty(spec.n_tokens, spec.top_k, dtype=torch.int32, device="cuda")
         self.wts = torch.empty(spec.n_tokens, spec.top_k, dtype=torch.float32, device="cuda")
         self.graph = None
+        self.direct = False  # the direct (per-pair) schedule instead of the grouped one
 
     def forward(self, aux):
-        moe.layer_forward(self.cfg, self.ws_struct, self.x, self.r, self.out, self.ids, self.wts, self.ws,
-                          aux_stream=aux)
+        if self.direct:
+            moe.layer_forward_direct(self.cfg, self.ws_struct, self.x, self.r, self.out, self.ids, self.wts, self.ws)
+        else:
+            moe.layer_forward(self.cfg, self.ws_struct, self.x, self.r, self.out, self.ids, self.wts, self.ws,
+                              aux_stream=aux)
 
     def stage(self, stage):
         moe.layer_stage(self.cfg, self.ws_struct, self.x, stage, self.ws)
@@ -532,27 +536,46 @@ def prefill_roofline(pre):
 
 
 def crossover(args):
-    """Direct (one work item per token-slot pair, each pair reading its
-    expert's weights) versus grouped (one work item per active expert)
-    execution of the routed gate/up stage at decode shape, on the same
-    routing.  Prints bytes the two would move without caches and their
-    measured launch times."""
-    for T in (1, 2, 4, 8, 16, 32):
+    """Direct execution (every (token, slot) pair its own work item, reading
+    its expert's weights) against grouped execution (the pairs of an expert
+    share one read of its weights) at decode shape, on the same routing: the
+    whole layer (moe_layer_forward_direct against moe_layer_forward, each as
+    captured chains of the 40 instances) and the routed gate/up stage alone.
+    Prints one JSON line per T with the bytes the two would move without
+    caches and the measured times."""
+    for T in (1, 2, 3, 4, 6, 8, 16, 32):
         spec = WORKLOADS["qwen_decode"].with_tokens(T)
         insts = build_instances(spec, min(args.instances, 40), f"crossover T={T}")
+        grouped = time_layer(insts, args.steps, args.warmup)
+        g_stage = time_stage(insts, moe.STAGE_GATE_UP, args.stage_reps)
+        d_stage = time_stage(insts, moe.STAGE_GATE_UP_DIRECT, args.stage_reps)
+        dn = {k: time_stage(insts, st, args.stage_reps) for k, st in
+              (("fused", moe.STAGE_DOWN), ("grouped", moe.STAGE_DOWN_GROUPED), ("direct", moe.STAGE_DOWN_DIRECT))}
+        g_ids = [inst.ids.clone() for inst in insts]
         for inst in insts:
-            inst.forward(None)
-        torch.cuda.synchronize()
-        grouped = time_stage(insts, moe.STAGE_GATE_UP, args.stage_reps)
-        direct = time_stage(insts, moe.STAGE_GATE_UP_DIRECT, args.stage_reps)
+            inst.direct = True
+        direct = time_layer(insts, args.steps, args.warmup)
+        if not all(torch.equal(a, inst.ids) for a, inst in zip(g_ids, insts)):
+            raise RuntimeError("direct and grouped schedules selected different experts")
         n_act = float(np.mean([inst.n_active() for inst in insts]))
-        wb = 2 * spec.d_model * spec.d_ff * BYTES_PER_PARAM[spec.expert_dtype]
-        line = {"study": "gate/up direct vs grouped", "n_tokens": T, "pairs": T * spec.top_k,
-                "n_active_mean": round(n_act, 2), "weight_bytes_grouped": round(n_act * wb),
-                "weight_bytes_direct_uncached": round(T * spec.top_k * wb),
-                "grouped_us": round(grouped * 1e3, 2), "direct_us": round(direct * 1e3, 2),
-                "direct_over_grouped": round(direct / grouped, 3)}
+        wb = 3 * spec.d_model * spec.d_ff * BYTES_PER_PARAM[spec.expert_dtype]
+        line = {"study": "layer, direct vs grouped", "n_tokens": T, "pairs": T * spec.top_k,
+                "n_active_mean": round(n_act, 2), "routed_weight_bytes_grouped": round(n_act * wb),
+                "routed_weight_bytes_direct_uncached": round(T * spec.top_k * wb),
+                "grouped_us_per_layer": round(grouped["ms"] * 1e3, 2),
+                "direct_us_per_layer": round(direct["ms"] * 1e3, 2),
+                "grouped_median_us": round(grouped["median_ms"] * 1e3, 2),
+                "direct_median_us": round(direct["median_ms"] * 1e3, 2),
+                "direct_over_grouped": round(direct["median_ms"] / grouped["median_ms"], 3),
+                "gate_up_stage_grouped_us": round(g_stage * 1e3, 2), "gate_up_stage_direct_us": round(d_stage * 1e3, 2),
+                "down_stage_fused_combine_us": round(dn["fused"] * 1e3, 2),
+                "down_stage_grouped_us": round(dn["grouped"] * 1e3, 2),
+                "down_stage_direct_us": round(dn["direct"] * 1e3, 2)}
         print(json.dumps(line), flush=True)
+        log(f"T={T}: layer grouped {line['grouped_median_us']} us, direct {line['direct_median_us']} us "
+            f"({line['direct_over_grouped']}x); gate/up stage {line['gate_up_stage_grouped_us']} / "
+            f"{line['gate_up_stage_direct_us']} us; down stage fused+combine / grouped / direct "
+            f"{line['down_stage_fused_combine_us']} / {line['down_stage_grouped_us']} / {line['down_stage_direct_us']} us")
         del insts
         torch.cuda.empty_cache()
 
@@ -601,8 +624,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="profiling aid: finish with a 1 GiB device-to-device copy (known bytes for counter scaling)")
     ap.add_argument("--crossover", action="store_true",
-                    help="small-T study: routed gate/up with one work item per (token, slot) pair versus grouped "
-                         "by expert, T = 1..32 at decode shape; prints one JSON line per T")
+                    help="small-T study: the layer (and its gate/up stage) with one work item per (token, slot) "
+                         "pair versus grouped by expert, T = 1..32 at decode shape; one JSON line per T")
     ap.add_argument("--no-chain", action="store_true")
     ap.add_argument("--configs", action="store_true",
                     help="one JSON line per parity configuration (every workload and token count)")

@@ -190,6 +190,25 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights, 
                              float* topk_weights_out, void* ws, size_t ws_bytes,
                              moe_stream_t stream, moe_stream_t aux_stream);
 
+/* The layer with direct (per-pair) execution of the routed experts, for
+ * small batches (Treebeard, "Intel SYCL path": below a few token columns the
+ * fused kernel runs one (token, slot) pair at a time instead of bucketing
+ * pairs by expert).  Same arguments, outputs and tolerances as
+ * moe_layer_forward (no aux stream: one stream); the routed gate/up and down
+ * projections take one work item per (token, slot) pair, each reading its
+ * expert's weights, where moe_layer_forward groups the pairs of an expert so
+ * its weights are read once; the combine is a separate launch.  Only for
+ * layers moe_layer_forward runs on its single-stream small-T schedule
+ * (T*K <= 256 and fewer than 16 pairs per expert on average for bf16 banks,
+ * 64 otherwise); MOE_ERR_UNSUPPORTED beyond.  The routing and the SwiGLU
+ * intermediate equal moe_layer_forward's bit for bit (same selection, same
+ * tile shape and sum order per pair); the routed down projection is the
+ * unfused one, so the output matches moe_layer_forward's within the layer
+ * tolerance (bit for bit with fp32 weights). */
+moe_status moe_layer_forward_direct(const moe_config* cfg, const moe_weights* weights, const void* x,
+                                    const float* residual, float* out, int32_t* topk_ids_out,
+                                    float* topk_weights_out, void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /* RMS normalisation of the attention residual (Treebeard "Routing math": x_t
  * is the post-attention, RMS-normalised hidden state; "Editable Mermaid
  * flowchart" and "Pseudocode": x = rms_norm(attention residual) before the
@@ -241,12 +260,18 @@ typedef enum {
     MOE_STAGE_DOWN = 2,          /* routed down GEMM x alpha -> staged slot rows in ws (small T
                                     with bf16/4-bit weights: the down projection fused with the
                                     combine, writing a [T, D] scratch in ws) */
-    MOE_STAGE_GATE_UP_DIRECT = 3 /* small T*K only (<= 256 pairs, fewer than 64 per expert):
+    MOE_STAGE_GATE_UP_DIRECT = 3, /* small T*K only (<= 256 pairs, fewer than 64 per expert):
                                     the gate/up stage with every (token, slot) pair as its
                                     own work item, no grouping by expert (Treebeard, "Intel
                                     SYCL path": direct versus bucketed execution); writes
-                                    the same h as MOE_STAGE_GATE_UP.  MOE_ERR_UNSUPPORTED
+                                    the same h as MOE_STAGE_GATE_UP (and selects inside the
+                                    launch when that stage does).  MOE_ERR_UNSUPPORTED
                                     otherwise. */
+    MOE_STAGE_DOWN_GROUPED = 4,  /* small T*K only: the down projection x alpha into slot rows
+                                    in ws, one work item per active expert (the unfused
+                                    grouped form; with fp32 weights the one the layer runs) */
+    MOE_STAGE_DOWN_DIRECT = 5    /* small T*K only: the same with one work item per (token,
+                                    slot) pair (moe_layer_forward_direct's down projection) */
 } moe_stage;
 
 /* Measurement aid: re-launches one kernel stage of the last

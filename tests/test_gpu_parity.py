@@ -266,6 +266,30 @@ def test_gate_up_direct_stage_matches_grouped(name, T):
     assert torch.equal(ws, grouped)
 
 
+@pytest.mark.parametrize("name,T", [("qwen_decode", 1), ("qwen_decode", 8), ("qwen_decode", 32), ("small_bf16", 37),
+                                    ("small_u4", 37), ("small_f32", 37), ("small_sigmoid", 9)])
+def test_down_direct_stage_matches_grouped(name, T):
+    """The (token, slot)-per-work-item down stage writes the same slot rows,
+    bit for bit, as the grouped unfused down stage (same tile shape and sum
+    order for each pair's output)."""
+    case = _small(name, T) if name in SMALL else make_case(spec_of(name, n_tokens=T))
+    cfg = moe.config_from_spec(case.spec)
+    ws = moe.alloc_workspace(cfg)
+    wst = moe.weights_struct(case.w)
+    moe.layer_forward(cfg, wst, case.x, case.r, torch.empty_like(case.r), None, None, ws)
+    torch.cuda.synchronize()
+    base = ws.clone()
+    moe.layer_stage(cfg, wst, case.x, moe.STAGE_DOWN_GROUPED, ws)
+    torch.cuda.synchronize()
+    grouped = ws.clone()
+    if name.startswith("qwen"):  # the layer ran the fused down + combine: the stage's slot rows are new
+        assert not torch.equal(grouped, base)
+    ws.copy_(base)
+    moe.layer_stage(cfg, wst, case.x, moe.STAGE_DOWN_DIRECT, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ws, grouped)
+
+
 def test_gate_up_direct_stage_rejects_large_t():
     case = _small("small_bf16", 700)  # 2800 pairs over 32 experts: the grouped large-T path
     cfg = moe.config_from_spec(case.spec)

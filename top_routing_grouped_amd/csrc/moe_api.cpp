@@ -378,13 +378,29 @@ moe_status stage_small_gateup(const moe_config& c, const Layout& L, void* ws, co
     return MOE_OK;
 }
 
-// The same stage with one work item per (token, slot) pair (no grouping).
+// The same stage with one work item per (token, slot) pair (no grouping);
+// with `sel`, the selection runs inside the launch as in the grouped one.
 moe_status stage_small_gateup_direct(const moe_config& c, const Layout& L, void* ws, const void* x,
-                                     const moe_weights& w, hipStream_t s) {
+                                     const moe_weights& w, hipStream_t s, const moe::SelParams* sel = nullptr,
+                                     const moe::GateParams* gate = nullptr) {
     moe::GemmArgs a = small_args(c, L, ws, w, true);
     a.act = x;
     a.out = at<void>(ws, L.h);
     a.direct_pairs = 1;
+    if (sel) {
+        a.fused_sel = 1;
+        a.sel_logits = sel->logits;
+        a.sel_ksplit = sel->ksplit;
+        a.sel_ids = at<int32_t>(ws, L.ids);
+        a.sel_wts = at<float>(ws, L.wts);
+        a.sel_ids2 = sel->ids2;
+        a.sel_wts2 = sel->wts2;
+        if (gate && gate->w) {
+            a.gate_w = gate->w;
+            a.gate_x_f32 = gate->x_f32;
+            a.gate_out = gate->out;
+        }
+    }
     // the grouped launch's tile shape, so both compute each h element alike
     a.shape_grid = (a.has_shared ? 1 : 0) + std::min(c.n_experts, c.n_tokens * c.top_k);
     const int grid = (a.has_shared ? 1 : 0) + c.n_tokens * c.top_k;
@@ -392,11 +408,22 @@ moe_status stage_small_gateup_direct(const moe_config& c, const Layout& L, void*
     return MOE_OK;
 }
 
-moe_status stage_small_down(const moe_config& c, const Layout& L, void* ws, const moe_weights& w, hipStream_t s) {
+// Small-T down projection into slot rows (K routed + the shared expert per
+// token), grouped by expert or, with `direct`, one work item per (token,
+// slot) pair (each pair reads its expert's rows; same tile shape, so the same
+// slot values).
+moe_status stage_small_down(const moe_config& c, const Layout& L, void* ws, const moe_weights& w, hipStream_t s,
+                            bool direct = false) {
     moe::GemmArgs a = small_args(c, L, ws, w, false);
     a.act = at<void>(ws, L.h);
     a.out = at<void>(ws, L.slots);
-    const int grid = (a.has_shared ? 1 : 0) + std::min(c.n_experts, c.n_tokens * c.top_k);
+    const int grouped = (a.has_shared ? 1 : 0) + std::min(c.n_experts, c.n_tokens * c.top_k);
+    int grid = grouped;
+    if (direct) {
+        a.direct_pairs = 1;
+        a.shape_grid = grouped;
+        grid = (a.has_shared ? 1 : 0) + c.n_tokens * c.top_k;
+    }
     HIP_TRY(moe::launch_gemm(moe::kSmallDown, wkind_of(c.expert_dtype), c.expert_dtype != MOE_F32, a, grid, 1, s));
     return MOE_OK;
 }
@@ -721,6 +748,41 @@ moe_status moe_layer_forward_noalloc(const moe_config* cfg, const moe_weights* w
     return layer_forward_impl(*cfg, weights, x, residual, out, topk_ids_out, topk_weights_out, ws, stream, nullptr);
 }
 
+moe_status moe_layer_forward_direct(const moe_config* cfg, const moe_weights* weights, const void* x,
+                                    const float* residual, float* out, int32_t* topk_ids_out,
+                                    float* topk_weights_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
+    g_err[0] = 0;
+    if (moe_status st = check_config(cfg)) return st;
+    if (cfg->n_tokens == 0) return MOE_OK;
+    if (!x || !residual || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL tensor argument");
+    if (!weights || !weights->router) return fail(MOE_ERR_INVALID_ARGUMENT, "router weights are NULL");
+    if (moe_status st = check_weights(*cfg, weights, true, true)) return st;
+    if (moe_status st = check_ws(*cfg, ws, ws_bytes)) return st;
+    const moe_config& c = *cfg;
+    if (!small_path(c))
+        return fail(MOE_ERR_UNSUPPORTED, "direct execution needs T*K <= 256 (and few pairs per expert); got %d pairs",
+                    c.n_tokens * c.top_k);
+    (void)hipGetLastError();
+    const Layout L = layout(c);
+    const bool has_shared = c.d_ff_shared > 0;
+    int32_t* ids = at<int32_t>(ws, L.ids);
+    float* wts = at<float>(ws, L.wts);
+    const moe::SelParams P = sel_params(c, L, ws, weights->expert_bias, topk_ids_out, topk_weights_out);
+    if (moe_status st = stage_logits(c, L, ws, x, weights->router, stream)) return st;
+    moe::GateParams G{};
+    if (has_shared && weights->shared_gate_vec) {
+        G.x = x; G.w = weights->shared_gate_vec; G.D = c.d_model; G.x_f32 = c.act_dtype == MOE_F32;
+        G.out = at<float>(ws, L.gate_logit);
+    }
+    const bool fuse = select_fused(c);
+    if (!fuse) HIP_TRY(moe::launch_route_select_gate(P, G, ids, wts, stream));
+    if (moe_status st = stage_small_gateup_direct(c, L, ws, x, *weights, stream, fuse ? &P : nullptr, &G)) return st;
+    if (moe_status st = stage_small_down(c, L, ws, *weights, stream, true)) return st;
+    HIP_TRY(moe::launch_combine(at<void>(ws, L.slots), c.expert_dtype != MOE_F32, nullptr, residual, out, c.n_tokens,
+                                c.top_k + (has_shared ? 1 : 0), c.d_model, stream));
+    return MOE_OK;
+}
+
 moe_status moe_rms_norm(const moe_config* cfg, const float* residual, const float* norm_weight, float eps, void* x,
                         moe_stream_t stream) {
     g_err[0] = 0;
@@ -775,22 +837,30 @@ moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, co
     switch (stage) {
         case MOE_STAGE_ROUTER_LOGITS: return stage_logits(c, L, ws, x, weights->router, stream);
         case MOE_STAGE_GATE_UP:
-            if (small_path(c)) {
-                if (!select_fused(c)) return stage_small_gateup(c, L, ws, x, *weights, stream);
-                // the launch the layer runs: selection (and the shared gate
-                // logit) from the router logits in ws, then gate/up
-                const moe::SelParams P = sel_params(c, L, ws, weights->expert_bias);
-                moe::GateParams G{};
-                if (c.d_ff_shared > 0 && weights->shared_gate_vec) {
-                    G.x = x; G.w = weights->shared_gate_vec; G.D = c.d_model; G.x_f32 = c.act_dtype == MOE_F32;
-                    G.out = at<float>(ws, L.gate_logit);
-                }
-                return stage_small_gateup(c, L, ws, x, *weights, stream, &P, &G);
+        case MOE_STAGE_GATE_UP_DIRECT: {
+            const bool direct = stage == MOE_STAGE_GATE_UP_DIRECT;
+            if (!small_path(c)) {
+                if (direct) return fail(MOE_ERR_UNSUPPORTED, "the direct gate/up stage needs the small-T path");
+                return stage_gateup(c, L, ws, x, *weights, pairs, tiles, nt, stream);
             }
-            return stage_gateup(c, L, ws, x, *weights, pairs, tiles, nt, stream);
-        case MOE_STAGE_GATE_UP_DIRECT:
-            if (!small_path(c)) return fail(MOE_ERR_UNSUPPORTED, "the direct gate/up stage needs the small-T path");
-            return stage_small_gateup_direct(c, L, ws, x, *weights, stream);
+            if (!select_fused(c))
+                return direct ? stage_small_gateup_direct(c, L, ws, x, *weights, stream)
+                              : stage_small_gateup(c, L, ws, x, *weights, stream);
+            // the launch the layer runs: selection (and the shared gate
+            // logit) from the router logits in ws, then gate/up
+            const moe::SelParams P = sel_params(c, L, ws, weights->expert_bias);
+            moe::GateParams G{};
+            if (c.d_ff_shared > 0 && weights->shared_gate_vec) {
+                G.x = x; G.w = weights->shared_gate_vec; G.D = c.d_model; G.x_f32 = c.act_dtype == MOE_F32;
+                G.out = at<float>(ws, L.gate_logit);
+            }
+            return direct ? stage_small_gateup_direct(c, L, ws, x, *weights, stream, &P, &G)
+                          : stage_small_gateup(c, L, ws, x, *weights, stream, &P, &G);
+        }
+        case MOE_STAGE_DOWN_GROUPED:
+        case MOE_STAGE_DOWN_DIRECT:
+            if (!small_path(c)) return fail(MOE_ERR_UNSUPPORTED, "the unfused small-T down stages need the small-T path");
+            return stage_small_down(c, L, ws, *weights, stream, stage == MOE_STAGE_DOWN_DIRECT);
         case MOE_STAGE_DOWN:
             if (down_combine_fused(c)) {
                 // the layer's own launch, writing into the workspace (y_shared region,

@@ -29,9 +29,10 @@ _FAM = {"softmax": SOFTMAX_TOPK, "sigmoid_group": SIGMOID_GROUP_TOPK}
 
 # Entry points the header declares (checked by the CPU tests).
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_experts", "moe_shared_expert",
-           "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_rms_norm", "moe_layer_forward_norm",
+           "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_layer_forward_direct",
+           "moe_rms_norm", "moe_layer_forward_norm",
            "moe_layer_stage", "moe_status_string", "moe_last_error")
-STAGE_ROUTER_LOGITS, STAGE_GATE_UP, STAGE_DOWN, STAGE_GATE_UP_DIRECT = 0, 1, 2, 3
+STAGE_ROUTER_LOGITS, STAGE_GATE_UP, STAGE_DOWN, STAGE_GATE_UP_DIRECT, STAGE_DOWN_GROUPED, STAGE_DOWN_DIRECT = range(6)
 
 
 class MoeConfig(ctypes.Structure):
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "moe_combine": [cfg, P, P, P, P, P],
             "moe_layer_forward": [cfg, wts, P, P, P, P, P, P, S, P, P],
             "moe_layer_forward_noalloc": [cfg, wts, P, P, P, P, P, P],
+            "moe_layer_forward_direct": [cfg, wts, P, P, P, P, P, P, S, P],
             "moe_rms_norm": [cfg, P, P, ctypes.c_float, P, P],
             "moe_layer_forward_norm": [cfg, wts, P, ctypes.c_float, P, P, P, P, P, P, S, P, P],
             "moe_layer_stage": [cfg, wts, P, I32, P, S, P],
@@ -190,6 +192,14 @@ def layer_forward_noalloc(cfg, wstruct: MoeWeights, x, residual, out, ids_out=No
     _check(lib().moe_layer_forward_noalloc(ctypes.byref(cfg), ctypes.byref(wstruct), _ptr(x), _ptr(residual),
                                            _ptr(out), _ptr(ids_out), _ptr(weights_out), _stream(stream)),
            "moe_layer_forward_noalloc")
+
+
+def layer_forward_direct(cfg, wstruct: MoeWeights, x, residual, out, ids_out=None, weights_out=None, ws=None,
+                         stream=None):
+    _check(lib().moe_layer_forward_direct(ctypes.byref(cfg), ctypes.byref(wstruct), _ptr(x), _ptr(residual),
+                                          _ptr(out), _ptr(ids_out), _ptr(weights_out), _ptr(ws),
+                                          0 if ws is None else ws.numel(), _stream(stream)),
+           "moe_layer_forward_direct")
 
 
 def rms_norm(cfg, residual, norm_weight, eps: float, x, stream=None):
