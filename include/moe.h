@@ -177,7 +177,8 @@ moe_status moe_combine(const moe_config* cfg, const float* slot_out, const float
  * non-NULL.  Internally the routed slot rows are staged in bf16 for bf16/u4
  * weights.  Schedules:
  *   T*K <= 256 (and experts averaging < 16 pairs for bf16 weights, < 64
- *     otherwise): a single stream; the
+ *     otherwise): a single stream (at most 32 pairs: the gate/up launch takes
+ *     one work item per pair instead of one per expert); the
  *     shared expert is one more work item of the routed gate/up and down
  *     launches, its sigmoid gate logit is computed with the routing, and each
  *     GEMM workgroup finds its expert and pairs from the routing ids itself
@@ -254,9 +255,10 @@ moe_status moe_layer_forward_noalloc(const moe_config* cfg, const moe_weights* w
 /* Stages of moe_layer_forward that moe_layer_stage can re-launch. */
 typedef enum {
     MOE_STAGE_ROUTER_LOGITS = 0, /* router GEMM: x [T,D] -> fp32 logits in ws */
-    MOE_STAGE_GATE_UP = 1,       /* routed gate/up GEMM + SwiGLU -> h in ws (where the layer
-                                    folds the selection into this launch, so does the stage:
-                                    it selects again from the router logits in ws) */
+    MOE_STAGE_GATE_UP = 1,       /* routed gate/up GEMM + SwiGLU -> h in ws, the launch the
+                                    layer runs (where the layer folds the selection into it,
+                                    so does the stage: it selects again from the router logits
+                                    in ws; at most 32 pairs it is the per-pair launch) */
     MOE_STAGE_DOWN = 2,          /* routed down GEMM x alpha -> staged slot rows in ws (small T
                                     with bf16/4-bit weights: the down projection fused with the
                                     combine, writing a [T, D] scratch in ws) */

@@ -425,6 +425,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     // the per-chunk loads: their reduction is short (d_ff), and the staging's
     // extra round trip before the K loop cost more than it saved there.
     constexpr bool U4S = (WK == kWU4) && DUAL;
+    constexpr bool PIPE = (WK == kWBF16) && TF == 1 && !NORM;  // double-buffered K trips (below)
     constexpr int kU4Stride = kU4MaxGroups + 1;  // words per row (odd: no bank conflicts)
     __shared__ uint32_t u4_sm[U4S ? NM * 16 * WN * kU4Stride : 1];
     if constexpr (U4S) {
@@ -543,6 +544,54 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                     for (int j = 0; j < TF; ++j) mma_chunk<F32>(acc[m][j], wa[i][m], xb[i][j]);
         };
         int c = 0;
+        if constexpr (PIPE) {
+            // bf16, one token fragment: two trip buffers, so that the next
+            // trip's loads are in flight while this trip waits and multiplies
+            // (a wave otherwise has nothing in flight between receiving a trip
+            // and issuing the next).  The last pair of trips is peeled: the
+            // loop body has no conditional load.
+            Frag<false> wb[2][U][NM];
+            Frag<false> xc[2][U][TF];
+            auto issue = [&](auto b_c, int t) __attribute__((always_inline)) {
+                constexpr int B = decltype(b_c)::value;
+#pragma unroll
+                for (int i = 0; i < U; ++i) {
+                    const int kc = kbeg + (t * U + i) * SPAN;
+                    load_w<WK>(wb[B][i][0], w0, s0, m0, wrow, K, kc, q);
+                    if constexpr (DUAL) load_w<WK>(wb[B][i][1], w1, s1, m1, wrow, K, kc, q);
+#pragma unroll
+                    for (int j = 0; j < TF; ++j) load_x<WK>(xc[B][i][j], xrow[j], kc, q);
+                }
+            };
+            auto mmas = [&](auto b_c) __attribute__((always_inline)) {
+                constexpr int B = decltype(b_c)::value;
+#pragma unroll
+                for (int i = 0; i < U; ++i)
+#pragma unroll
+                    for (int m = 0; m < NM; ++m)
+#pragma unroll
+                        for (int j = 0; j < TF; ++j) mma_chunk<F32>(acc[m][j], wb[B][i][m], xc[B][i][j]);
+            };
+            constexpr std::integral_constant<int, 0> I0{};
+            constexpr std::integral_constant<int, 1> I1{};
+            const int npair = nchunks / (2 * U);
+            if (npair > 0) {
+                issue(I0, 0);
+                for (int p = 0; p + 1 < npair; ++p) {
+                    issue(I1, 2 * p + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mmas(I0);
+                    issue(I0, 2 * p + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mmas(I1);
+                }
+                issue(I1, 2 * npair - 1);
+                __builtin_amdgcn_sched_barrier(0);
+                mmas(I0);
+                mmas(I1);
+                c = npair * 2 * U;
+            }
+        }
         for (; c + U <= nchunks; c += U) trip(c, std::integral_constant<int, U>{});
         for (; c < nchunks; ++c) trip(c, std::integral_constant<int, 1>{});
     }

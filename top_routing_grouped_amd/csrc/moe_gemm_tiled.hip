@@ -412,29 +412,36 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* dst, uint32
 }
 constexpr uint32_t kDropOffset = 0x80000000u;  // past every buffer: the store is dropped
 
-template <int MODE, bool OUTBF, class C>
+// KS: K elements per step (64 or 32); NST: LDS stages, the DMA running
+// PD = NST - 1 steps ahead of the MFMAs.
+template <int MODE, bool OUTBF, class C, int KS, int NST>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs a) {
     constexpr int BW = C::BW, BT = C::BT, WM = C::WM, WN = C::WN, FM = C::FM, FT = C::FT;
     constexpr int NW = C::NW;
     constexpr bool DUAL = (MODE == kRoutedGateUp);
     constexpr int ROWS = DUAL ? BW / 2 : BW;
-    constexpr int NST = 3;                  // LDS stages
-    constexpr int STAGE = (BW + BT) * RS;   // elements: A rows then B rows
-    constexpr int AJ = BW / 8 / NW;         // 8-row A blocks per wave per step
-    constexpr int BJ = BT / 8 / NW;         // 8-row B blocks per wave per step
+    constexpr int PD = NST - 1;             // steps in flight ahead of the one computed
+    constexpr int RSK = KS;                 // LDS row stride (elements)
+    constexpr int PPR = KS / 8;             // 16-byte pieces per LDS row
+    constexpr int RPC = 64 / PPR;           // rows one 64-lane DMA call covers
+    constexpr int STAGE = (BW + BT) * RSK;  // elements: A rows then B rows
+    constexpr int AJ = BW / RPC / NW;       // RPC-row A blocks per wave per step
+    constexpr int BJ = BT / RPC / NW;       // RPC-row B blocks per wave per step
     constexpr int kDmaPerStep = AJ + BJ;
     constexpr int kStores = DUAL ? FT * FM / 2 : FT * FM;
     constexpr int kPrefetch = DUAL ? 1 : 2 * FT;
+    static_assert(KS == 32 || KS == 64, "K steps of one or two 32-wide MFMA steps");
     static_assert(MODE == kRoutedGateUp || MODE == kRoutedDown, "routed modes");
-    static_assert(AJ * 8 * NW == BW && BJ * 8 * NW == BT, "whole 8-row blocks per wave");
-    static_assert(!DUAL || (NW / 2) * AJ * 8 == BW / 2, "a wave's A rows lie in the gate or the up half");
-    static_assert(6 + kStores + kPrefetch + kDmaPerStep < 64, "vmcnt range");
+    static_assert(AJ * RPC * NW == BW && BJ * RPC * NW == BT, "whole row blocks per wave");
+    static_assert(!DUAL || (NW / 2) * AJ * RPC == BW / 2, "a wave's A rows lie in the gate or the up half");
+    static_assert((PD - 1) * kDmaPerStep + kStores + kPrefetch < 64 && PD * kDmaPerStep < 64, "vmcnt range");
+    static_assert(RPC * BJ <= 64, "one pair id per lane covers the wave's B rows");
     __shared__ __attribute__((aligned(16))) uint16_t lds[NST][STAGE];
     __shared__ int4 items[kPersistMaxItems];
     // gate/up: pair ids of the item after next, 64 per wave (one DMA per item)
     __shared__ uint32_t pair_ids[DUAL ? NW * 64 : 1];
 
-    const int N = a.N, K = a.K, nk = K / BK;
+    const int N = a.N, K = a.K, nk = K / KS;
     const int nrb = (N + ROWS - 1) / ROWS;
     const int n_items = uniform(*a.n_tiles) * nrb;
     const int chunk = (n_items + 7) / 8;
@@ -462,23 +469,23 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
     }
     __syncthreads();
 
-    // ---- this lane's DMA pieces: A block j covers tile rows wave*8*AJ + 8j ..
-    // +7, lane = 8 * (row in block) + slot; the slot holds logical 16-byte
-    // piece slot ^ ((row >> 1) & 7)
+    // ---- this lane's DMA pieces: A block j covers tile rows wave*RPC*AJ +
+    // RPC*j .. + RPC-1, lane = PPR * (row in block) + slot; the slot holds
+    // logical 16-byte piece slot ^ ((row >> 1) & (PPR - 1))
     uint32_t aoff[AJ];
     int brow[BJ], bpiece[BJ];
 #pragma unroll
     for (int j = 0; j < AJ; ++j) {
-        const int ra = wave * 8 * AJ + 8 * j + (lane >> 3);
-        const int p = (lane & 7) ^ ((ra >> 1) & 7);
+        const int ra = wave * RPC * AJ + RPC * j + lane / PPR;
+        const int p = (lane % PPR) ^ ((ra >> 1) & (PPR - 1));
         aoff[j] = uint32_t(((DUAL ? (ra & (BW / 2 - 1)) : ra) * K + 8 * p) * 2);
     }
 #pragma unroll
     for (int j = 0; j < BJ; ++j) {
-        brow[j] = wave * 8 * BJ + 8 * j + (lane >> 3);
-        bpiece[j] = (lane & 7) ^ ((brow[j] >> 1) & 7);
+        brow[j] = wave * RPC * BJ + RPC * j + lane / PPR;
+        bpiece[j] = (lane % PPR) ^ ((brow[j] >> 1) & (PPR - 1));
     }
-    const bool up_wave = DUAL && wave * 8 * AJ >= BW / 2;
+    const bool up_wave = DUAL && wave * RPC * AJ >= BW / 2;
     const auto rs_x = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.act), 0,
                                                         uint32_t(size_t(a.n_act_rows) * K * 2), kRsrcWord3);
     const auto rs_out = __builtin_amdgcn_make_buffer_rsrc(
@@ -509,15 +516,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
     // K step kt of an item into LDS stage st
     auto dma = [&](int st, const __amdgpu_buffer_rsrc_t& rw, const uint32_t (&xo)[BJ], int kt)
                    __attribute__((always_inline)) {
-        const int so = kt * BK * 2;
+        const int so = kt * KS * 2;
         uint16_t* base = &lds[st][0];
 #pragma unroll
         for (int j = 0; j < AJ; ++j)
-            dma16(rw, base + (wave * 8 * AJ + 8 * j) * RS, aoff[j], so);
+            dma16(rw, base + (wave * RPC * AJ + RPC * j) * RSK, aoff[j], so);
 #pragma unroll
         for (int j = 0; j < BJ; ++j)
-            dma16(rs_x, base + (BW + wave * 8 * BJ + 8 * j) * RS, xo[j], so);
+            dma16(rs_x, base + (BW + wave * RPC * BJ + RPC * j) * RSK, xo[j], so);
     };
+    // element offset of 16-byte piece p of LDS row r of a stage
+    auto soff = [](int r, int p) __attribute__((always_inline)) { return r * RSK + ((p ^ ((r >> 1) & (PPR - 1))) << 3); };
 
     int arow_l[FM];
 #pragma unroll
@@ -529,21 +538,21 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
     }
     const int brow_l = wn * (BT / WN) + r;
     f32x4 acc[FM][FT];
+    constexpr int NKS = KS / 32;  // 32-wide MFMA steps per K step
     // byte offsets of the wave's fragments inside a stage: [ks][fragment]
-    uint32_t aofs[2][FM], bofs[2][FT];
+    uint32_t aofs[NKS][FM], bofs[NKS][FT];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) aofs[ks][i] = uint32_t(lds_off(arow_l[i], ks * 4 + q) * 2);
+        for (int i = 0; i < FM; ++i) aofs[ks][i] = uint32_t(soff(arow_l[i], ks * 4 + q) * 2);
 #pragma unroll
-        for (int jj = 0; jj < FT; ++jj) bofs[ks][jj] = uint32_t((BW * RS + lds_off(brow_l + jj * 16, ks * 4 + q)) * 2);
+        for (int jj = 0; jj < FT; ++jj) bofs[ks][jj] = uint32_t((BW * RSK + soff(brow_l + jj * 16, ks * 4 + q)) * 2);
     }
     const uint32_t lds0 = lds_byte_addr(&lds[0][0]);
-    static_assert(BK == 64, "two 32-wide MFMA K steps per stage");
     auto compute = [&](int st, auto nf_c) __attribute__((always_inline)) {
         constexpr int NF = decltype(nf_c)::value;
         const uint32_t sb = lds0 + uint32_t(st * STAGE * 2);
-        u32x4 af[2][FM], bfv[2][NF > 0 ? NF : 1];
+        u32x4 af[NKS][FM], bfv[NKS][NF > 0 ? NF : 1];
         auto reads = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) af[ks][i] = ds_read16(sb + aofs[ks][i]);
@@ -569,10 +578,14 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
         if constexpr (NF > 0) {
             reads(0);
             ready(0);
-            reads(1);  // in flight during the first half's MFMAs
-            mfmas(0);
-            ready(1);
-            mfmas(1);
+            if constexpr (NKS == 2) {
+                reads(1);  // in flight during the first half's MFMAs
+                mfmas(0);
+                ready(1);
+                mfmas(1);
+            } else {
+                mfmas(0);
+            }
         }
     };
 
@@ -598,8 +611,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
         for (int j = 0; j < FT; ++j) ep_cur[j] = a.pairs[pair_index(cur, wn * (BT / WN) + j * 16 + r)];
     }
     auto rw_cur = w_rsrc(cur);
-    dma(0, rw_cur, xo_cur, 0);
-    dma(1, rw_cur, xo_cur, 1);
+#pragma unroll
+    for (int st = 0; st < PD; ++st) dma(st, rw_cur, xo_cur, st);
 #pragma unroll
     for (int i = 0; i < kStores; ++i) {  // distinct offsets: identical stores would be merged
         if constexpr (OUTBF || DUAL)
@@ -607,7 +620,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
         else
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, rs_out, kDropOffset + 16u * i, 0, 0);
     }
-    int g = 0;  // global K step: LDS stage g % 3
+    int g = 0;  // global K step: LDS stage g % NST
 
     // Token-row offsets are formed one item ahead of their first DMA: the
     // pair ids of the item after next go into LDS by DMA at an item's top
@@ -625,8 +638,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
         // next (gate/up: its token rows) or the next item's store rows
         // (down), and this item's routing weights
         const int4 nx2 = item_at(min(m + 2, n_mine - 1));
-        if constexpr (DUAL)  // lane l: the pair id of the wave's row l mod 8 BJ (past the end: zero)
-            dma4(rs_pairs, &pair_ids[wave * 64], uint32_t(nx2.y + wave * 8 * BJ + (lane & (8 * BJ - 1))) * 4u);
+        if constexpr (DUAL)  // lane l: the pair id of the wave's row l mod RPC BJ (past the end: zero)
+            dma4(rs_pairs, &pair_ids[wave * 64], uint32_t(nx2.y + wave * RPC * BJ + (lane & (RPC * BJ - 1))) * 4u);
         if constexpr (!DUAL) {
 #pragma unroll
             for (int jj = 0; jj < FT; ++jj) {
@@ -647,25 +660,26 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
                 // two calls on the two arrays were merged by the compiler into
                 // one call on a selected array address, which put both arrays
                 // in scratch memory
-                const int st = (g + 2) % NST;
-                const bool same = kt + 2 < nk;
+                const int st = (g + PD) % NST;
+                const bool same = kt + PD < nk;
                 uint32_t xo_s[BJ];
 #pragma unroll
                 for (int jj = 0; jj < BJ; ++jj) xo_s[jj] = same ? xo_cur[jj] : xo_nxt[jj];
-                dma(st, same ? rw_cur : rw_nxt, xo_s, same ? kt + 2 : kt + 2 - nk);
+                dma(st, same ? rw_cur : rw_nxt, xo_s, same ? kt + PD : kt + PD - nk);
                 compute(g % NST, nf_c);
                 ++g;
             };
-            // steps 0 and 1: newer than their DMA: the next step's DMA, the
-            // stores and the prefetch
-            vm_wait_lgkm0<kDmaPerStep + kStores + kPrefetch>();
-            bare_barrier();
-            step(0);
-            vm_wait_lgkm0<kDmaPerStep + kStores + kPrefetch>();
-            bare_barrier();
-            step(1);
-            for (int kt = 2; kt < nk; ++kt) {
-                vm_wait_lgkm0<kDmaPerStep>();
+            // steps 0 .. PD-1: newer than their DMA are the DMA of the PD-1
+            // steps after them, the previous item's stores and this item's
+            // prefetch; later steps: the PD-1 steps' DMA only
+#pragma unroll
+            for (int kt = 0; kt < PD; ++kt) {
+                vm_wait_lgkm0<(PD - 1) * kDmaPerStep + kStores + kPrefetch>();
+                bare_barrier();
+                step(kt);
+            }
+            for (int kt = PD; kt < nk; ++kt) {
+                vm_wait_lgkm0<(PD - 1) * kDmaPerStep>();
                 bare_barrier();
                 step(kt);
             }
@@ -680,15 +694,15 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
                 self(self, std::integral_constant<int, NF - 1>{});
         };
         dispatch(dispatch, std::integral_constant<int, FT>{});
-        // exactly the two newest steps' DMA may be in flight here; everything
+        // exactly the PD newest steps' DMA may be in flight here; everything
         // older (the prefetch) is complete
-        vm_wait_lgkm0<2 * kDmaPerStep>();
+        vm_wait_lgkm0<PD * kDmaPerStep>();
         uint32_t xo_nn[BJ];
         if constexpr (DUAL) {
             uint32_t pid[BJ];
 #pragma unroll
             for (int jj = 0; jj < BJ; ++jj)
-                pid[jj] = ds_read4(lds_byte_addr(&pair_ids[wave * 64]) + 4u * uint32_t(brow[jj] - wave * 8 * BJ));
+                pid[jj] = ds_read4(lds_byte_addr(&pair_ids[wave * 64]) + 4u * uint32_t(brow[jj] - wave * RPC * BJ));
             lgkm_wait_all();
 #pragma unroll
             for (int jj = 0; jj < BJ; ++jj) {
@@ -788,22 +802,29 @@ static hipError_t launch_cfg(int mode, bool outbf, const GemmArgs& a, int grid_x
 // Persistent routed launch: one workgroup per CU (at most), each XCD's 32
 // taking its run of items in turn.  Needs an even number of K steps, byte
 // offsets inside 32 bits and at most kPersistMaxItems items per workgroup.
+#ifndef MOE_PERSIST_KS
+#define MOE_PERSIST_KS 64
+#endif
+constexpr int kPersistKS = MOE_PERSIST_KS;           // K per step of the persistent kernel
+constexpr int kPersistNST = kPersistKS == 64 ? 3 : 6;  // LDS stages: 144 KB either way
 static bool launch_persist(int mode, bool outbf, const GemmArgs& a, int max_tiles, hipStream_t s) {
     using C = CfgLarge;
+    constexpr int KS = kPersistKS, NST = kPersistNST;
     const int rows = mode == kRoutedGateUp ? C::BW / 2 : C::BW;
     const long long max_items = (long long)max_tiles * ((a.N + rows - 1) / rows);
     const long long per_xcd = (max_items + 7) / 8;
     const int nl = int(std::min<long long>(32, per_xcd));
-    if (nl <= 0 || a.K % (2 * BK) || (per_xcd + nl - 1) / nl > kPersistMaxItems) return false;
+    // whole K steps, at least NST - 1 of them per item (the DMA runs that far ahead)
+    if (nl <= 0 || a.K % KS || a.K / KS < NST - 1 || (per_xcd + nl - 1) / nl > kPersistMaxItems) return false;
     if ((unsigned long long)a.n_act_rows * a.K * 2 >= (1ull << 32) ||
         (unsigned long long)rows * a.K * 2 >= (1ull << 32))
         return false;
     const dim3 g(unsigned(8 * nl)), b(C::THREADS);
     // stores address the output with 32-bit offsets below the drop offset
     if ((unsigned long long)a.n_pairs * a.N * (outbf || mode == kRoutedGateUp ? 2 : 4) >= (1ull << 31)) return false;
-    if (mode == kRoutedGateUp) gemm_routed_dma_kernel<kRoutedGateUp, true, C><<<g, b, 0, s>>>(a);
-    else if (outbf) gemm_routed_dma_kernel<kRoutedDown, true, C><<<g, b, 0, s>>>(a);
-    else gemm_routed_dma_kernel<kRoutedDown, false, C><<<g, b, 0, s>>>(a);
+    if (mode == kRoutedGateUp) gemm_routed_dma_kernel<kRoutedGateUp, true, C, KS, NST><<<g, b, 0, s>>>(a);
+    else if (outbf) gemm_routed_dma_kernel<kRoutedDown, true, C, KS, NST><<<g, b, 0, s>>>(a);
+    else gemm_routed_dma_kernel<kRoutedDown, false, C, KS, NST><<<g, b, 0, s>>>(a);
     return true;
 }
 

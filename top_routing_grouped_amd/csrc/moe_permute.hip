@@ -39,10 +39,10 @@ int max_tiles_for(int n_pairs, int E, int tile_rows) {
 
 // Many pairs: three launches over chunks of kPermChunk pairs.
 //  1. count: each chunk's per-expert histogram (LDS atomics) -> chunk_base[c][e];
-//  2. scan (one workgroup): per expert, the exclusive prefix over chunks and
-//     the total; the totals give offsets, the active list and the tile list,
-//     and chunk_base[c][e] becomes the position of chunk c's first pair of
-//     expert e;
+//  2. scan (one workgroup, threads over experts x slices of chunks): per
+//     expert, the exclusive prefix over chunks and the total; the totals give
+//     offsets, the active list and the tile list, and chunk_base[c][e] becomes
+//     the position of chunk c's first pair of expert e;
 //  3. scatter: each chunk ranks its pairs within their expert (ballots over
 //     the id bits inside a wave, earlier waves' counts through LDS) and writes
 //     them from chunk_base, so pairs stay in ascending pair-id order inside
@@ -63,18 +63,34 @@ __global__ __launch_bounds__(256) void permute_count_kernel(PermParams P) {
 
 __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(PermParams P, int nchunks) {
     __shared__ int sh[32];
-    // chunk counts held in registers G at a time: unconditional loads from
-    // clamped addresses, so they are all in flight together
+    __shared__ int part[kPermThreads];  // per (slice, expert): the slice's count of the expert's pairs
+    __shared__ int off_l[kPermThreads];  // per expert: its offset
+    // Thread (slice sl, expert e) = tid: the chunks split into S contiguous
+    // slices, one per group of E threads; a thread's first G chunk counts are
+    // loaded in one round trip (unconditional loads from clamped addresses)
+    // and kept in registers for the second pass.
     constexpr int G = 16;
     const int E = P.E, tid = threadIdx.x;
-    int total = 0;
-    if (tid < E) {
-        for (int c0 = 0; c0 < nchunks; c0 += G) {
-            int v[G];
+    const int S = max(1, kPermThreads / E);
+    const int e = tid % E, sl = tid / E;
+    const bool act = sl < S;
+    const int per = (nchunks + S - 1) / S;
+    const int c0 = act ? min(nchunks, sl * per) : nchunks, c1 = min(nchunks, c0 + per);
+    int v[G];
 #pragma unroll
-            for (int i = 0; i < G; ++i) v[i] = P.chunk_base[size_t(min(c0 + i, nchunks - 1)) * E + tid];
+    for (int i = 0; i < G; ++i) v[i] = P.chunk_base[size_t(min(c0 + i, nchunks - 1)) * E + e];
+    int sum = 0;
 #pragma unroll
-            for (int i = 0; i < G; ++i) total += c0 + i < nchunks ? v[i] : 0;
+    for (int i = 0; i < G; ++i) sum += c0 + i < c1 ? v[i] : 0;
+    for (int c = c0 + G; c < c1; ++c) sum += P.chunk_base[size_t(c) * E + e];  // slices longer than G
+    part[tid] = act ? sum : 0;
+    __syncthreads();
+    int total = 0, before = 0;
+    if (act) {
+        for (int q = 0; q < S; ++q) {
+            const int n = part[q * E + e];
+            total += n;
+            before += q < sl ? n : 0;
         }
     }
     const int cnt = tid < E ? total : 0;
@@ -85,23 +101,27 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(PermParams P
     const int tpos = block_exclusive_scan(P.tiles ? nt : 0, &n_tiles, sh);
     if (tid < E) {
         P.offsets[tid] = off;
+        off_l[tid] = off;
         if (cnt > 0) {
             P.active[apos] = tid;
             if (P.tiles) write_tiles(P.tiles, tpos, tid, off, cnt, P.tile_rows, P.max_tiles);
         }
-        // chunk c's first pair of expert tid goes to off + (its pairs in chunks < c)
-        int run = off;
-        for (int c0 = 0; c0 < nchunks; c0 += G) {
-            int v[G];
+    }
+    __syncthreads();
+    if (act) {
+        // chunk c's first pair of expert e goes to off + (its pairs in chunks < c)
+        int run = off_l[e] + before;
 #pragma unroll
-            for (int i = 0; i < G; ++i) v[i] = P.chunk_base[size_t(min(c0 + i, nchunks - 1)) * E + tid];
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-                if (c0 + i < nchunks) {
-                    P.chunk_base[size_t(c0 + i) * E + tid] = run;
-                    run += v[i];
-                }
+        for (int i = 0; i < G; ++i) {
+            if (c0 + i < c1) {
+                P.chunk_base[size_t(c0 + i) * E + e] = run;
+                run += v[i];
             }
+        }
+        for (int c = c0 + G; c < c1; ++c) {
+            const int n = P.chunk_base[size_t(c) * E + e];
+            P.chunk_base[size_t(c) * E + e] = run;
+            run += n;
         }
     }
     if (tid == 0) {

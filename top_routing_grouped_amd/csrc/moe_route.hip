@@ -22,39 +22,44 @@
 
 namespace moe {
 
-// One wave per token; blocks of 4 tokens.  Optionally also the shared-expert
-// gate logit w_shared . x_t of the token (Treebeard, "Shared expert
-// computation"), issued first so its loads overlap the selection.
-template <int NV>
+// One wave per token, blocks of 4 tokens; or (softmax family, PAIR) one wave
+// per two tokens, blocks of 8, whose selection chains interleave.
+// Optionally also the shared-expert gate logit w_shared . x_t of the token
+// (Treebeard, "Shared expert computation").
+template <int NV, bool PAIR>
 __global__ __launch_bounds__(256) void route_select_kernel(SelParams P, GateParams G, int32_t* __restrict__ ids,
                                                            float* __restrict__ wts) {
     __shared__ float sel_s[4][64 * NV];
     __shared__ float sig_s[4][64 * NV];
+    constexpr int B = PAIR ? 2 : 1;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + wave;
-    if (t >= P.T) return;  // no block-wide barrier below
-    int id;
-    float w;
-    if (P.family == 0) {
-        const int tt[1] = {t};
-        int ids1[1];
-        float w1[1];
-        select_softmax_lanes<NV, 1>(P, tt, ids1, w1);
-        id = ids1[0];
-        w = w1[0];
+    const int t0 = blockIdx.x * 4 * B + wave;
+    if (t0 >= P.T) return;  // no block-wide barrier below
+    int id[B];
+    float w[B];
+    int tt[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) tt[b] = min(t0 + 4 * b, P.T - 1);  // a clamped second token repeats the last
+    if (PAIR || P.family == 0) {
+        select_softmax_lanes<NV, B>(P, tt, id, w);
     } else {
-        select_token<NV>(P, t, sel_s[wave], sig_s[wave], &id, &w);
+        select_token<NV>(P, t0, sel_s[wave], sig_s[wave], &id[0], &w[0]);
     }
-    float gl = 0.f;
-    if (G.w) gl = wave_dot_row(G.x, G.w, t, G.D, G.x_f32 != 0);
-    if (lane < P.K) {
-        const size_t o = size_t(t) * P.K + lane;
-        ids[o] = id;
-        wts[o] = w;
-        if (P.ids2) P.ids2[o] = id;
-        if (P.wts2) P.wts2[o] = w;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const int t = t0 + 4 * b;
+        if (t >= P.T) break;
+        float gl = 0.f;
+        if (G.w) gl = wave_dot_row(G.x, G.w, t, G.D, G.x_f32 != 0);
+        if (lane < P.K) {
+            const size_t o = size_t(t) * P.K + lane;
+            ids[o] = id[b];
+            wts[o] = w[b];
+            if (P.ids2) P.ids2[o] = id[b];
+            if (P.wts2) P.wts2[o] = w[b];
+        }
+        if (G.w && lane == 0) G.out[t] = gl;
     }
-    if (G.w && lane == 0) G.out[t] = gl;
 }
 
 // Small T: every token's selection, then the permute, in one 1024-thread
@@ -89,7 +94,11 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_kernel(SelParams P
 
 template <int NV>
 static void launch_nv(const SelParams& P, const GateParams& G, int32_t* ids, float* wts, hipStream_t s) {
-    route_select_kernel<NV><<<(P.T + 3) / 4, 256, 0, s>>>(P, G, ids, wts);
+    // many tokens, softmax family: two tokens per wave
+    if (P.family == 0 && P.T >= 1024 && NV <= 8)
+        route_select_kernel<NV, true><<<(P.T + 7) / 8, 256, 0, s>>>(P, G, ids, wts);
+    else
+        route_select_kernel<NV, false><<<(P.T + 3) / 4, 256, 0, s>>>(P, G, ids, wts);
 }
 
 hipError_t launch_route_select_gate(const SelParams& P, const GateParams& G, int32_t* ids, float* weights,
