@@ -134,8 +134,21 @@ Layout layout(const moe_config& c) {
     return L;
 }
 
+// The value a C caller stored in an enum-typed field or argument, read as
+// the 32-bit integer the ABI passes: C allows any int there, and loading an
+// out-of-range value through the C++ enum type is undefined.
+template <class E>
+int32_t raw(const E& v) {
+    static_assert(sizeof(E) == sizeof(int32_t), "enums are 32-bit in this ABI");
+    int32_t r;
+    std::memcpy(&r, &v, sizeof r);
+    return r;
+}
+
 moe_status check_config(const moe_config* c) {
     if (!c) return fail(MOE_ERR_INVALID_ARGUMENT, "config is NULL");
+    const int32_t family = raw(c->family), act = raw(c->act_dtype), rdt = raw(c->router_dtype),
+                  edt = raw(c->expert_dtype);
     if (c->n_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "n_tokens < 0");
     if (c->d_model <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->d_ff <= 0 || c->d_ff_shared < 0)
         return fail(MOE_ERR_INVALID_ARGUMENT, "sizes must be positive (d_ff_shared >= 0)");
@@ -143,9 +156,9 @@ moe_status check_config(const moe_config* c) {
     if (c->top_k > 32) return fail(MOE_ERR_UNSUPPORTED, "top_k > 32");
     if (c->n_experts > 1024 || c->n_experts % 16) return fail(MOE_ERR_UNSUPPORTED, "n_experts must be a multiple of 16, <= 1024");
     if ((int64_t)c->n_tokens * c->top_k > (int64_t(1) << 30)) return fail(MOE_ERR_UNSUPPORTED, "n_tokens * top_k too large");
-    if (c->family != MOE_ROUTE_SOFTMAX_TOPK && c->family != MOE_ROUTE_SIGMOID_GROUP_TOPK)
+    if (family != MOE_ROUTE_SOFTMAX_TOPK && family != MOE_ROUTE_SIGMOID_GROUP_TOPK)
         return fail(MOE_ERR_INVALID_ARGUMENT, "unknown routing family");
-    if (c->family == MOE_ROUTE_SIGMOID_GROUP_TOPK) {
+    if (family == MOE_ROUTE_SIGMOID_GROUP_TOPK) {
         const int E = c->n_experts, G = c->n_group, TG = c->topk_group;
         if (G < 1 || G > 64) return fail(MOE_ERR_INVALID_ARGUMENT, "n_group must be in [1, 64]");
         if (E % G || E / G < 2) return fail(MOE_ERR_INVALID_ARGUMENT, "n_experts must split into n_group groups of >= 2");
@@ -154,17 +167,17 @@ moe_status check_config(const moe_config* c) {
         if (!(std::isfinite(c->routed_scaling) && c->routed_scaling > 0.f))
             return fail(MOE_ERR_INVALID_ARGUMENT, "routed_scaling must be finite and > 0");
     }
-    const bool f32 = c->act_dtype == MOE_F32;
-    if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "act_dtype must be F32 or BF16");
-    if (c->router_dtype != c->act_dtype) return fail(MOE_ERR_UNSUPPORTED, "router_dtype must equal act_dtype");
-    if (f32 ? c->expert_dtype != MOE_F32 : (c->expert_dtype != MOE_BF16 && c->expert_dtype != MOE_U4_AFFINE_G64))
+    const bool f32 = act == MOE_F32;
+    if (act != MOE_F32 && act != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "act_dtype must be F32 or BF16");
+    if (rdt != act) return fail(MOE_ERR_UNSUPPORTED, "router_dtype must equal act_dtype");
+    if (f32 ? edt != MOE_F32 : (edt != MOE_BF16 && edt != MOE_U4_AFFINE_G64))
         return fail(MOE_ERR_UNSUPPORTED, "expert_dtype must be F32 with F32 activations, BF16 or U4_AFFINE_G64 with BF16");
-    if (c->expert_dtype == MOE_U4_AFFINE_G64 &&
+    if (edt == MOE_U4_AFFINE_G64 &&
         (c->d_model > 64 * moe::kU4MaxGroups || c->d_ff > 64 * moe::kU4MaxGroups ||
          c->d_ff_shared > 64 * moe::kU4MaxGroups))
         return fail(MOE_ERR_UNSUPPORTED, "4-bit weights: d_model, d_ff and d_ff_shared must be <= %d",
                     64 * moe::kU4MaxGroups);
-    const int span = kspan_of(c->expert_dtype);
+    const int span = edt == MOE_F32 ? 16 : 128;
     if (c->d_model % span || c->d_ff % span || c->d_ff_shared % span)
         return fail(MOE_ERR_UNSUPPORTED, "d_model, d_ff, d_ff_shared must be multiples of %d for this dtype", span);
     return MOE_OK;
@@ -627,8 +640,8 @@ moe_status scratch_ptr(void** out) {
 
 extern "C" {
 
-const char* moe_status_string(moe_status st) {
-    switch (st) {
+const char* moe_status_string(moe_status status) {
+    switch (raw(status)) {
         case MOE_OK: return "MOE_OK";
         case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
         case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
@@ -846,11 +859,12 @@ moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, co
     int32_t* pairs = at<int32_t>(ws, L.pairs);
     int4* tiles = at<int4>(ws, L.tiles);
     int32_t* nt = at<int32_t>(ws, L.n_tiles);
-    switch (stage) {
+    const int32_t stage_v = raw(stage);
+    switch (stage_v) {
         case MOE_STAGE_ROUTER_LOGITS: return stage_logits(c, L, ws, x, weights->router, stream);
         case MOE_STAGE_GATE_UP:
         case MOE_STAGE_GATE_UP_DIRECT: {
-            const bool direct = stage == MOE_STAGE_GATE_UP_DIRECT;
+            const bool direct = stage_v == MOE_STAGE_GATE_UP_DIRECT;
             if (!small_path(c)) {
                 if (direct) return fail(MOE_ERR_UNSUPPORTED, "the direct gate/up stage needs the small-T path");
                 return stage_gateup(c, L, ws, x, *weights, pairs, tiles, nt, stream);
@@ -872,7 +886,7 @@ moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, co
         case MOE_STAGE_DOWN_GROUPED:
         case MOE_STAGE_DOWN_DIRECT:
             if (!small_path(c)) return fail(MOE_ERR_UNSUPPORTED, "the unfused small-T down stages need the small-T path");
-            return stage_small_down(c, L, ws, *weights, stream, stage == MOE_STAGE_DOWN_DIRECT);
+            return stage_small_down(c, L, ws, *weights, stream, stage_v == MOE_STAGE_DOWN_DIRECT);
         case MOE_STAGE_DOWN:
             if (down_combine_fused(c)) {
                 // the layer's own launch, writing into the workspace (y_shared region,
@@ -885,7 +899,7 @@ moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, co
             return stage_down(c, L, ws, *weights, pairs, tiles, nt, at<float>(ws, L.wts), at<void>(ws, L.slots),
                               c.expert_dtype != MOE_F32, stream);
     }
-    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown stage %d", int(stage));
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown stage %d", int(stage_v));
 }
 
 }  // extern "C"
