@@ -417,6 +417,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < TF; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // routed down: each token column's pair id (its store row and routing
+    // weight) is requested before the K loop, so it arrives during it
+    [[maybe_unused]] int down_pair[TF];
+    if constexpr (MODE == kRoutedDown) {
+#pragma unroll
+        for (int j = 0; j < TF; ++j) down_pair[j] = a.pairs[begin + min(j * 16 + r, count - 1)];
+    }
+
     // 4-bit gate/up weights: the group scales and mins of this workgroup's
     // weight rows (16 * WN rows over its K range) are staged in LDS once, 16
     // bytes per load where aligned, as (scale | min << 16) words.  Loading the
@@ -549,7 +557,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
             // trip's loads are in flight while this trip waits and multiplies
             // (a wave otherwise has nothing in flight between receiving a trip
             // and issuing the next).  The last pair of trips is peeled: the
-            // loop body has no conditional load.
+            // loop body has no conditional load.  (4-bit chunks held as loaded
+            // and dequantised at use measured slower: 4-bit T = 64 layer 137
+            // -> 144 us, one wave per SIMD fewer.)
             Frag<false> wb[2][U][NM];
             Frag<false> xc[2][U][TF];
             auto issue = [&](auto b_c, int t) __attribute__((always_inline)) {
@@ -563,7 +573,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                     for (int j = 0; j < TF; ++j) load_x<WK>(xc[B][i][j], xrow[j], kc, q);
                 }
             };
-            auto mmas = [&](auto b_c) __attribute__((always_inline)) {
+            auto mmas = [&](auto b_c, int) __attribute__((always_inline)) {
                 constexpr int B = decltype(b_c)::value;
 #pragma unroll
                 for (int i = 0; i < U; ++i)
@@ -580,15 +590,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                 for (int p = 0; p + 1 < npair; ++p) {
                     issue(I1, 2 * p + 1);
                     __builtin_amdgcn_sched_barrier(0);
-                    mmas(I0);
+                    mmas(I0, 2 * p);
                     issue(I0, 2 * p + 2);
                     __builtin_amdgcn_sched_barrier(0);
-                    mmas(I1);
+                    mmas(I1, 2 * p + 1);
                 }
                 issue(I1, 2 * npair - 1);
                 __builtin_amdgcn_sched_barrier(0);
-                mmas(I0);
-                mmas(I1);
+                mmas(I0, 2 * npair - 2);
+                mmas(I1, 2 * npair - 1);
                 c = npair * 2 * U;
             }
         }
@@ -646,7 +656,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
             else
                 dest = size_t(begin + i);
         } else if constexpr (MODE == kRoutedDown) {
-            const int pair = a.pairs[begin + i];
+            const int pair = down_pair[j];
             if (pair < 0 || pair >= a.n_pairs) continue;
             const float s = a.row_scale[pair];
 #pragma unroll

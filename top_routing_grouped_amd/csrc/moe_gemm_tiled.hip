@@ -507,10 +507,14 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
     auto pair_index = [&](int4 it, int row) __attribute__((always_inline)) {
         return it.y + (row < it.z ? row : 0);
     };
+    // byte offset of this lane's piece of a token row; rows past the tile
+    // (partial tiles: every cold expert's, each expert's last) get an
+    // offset past the buffer's records, which the hardware answers with
+    // zeros and no memory request (their columns are never stored)
     auto x_offset = [&](int j, int pair_or_row, bool valid) __attribute__((always_inline)) {
         int arow = pair_or_row;
         if constexpr (DUAL) arow = (pair_or_row >= 0 && pair_or_row < a.n_pairs) ? pair_or_row / a.topk : -1;
-        if (!valid || arow < 0 || arow >= a.n_act_rows) arow = 0;
+        if (!valid || arow < 0 || arow >= a.n_act_rows) return kDropOffset;
         return uint32_t((arow * K + 8 * bpiece[j]) * 2);
     };
     // K step kt of an item into LDS stage st
