@@ -14,7 +14,8 @@ region, which is bracketed by device synchronisation and HIP events.
 
 Prints one JSON line: tokens/s of the Qwen3.6-35B-A3B layer at decode shape
 (T = 8), the roofline of its dominant kernel (routed gate/up GEMM, timed
-alone with HIP events over re-launches of that stage on the same routing),
+with HIP events as the layer runs it: re-launched right after the router launch on
+the same routing, less the router alone),
 the fp64 oracle timed on the host cores on a bounded sample, and the
 T = 4096 skewed prefill layer as a secondary entry.
 """
@@ -235,15 +236,17 @@ def single_layer_ms(insts, reps=10, flush_bytes=0):
 
 
 def time_stage(insts, stage, reps):
-    """Average duration of one stage launch, re-launched `reps` times in one
-    captured graph over the instances' real routing; HIP events on the
-    replay stream."""
+    """Average duration of one stage launch (or of a sequence of stage
+    launches, given a tuple), re-launched `reps` times in one captured graph
+    over the instances' real routing; HIP events on the replay stream."""
     L = len(insts)
+    stages = stage if isinstance(stage, tuple) else (stage,)
     cap = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=cap):
         for i in range(reps):
-            insts[i % L].stage(stage)
+            for st in stages:
+                insts[i % L].stage(st)
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
@@ -368,6 +371,33 @@ def copy_calibration(nbytes=1 << 30):
     log(f"copy calibration: {nbytes} bytes")
 
 
+def hbm_reference(nbytes=1 << 30, reps=10):
+    """The chip's streaming rate through plain library kernels, as a reference
+    for the roofline fractions: a device-to-device copy of `nbytes` (reads and
+    writes nbytes) and a read-only pass (a sum over `nbytes` of fp32), each
+    over distinct buffers larger than the 256 MB last-level cache, HIP events
+    around `reps` launches."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
+                            ("read", lambda: torch.sum(src, out=out), nbytes)):
+        fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        res[f"{name}_GBps"] = round(moved * reps / (s.elapsed_time(e) / 1e3) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    res["bytes"] = nbytes
+    return res
+
+
 def run_workload(name, T, L, steps, warmup, stage_reps):
     spec = WORKLOADS[name].with_tokens(T)
     insts = build_instances(spec, L, f"{name} T={T}")
@@ -380,7 +410,13 @@ def run_workload(name, T, L, steps, warmup, stage_reps):
     byts = float(np.mean([layer_bytes(spec, a) for a in n_act]))
     flops = layer_flops(spec)
     t = ms / 1e3
-    stage_ms = time_stage(insts, moe.STAGE_GATE_UP, stage_reps)
+    # the routed gate/up launch as the layer runs it: right after the router
+    # launch (router + gate/up pairs, less the router alone); the stage
+    # re-launched back to back is reported beside it
+    router_ms = time_stage(insts, moe.STAGE_ROUTER_LOGITS, stage_reps)
+    pair_ms = time_stage(insts, (moe.STAGE_ROUTER_LOGITS, moe.STAGE_GATE_UP), stage_reps)
+    alone_stage_ms = time_stage(insts, moe.STAGE_GATE_UP, stage_reps)
+    stage_ms = pair_ms - router_ms
     gu_bytes = float(np.mean([gateup_bytes(spec, a) for a in n_act]))
     gu_flops = gateup_flops(spec)
     gu_t = stage_ms / 1e3
@@ -392,7 +428,8 @@ def run_workload(name, T, L, steps, warmup, stage_reps):
         "mfma_ceiling": t_mfma / max(t_hbm, t_mfma),
         "n_active_mean": mean_act, "layer_bytes": byts, "layer_flops": flops,
         "layer_hbm_frac": byts / t / (HBM_PEAK_GBS * 1e9), "layer_mfma_frac": flops / t / (BF16_PEAK_TFLOPS * 1e12),
-        "gateup_ms": stage_ms, "gateup_bytes": gu_bytes, "gateup_flops": gu_flops,
+        "gateup_ms": stage_ms, "gateup_alone_ms": alone_stage_ms, "router_ms": router_ms,
+        "gateup_bytes": gu_bytes, "gateup_flops": gu_flops,
         "gateup_gbs": gu_bytes / gu_t / 1e9, "gateup_tflops": gu_flops / gu_t / 1e12,
     }
     log(f"{name} T={T}: {ms * 1e3:.1f} us/layer, {T / t:,.0f} tok/s, n_active {mean_act:.1f}, "
@@ -530,6 +567,7 @@ def prefill_roofline(pre):
     r.update(mfma if bound == "mfma" else hbm)
     r.update({"intensity_flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1),
               "other": other, "launch_us": round(pre["gateup_ms"] * 1e3, 2),
+              "launch_us_back_to_back": round(pre["gateup_alone_ms"] * 1e3, 2),
               "algorithmic_bytes": round(pre["gateup_bytes"]), "algorithmic_flops": round(pre["gateup_flops"]),
               "traffic": traffic_record("gateup", "qwen_prefill_T4096", pre["gateup_bytes"])})
     return r
@@ -655,6 +693,8 @@ def main():
         big = T > 512
         run_workload(args.workload, T, min(args.instances, 4) if big else args.instances, args.steps, args.warmup,
                      args.stage_reps)
+        if args.copy_calibration:
+            copy_calibration()
         return
     if args.only == "chain":
         chained_decode(args, float("nan"))
@@ -708,8 +748,12 @@ def main():
                      "achieved": round(dec["gateup_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec["gateup_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": gu_traffic, "launch_us": round(dec["gateup_ms"] * 1e3, 3),
+                     "launch_us_measured_as": "router + gate/up launch pairs less the router alone, "
+                                              f"{args.stage_reps} of each in captured graphs over the instances' routing",
+                     "launch_us_back_to_back": round(dec["gateup_alone_ms"] * 1e3, 3),
                      "algorithmic_bytes": round(dec["gateup_bytes"])},
     }
+    line["hbm_reference"] = hbm_reference()
     if not args.no_chain:
         line["chained_decode"] = chained_decode(args, dec["ms_per_step"] * 1e3)
     if not args.no_cpu_baseline:
