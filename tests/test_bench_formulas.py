@@ -54,3 +54,29 @@ def test_small_path_rule_matches_library():
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True, timeout=120)
     assert r.returncode != 0 and "one GPU" in (r.stdout + r.stderr)
+
+
+def test_chain_length_divides_steps_within_the_instances():
+    assert bench.chain_length(20, 40) == 20
+    assert bench.chain_length(800, 40) == 40
+    assert bench.chain_length(50, 40) == 25
+    assert bench.chain_length(41, 40) == 1
+    for steps in range(1, 120):
+        c = bench.chain_length(steps, 40)
+        assert steps % c == 0 and 1 <= c <= 40
+
+
+def test_streaming_reference_ops_run_and_count_bytes():
+    import torch
+    src = torch.arange(1024, dtype=torch.float32)
+    dst, out = torch.empty_like(src), torch.empty(())
+    ops = bench.stream_ops(src, dst, out)
+    assert [o[0] for o in ops] == ["copy", "read"] and [o[2] for o in ops] == [8192, 4096]
+    for _, fn, _ in ops:
+        fn()
+    assert torch.equal(dst, src) and out.item() == float(sum(range(1024)))
+
+
+def test_host_description_reports_cores_and_blas():
+    d = bench.host_description()
+    assert d["cores"] >= 1 and isinstance(d["cpu_model"], str) and isinstance(d["blas"], str)
