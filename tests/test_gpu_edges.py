@@ -124,8 +124,9 @@ def test_layer_sigmoid_group_degenerate(G, TG, K, bias, T):
 # Token counts on both sides of every switch of the schedule at E=32, K=4:
 # selection folded into the gate/up launch (T <= 8), dense 64-token tiles
 # (T >= 64), the small-T path (T*K <= 256), the tiled router and shared expert
-# (T >= 128), the tiled routed GEMMs (bf16: T*K >= 16 E; 4-bit: >= 64 E) and the
-# chunked permute (T*K >= 4096).
+# (T >= 128), the tiled routed GEMMs (bf16: T*K >= 16 E; 4-bit with d_ff 128,
+# too short a reduction for the tiled 4-bit kernel: 64-token register tiles
+# from T*K >= 64 E) and the chunked permute (T*K >= 4096).
 BOUNDARY_T = [8, 9, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1023, 1024]
 
 

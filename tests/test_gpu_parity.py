@@ -22,7 +22,8 @@ SMALL = {
     "small_sigmoid": ("sigmoid_group", dict(d_model=256, n_experts=32, n_group=4, topk_group=2, top_k=4,
                                             d_ff=128, d_ff_shared=128)),
     "small_u4": ("qwen_u4", dict(d_model=256, n_experts=32, top_k=4, d_ff=128, d_ff_shared=128)),
-    # d_ff 256: the fused down + combine launch with 4-bit weights at small T
+    # d_ff 256: the fused down + combine launch with 4-bit weights at small T,
+    # and from T = 128 (16 pairs per expert) the tiled 4-bit routed GEMMs
     "small_u4_f256": ("qwen_u4", dict(d_model=256, n_experts=32, top_k=4, d_ff=256, d_ff_shared=256)),
 }
 SMALL_T = [1, 37, 100, 301, 700]  # 100: bf16 experts average < 16 pairs above the small path (16-token tiles)

@@ -51,7 +51,31 @@ bool routed_large(const moe_config& c) {
     const int64_t per_expert = c.expert_dtype == MOE_BF16 ? 16 : 64;
     return (int64_t)c.n_tokens * c.top_k >= per_expert * c.n_experts;
 }
-bool routed_tiled(const moe_config& c) { return routed_large(c) && c.expert_dtype == MOE_BF16; }
+int64_t max_tiles(int64_t n_pairs, int E, int tile_rows) {
+    const int64_t act = std::min<int64_t>(E, n_pairs);
+    return (n_pairs + act * (tile_rows - 1)) / tile_rows;
+}
+// 4-bit banks averaging at least kU4TiledMinPairs pairs per expert use the
+// persistent LDS-tiled kernel (codes and group scales staged in LDS,
+// 128-token tiles) where both routed GEMMs fit it; fewer pairs keep the
+// register tiles (measured at Qwen3.6 shape, K = 4: 16 pairs per expert,
+// T = 1024, layer 328 -> 268 us on the tiled kernel; 8 pairs, T = 512,
+// 222 -> 238 us).
+#ifndef MOE_U4_TILED_MIN_PAIRS
+#define MOE_U4_TILED_MIN_PAIRS 16
+#endif
+constexpr int kU4TiledMinPairs = MOE_U4_TILED_MIN_PAIRS;
+bool routed_tiled_u4(const moe_config& c) {
+    if (c.expert_dtype != MOE_U4_AFFINE_G64) return false;
+    const int64_t TK = (int64_t)c.n_tokens * c.top_k;
+    if (TK < (int64_t)kU4TiledMinPairs * c.n_experts || TK >= (int64_t(1) << 31)) return false;
+    const int mt = int(max_tiles(TK, c.n_experts, moe::tiled_rows()));
+    return moe::routed_tiled_u4_fits(moe::kRoutedGateUp, c.d_ff, c.d_model, mt, c.n_tokens, int(TK), true) &&
+           moe::routed_tiled_u4_fits(moe::kRoutedDown, c.d_model, c.d_ff, mt, int(TK), int(TK), false);
+}
+bool routed_tiled(const moe_config& c) {
+    return (routed_large(c) && c.expert_dtype == MOE_BF16) || routed_tiled_u4(c);
+}
 int routed_tf(const moe_config& c) { return routed_large(c) ? 4 : 1; }
 int routed_tile_rows(const moe_config& c) { return routed_tiled(c) ? moe::tiled_rows() : 16 * routed_tf(c); }
 int dense_tf(const moe_config& c) { return c.n_tokens >= 64 ? 4 : 1; }
@@ -59,7 +83,9 @@ bool dense_tiled(const moe_config& c, moe_dtype d) { return c.n_tokens >= 128 &&
 // Small T*K: one stream; every GEMM workgroup finds its expert and pairs from
 // the routing ids itself (no permute launch) and the shared expert is an
 // extra work item of the routed launches.
-bool small_path(const moe_config& c) { return !routed_large(c) && (int64_t)c.n_tokens * c.top_k <= 256; }
+bool small_path(const moe_config& c) {
+    return !routed_large(c) && !routed_tiled_u4(c) && (int64_t)c.n_tokens * c.top_k <= 256;
+}
 int h_ld(const moe_config& c) { return std::max(c.d_ff, c.d_ff_shared); }
 // Small path with bf16 or 4-bit weights: the down projection and the combine
 // are one launch (each workgroup owns a slice of output features for every
@@ -89,11 +115,6 @@ int router_ksplit(const moe_config& c) {
     for (int s = 8; s > 1; --s)
         if (c.d_model % (s * per) == 0) return s;
     return 1;
-}
-
-int64_t max_tiles(int64_t n_pairs, int E, int tile_rows) {
-    const int64_t act = std::min<int64_t>(E, n_pairs);
-    return (n_pairs + act * (tile_rows - 1)) / tile_rows;
 }
 
 struct Layout {
@@ -305,6 +326,10 @@ moe_status stage_gateup(const moe_config& c, const Layout& L, void* ws, const vo
     a.act = x; a.n_act_rows = T;
     a.tiles = tiles; a.n_tiles = n_tiles; a.pairs = pairs; a.n_pairs = TK; a.topk = K;
     a.out = at<void>(ws, L.h);
+    if (routed_tiled_u4(c)) {
+        HIP_TRY(moe::launch_gemm_routed_u4(moe::kRoutedGateUp, true, a, int(max_tiles(TK, c.n_experts, routed_tile_rows(c))), s));
+        return MOE_OK;
+    }
     if (routed_tiled(c)) {
         HIP_TRY(moe::launch_gemm_tiled(moe::kRoutedGateUp, true, a, int(max_tiles(TK, c.n_experts, routed_tile_rows(c))), s));
         return MOE_OK;
@@ -323,6 +348,10 @@ moe_status stage_down(const moe_config& c, const Layout& L, void* ws, const moe_
     d.act = at<void>(ws, L.h); d.n_act_rows = TK;
     d.tiles = tiles; d.n_tiles = n_tiles; d.pairs = pairs; d.n_pairs = TK; d.topk = K;
     d.out = slot_out; d.row_scale = wts;
+    if (routed_tiled_u4(c)) {
+        HIP_TRY(moe::launch_gemm_routed_u4(moe::kRoutedDown, slot_bf16, d, int(max_tiles(TK, c.n_experts, routed_tile_rows(c))), s));
+        return MOE_OK;
+    }
     if (routed_tiled(c)) {
         HIP_TRY(moe::launch_gemm_tiled(moe::kRoutedDown, slot_bf16, d, int(max_tiles(TK, c.n_experts, routed_tile_rows(c))), s));
         return MOE_OK;

@@ -38,6 +38,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2_split(float lo, float hi) {
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// 4-bit codes: the low nibbles (even elements) and the high nibbles (odd
+// elements) of a word of 8 codes, one code per byte.  OPAQUE: the two
+// registers are hidden from the compiler, so that each byte converts with
+// one v_cvt_f32_ubyteN; seeing the masks, it extracts every nibble with a
+// bit-field extract before a byte-0 conversion (two instructions a code, but
+// only the word stays live: fewer registers).
+template <bool OPAQUE>
+__device__ __forceinline__ void nibble_bytes(uint32_t w, uint32_t& even, uint32_t& odd) {
+    even = w & 0x0f0f0f0fu;
+    odd = (w >> 4) & 0x0f0f0f0fu;
+    if constexpr (OPAQUE) {
+        asm("" : "+v"(even));
+        asm("" : "+v"(odd));
+    }
+}
+// The register-streaming 4-bit kernels keep the plain form: with the opaque
+// one they hold a wave per SIMD fewer and measured slower (Qwen3.6 shape,
+// K = 4: T = 64 layer 136.4 -> 140.5 us, T = 512 219.4 -> 227.6 us); the
+// LDS-tiled kernel, whose occupancy its LDS fixes, gained 2-3%.
+constexpr bool kU4OpaqueReg = false;
+
 // ------------------------------------------------------------ wave64 reductions
 // Butterfly reductions: every lane ends with the same value; the combination
 // order is fixed by lane position, so results are deterministic.

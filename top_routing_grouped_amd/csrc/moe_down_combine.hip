@@ -58,7 +58,8 @@ __device__ __forceinline__ float dot_u4_piece(const u32x4& c, float s, float m, 
     const uint32_t words[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t even = words[i] & 0x0f0f0f0fu, odd = (words[i] >> 4) & 0x0f0f0f0fu;
+        uint32_t even, odd;
+        nibble_bytes<kU4OpaqueReg>(words[i], even, odd);
         const uint32_t h0 = h[i].x, h1 = h[i].y, h2 = h[i].z, h3 = h[i].w;
         const uint32_t hp[4] = {h0, h1, h2, h3};
 #pragma unroll

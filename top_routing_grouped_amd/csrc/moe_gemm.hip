@@ -96,11 +96,12 @@ __device__ __forceinline__ void load_w(Frag<WK == kWF32>& f, const void* w, cons
         const uint32_t words[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            uint32_t packed[4];
+            uint32_t packed[4], even, odd;
+            nibble_bytes<kU4OpaqueReg>(words[j], even, odd);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float lo = fmaf(s, float((words[j] >> (8 * i)) & 0xfu), m);
-                const float hi = fmaf(s, float((words[j] >> (8 * i + 4)) & 0xfu), m);
+                const float lo = fmaf(s, float((even >> (8 * i)) & 0xffu), m);
+                const float hi = fmaf(s, float((odd >> (8 * i)) & 0xffu), m);
                 packed[i] = pack_bf16x2_split(lo, hi);
             }
             f.v[j] = as_bf16x8(make_uint4(packed[0], packed[1], packed[2], packed[3]));
@@ -118,7 +119,8 @@ __device__ __forceinline__ void load_w_u4_staged(Frag<false>& f, const void* w, 
     const uint32_t words[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint32_t even = words[j] & 0x0f0f0f0fu, odd = (words[j] >> 4) & 0x0f0f0f0fu;
+        uint32_t even, odd;
+        nibble_bytes<kU4OpaqueReg>(words[j], even, odd);
         uint32_t packed[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

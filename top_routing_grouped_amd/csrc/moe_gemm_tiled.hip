@@ -56,6 +56,14 @@ struct Cfg {
 // against 256 x 256 (one stage: fewer steps in flight), 128 x 128 (two
 // workgroups per CU: twice the bytes per MFMA) and 16-wave shapes (spills).
 using CfgLarge = Cfg<256, 128, 4, 2, 2, 1>;
+// 4-bit routed experts: the same tile with the 8 waves as 8 x 1, so that
+// each weight fragment is dequantised by one wave only (measured at Qwen3.6
+// shape, K = 4: T = 4096 layer 539 -> 484 us, T = 2048 363 -> 343 us against
+// 4 x 2; 2 x 4: 662 and 470 us)
+#ifndef MOE_U4_WM
+#define MOE_U4_WM 8
+#endif
+using CfgU4 = Cfg<256, 128, MOE_U4_WM, 8 / MOE_U4_WM, 2, 1>;
 // Dense products (shared expert, router logits): 128 x 128, 4 waves of
 // 64 x 64, one register stage ahead, 2 workgroups per CU (a dense T = 4096
 // product has too few 256 x 128 tiles to fill the chip).
@@ -403,8 +411,19 @@ __device__ __forceinline__ uint32_t ds_read4(uint32_t addr) {
     asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
     return v;
 }
+__device__ __forceinline__ u32x2 ds_read8(uint32_t addr) {
+    u32x2 v;
+    asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+__device__ __forceinline__ uint32_t ds_read_u16(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_u16 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
 __device__ __forceinline__ void lgkm_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void tie(u32x2& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void tie(uint32_t& v) { asm volatile("" : "+v"(v)); }
 // 4 bytes per lane from a buffer straight into LDS at dst + 4 * lane
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff) {
@@ -413,30 +432,60 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* dst, uint32
 constexpr uint32_t kDropOffset = 0x80000000u;  // past every buffer: the store is dropped
 
 // KS: K elements per step (64 or 32); NST: LDS stages, the DMA running
-// PD = NST - 1 steps ahead of the MFMAs.
-template <int MODE, bool OUTBF, class C, int KS, int NST>
+// PD = NST - 1 steps ahead of the MFMAs.  U4G > 0: 4-bit affine group-64
+// weights whose rows hold at most U4G groups (below); 0: bf16 weights.
+//
+// 4-bit weights: a K step is one group of 64 codes, 32 bytes of each weight
+// row, so the A part of a stage is a quarter of the bf16 one.  The group
+// scales and mins of an item's rows (one contiguous block of each array,
+// [rows][K/64] bf16, as they lie in memory) go into one of two LDS buffers
+// by DMA in the first K step of the item before (the barrier of that step
+// is the one after which no wave reads that buffer for the item before
+// it).  Each lane dequantises its A fragment (8 codes -> bf16 of
+// scale * q + min, the rounding of the register-streaming kernels) right
+// before the MFMAs that use it, so every code is dequantised once per wave
+// that holds its row and used against all of the wave's token fragments.
+// The K order inside a step differs from the bf16 one: lane-group q takes
+// the 16 contiguous codes at 16q (8 bytes, one LDS read for both 32-wide
+// MFMA steps), so its token operand is the 16-byte pieces 2q and 2q+1.
+template <int MODE, bool OUTBF, class C, int KS, int NST, int U4G>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs a) {
     constexpr int BW = C::BW, BT = C::BT, WM = C::WM, WN = C::WN, FM = C::FM, FT = C::FT;
     constexpr int NW = C::NW;
     constexpr bool DUAL = (MODE == kRoutedGateUp);
+    constexpr bool U4 = U4G > 0;
     constexpr int ROWS = DUAL ? BW / 2 : BW;
     constexpr int PD = NST - 1;             // steps in flight ahead of the one computed
     constexpr int RSK = KS;                 // LDS row stride (elements)
     constexpr int PPR = KS / 8;             // 16-byte pieces per LDS row
     constexpr int RPC = 64 / PPR;           // rows one 64-lane DMA call covers
-    constexpr int STAGE = (BW + BT) * RSK;  // elements: A rows then B rows
-    constexpr int AJ = BW / RPC / NW;       // RPC-row A blocks per wave per step
+    constexpr int ARB = U4 ? KS / 2 : KS * 2;  // bytes of an A row per K step
+    constexpr int ARPC = 1024 / ARB;        // A rows one 64-lane DMA call covers
+    constexpr int AEL = BW * ARB / 2;       // elements of the A part of a stage
+    constexpr int STAGE = AEL + BT * RSK;   // elements: A rows then B rows
+    constexpr int AJ = BW / ARPC / NW;      // ARPC-row A blocks per wave per step
     constexpr int BJ = BT / RPC / NW;       // RPC-row B blocks per wave per step
     constexpr int kDmaPerStep = AJ + BJ;
     constexpr int kStores = DUAL ? FT * FM / 2 : FT * FM;
     constexpr int kPrefetch = DUAL ? 1 : 2 * FT;
+    // 4-bit scale staging: NSA arrays (gate scale, gate min, up scale, up
+    // min; down: scale, min) of ROWS x U4G bf16 per buffer, kSc DMA calls
+    // of 1 KB per wave per item
+    constexpr int NSA = DUAL ? 4 : 2;
+    constexpr int SCB = U4 ? ROWS * U4G * 2 : 0;  // bytes per array
+    constexpr int CPA = SCB / 1024;               // DMA calls per array
+    constexpr int kSc = U4 ? NSA * CPA / NW : 0;
     static_assert(KS == 32 || KS == 64, "K steps of one or two 32-wide MFMA steps");
+    static_assert(!U4 || KS == 64, "4-bit: a K step is one group of 64");
+    static_assert(!U4 || (SCB % 1024 == 0 && kSc * NW == NSA * CPA && CPA % kSc == 0),
+                  "whole scale DMA calls per wave, each wave's inside one array");
     static_assert(MODE == kRoutedGateUp || MODE == kRoutedDown, "routed modes");
-    static_assert(AJ * RPC * NW == BW && BJ * RPC * NW == BT, "whole row blocks per wave");
-    static_assert(!DUAL || (NW / 2) * AJ * RPC == BW / 2, "a wave's A rows lie in the gate or the up half");
-    static_assert((PD - 1) * kDmaPerStep + kStores + kPrefetch < 64 && PD * kDmaPerStep < 64, "vmcnt range");
+    static_assert(AJ * ARPC * NW == BW && BJ * RPC * NW == BT, "whole row blocks per wave");
+    static_assert(!DUAL || (NW / 2) * AJ * ARPC == BW / 2, "a wave's A rows lie in the gate or the up half");
+    static_assert((PD - 1) * kDmaPerStep + kStores + kPrefetch + kSc < 64 && PD * kDmaPerStep < 64, "vmcnt range");
     static_assert(RPC * BJ <= 64, "one pair id per lane covers the wave's B rows");
     __shared__ __attribute__((aligned(16))) uint16_t lds[NST][STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t sc_lds[U4 ? 2 : 1][U4 ? NSA * SCB : 16];
     __shared__ int4 items[kPersistMaxItems];
     // gate/up: pair ids of the item after next, 64 per wave (one DMA per item)
     __shared__ uint32_t pair_ids[DUAL ? NW * 64 : 1];
@@ -476,16 +525,21 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
     int brow[BJ], bpiece[BJ];
 #pragma unroll
     for (int j = 0; j < AJ; ++j) {
-        const int ra = wave * RPC * AJ + RPC * j + lane / PPR;
-        const int p = (lane % PPR) ^ ((ra >> 1) & (PPR - 1));
-        aoff[j] = uint32_t(((DUAL ? (ra & (BW / 2 - 1)) : ra) * K + 8 * p) * 2);
+        if constexpr (U4) {  // 4-bit rows: 2 pieces per step, unswizzled
+            const int ra = wave * ARPC * AJ + ARPC * j + lane / 2;
+            aoff[j] = uint32_t((DUAL ? (ra & (BW / 2 - 1)) : ra) * (K / 2) + 16 * (lane & 1));
+        } else {
+            const int ra = wave * RPC * AJ + RPC * j + lane / PPR;
+            const int p = (lane % PPR) ^ ((ra >> 1) & (PPR - 1));
+            aoff[j] = uint32_t(((DUAL ? (ra & (BW / 2 - 1)) : ra) * K + 8 * p) * 2);
+        }
     }
 #pragma unroll
     for (int j = 0; j < BJ; ++j) {
         brow[j] = wave * RPC * BJ + RPC * j + lane / PPR;
         bpiece[j] = (lane % PPR) ^ ((brow[j] >> 1) & (PPR - 1));
     }
-    const bool up_wave = DUAL && wave * RPC * AJ >= BW / 2;
+    const bool up_wave = DUAL && wave * ARPC * AJ >= BW / 2;
     const auto rs_x = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.act), 0,
                                                         uint32_t(size_t(a.n_act_rows) * K * 2), kRsrcWord3);
     const auto rs_out = __builtin_amdgcn_make_buffer_rsrc(
@@ -496,9 +550,26 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
     auto w_rsrc = [&](int4 it) __attribute__((always_inline)) {
         const int r0 = it.w * ROWS;
         const void* bank = up_wave ? a.w1 : a.w0;
-        const uint16_t* p = static_cast<const uint16_t*>(bank) + (size_t(it.x) * N + r0) * K;
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), 0, uint32_t(min(ROWS, N - r0) * K * 2),
-                                                 kRsrcWord3);
+        constexpr int EB = U4 ? 1 : 4;  // (bytes per element) x 2
+        const uint8_t* p = static_cast<const uint8_t*>(bank) + (size_t(it.x) * N + r0) * K * EB / 2;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), 0,
+                                                 uint32_t(min(ROWS, N - r0) * K * EB / 2), kRsrcWord3);
+    };
+    // 4-bit: the group scales and mins of an item's rows into scale buffer
+    // buf; wave w's kSc calls lie in one array
+    const int G = K / 64;
+    auto scale_dma = [&](int4 it, int buf) __attribute__((always_inline)) {
+        if constexpr (U4) {
+            const int r0 = it.w * ROWS;
+            const int arr = (wave * kSc) / CPA, ch0 = (wave * kSc) % CPA;
+            const void* base = arr == 0 ? a.s0 : arr == 1 ? a.m0 : arr == 2 ? a.s1 : a.m1;
+            const uint8_t* p = static_cast<const uint8_t*>(base) + (size_t(it.x) * N + r0) * G * 2;
+            const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), 0,
+                                                              uint32_t(min(ROWS, N - r0) * G * 2), kRsrcWord3);
+            uint8_t* dst = &sc_lds[buf][arr * SCB + ch0 * 1024];
+#pragma unroll
+            for (int j = 0; j < kSc; ++j) dma16(rs, dst + j * 1024, uint32_t((ch0 + j) * 1024 + 16 * lane), 0);
+        }
     };
     auto item_at = [&](int m) __attribute__((always_inline)) {
         const int4 t = items[m];
@@ -524,10 +595,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
         uint16_t* base = &lds[st][0];
 #pragma unroll
         for (int j = 0; j < AJ; ++j)
-            dma16(rw, base + (wave * RPC * AJ + RPC * j) * RSK, aoff[j], so);
+            dma16(rw, base + (wave * ARPC * AJ + ARPC * j) * (ARB / 2), aoff[j], kt * ARB);
 #pragma unroll
         for (int j = 0; j < BJ; ++j)
-            dma16(rs_x, base + (BW + wave * RPC * BJ + RPC * j) * RSK, xo[j], so);
+            dma16(rs_x, base + (AEL + (wave * RPC * BJ + RPC * j) * RSK), xo[j], so);
     };
     // element offset of 16-byte piece p of LDS row r of a stage
     auto soff = [](int r, int p) __attribute__((always_inline)) { return r * RSK + ((p ^ ((r >> 1) & (PPR - 1))) << 3); };
@@ -544,15 +615,78 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
     f32x4 acc[FM][FT];
     constexpr int NKS = KS / 32;  // 32-wide MFMA steps per K step
     // byte offsets of the wave's fragments inside a stage: [ks][fragment]
+    // (4-bit A: one 8-byte read per fragment for both ks, at aofs[0])
     uint32_t aofs[NKS][FM], bofs[NKS][FT];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) aofs[ks][i] = uint32_t(soff(arow_l[i], ks * 4 + q) * 2);
+        for (int i = 0; i < FM; ++i)
+            aofs[ks][i] = U4 ? uint32_t(arow_l[i] * ARB + 8 * q) : uint32_t(soff(arow_l[i], ks * 4 + q) * 2);
 #pragma unroll
-        for (int jj = 0; jj < FT; ++jj) bofs[ks][jj] = uint32_t((BW * RSK + soff(brow_l + jj * 16, ks * 4 + q)) * 2);
+        for (int jj = 0; jj < FT; ++jj)
+            bofs[ks][jj] = uint32_t((AEL + soff(brow_l + jj * 16, U4 ? 2 * q + ks : ks * 4 + q)) * 2);
+    }
+    // 4-bit: byte offset of fragment i's row scale in a scale buffer (its
+    // min is SCB further)
+    uint32_t scofs[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int arr = (DUAL && i >= FM / 2) ? 2 : 0;
+        const int row = DUAL ? (arow_l[i] & (BW / 2 - 1)) : arow_l[i];
+        scofs[i] = uint32_t(arr * SCB + row * G * 2);
     }
     const uint32_t lds0 = lds_byte_addr(&lds[0][0]);
+    const uint32_t sc0 = lds_byte_addr(&sc_lds[0][0]);
+    auto compute_u4 = [&](int st, auto nf_c, int kt, int buf) __attribute__((always_inline)) {
+        constexpr int NF = decltype(nf_c)::value;
+        if constexpr (NF > 0) {
+            const uint32_t sb = lds0 + uint32_t(st * STAGE * 2);
+            const uint32_t scb = sc0 + uint32_t(buf * NSA * SCB + 2 * kt);
+            u32x2 cw[FM];
+            uint32_t sw[FM], mw[FM];
+            u32x4 bfv[NKS][NF];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                cw[i] = ds_read8(sb + aofs[0][i]);
+                sw[i] = ds_read_u16(scb + scofs[i]);
+                mw[i] = ds_read_u16(scb + scofs[i] + SCB);
+            }
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int jj = 0; jj < NF; ++jj) bfv[ks][jj] = ds_read16(sb + bofs[ks][jj]);
+            lgkm_wait_all();
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                tie(cw[i]);
+                tie(sw[i]);
+                tie(mw[i]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int jj = 0; jj < NF; ++jj) tie(bfv[ks][jj]);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const float sc = bf16_lo(sw[i]), mn = bf16_lo(mw[i]);
+                    const uint32_t w = ks == 0 ? cw[i].x : cw[i].y;
+                    uint32_t even, odd;
+                    nibble_bytes<true>(w, even, odd);
+                    u32x4 af;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        af[b] = pack_bf16x2(fmaf(sc, float((even >> (8 * b)) & 0xffu), mn),
+                                            fmaf(sc, float((odd >> (8 * b)) & 0xffu), mn));
+#pragma unroll
+                    for (int jj = 0; jj < NF; ++jj)
+                        acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, af), __builtin_bit_cast(bf16x8, bfv[ks][jj]), acc[i][jj], 0, 0, 0);
+                }
+            }
+        }
+    };
     auto compute = [&](int st, auto nf_c) __attribute__((always_inline)) {
         constexpr int NF = decltype(nf_c)::value;
         const uint32_t sb = lds0 + uint32_t(st * STAGE * 2);
@@ -615,6 +749,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
         for (int j = 0; j < FT; ++j) ep_cur[j] = a.pairs[pair_index(cur, wn * (BT / WN) + j * 16 + r)];
     }
     auto rw_cur = w_rsrc(cur);
+    scale_dma(cur, 0);
 #pragma unroll
     for (int st = 0; st < PD; ++st) dma(st, rw_cur, xo_cur, st);
 #pragma unroll
@@ -659,7 +794,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
         const int nfrag = uniform(min(FT, max(0, (cur.z - wn * (BT / WN) + 15) / 16)));
 
         auto run = [&](auto nf_c) __attribute__((always_inline)) {
-            auto step = [&](int kt) __attribute__((always_inline)) {
+            auto step = [&](int kt, bool first) __attribute__((always_inline)) {
                 // one DMA call with its operands selected element by element:
                 // two calls on the two arrays were merged by the compiler into
                 // one call on a selected array address, which put both arrays
@@ -670,22 +805,38 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_routed_dma_kernel(GemmArgs
 #pragma unroll
                 for (int jj = 0; jj < BJ; ++jj) xo_s[jj] = same ? xo_cur[jj] : xo_nxt[jj];
                 dma(st, same ? rw_cur : rw_nxt, xo_s, same ? kt + PD : kt + PD - nk);
-                compute(g % NST, nf_c);
+                if constexpr (U4) {
+                    if (first) scale_dma(nxt, (m + 1) & 1);
+                    compute_u4(g % NST, nf_c, kt, m & 1);
+                } else {
+                    compute(g % NST, nf_c);
+                }
                 ++g;
             };
-            // steps 0 .. PD-1: newer than their DMA are the DMA of the PD-1
-            // steps after them, the previous item's stores and this item's
-            // prefetch; later steps: the PD-1 steps' DMA only
+            // Newer than step kt's DMA at its wait: kt < PD: the DMA of
+            // steps kt+1 .. PD-1 (issued by the previous item), the previous
+            // item's stores, this item's prefetch and the DMA of steps 0 ..
+            // kt-1, i.e. (PD-1) steps' DMA + stores + prefetch, plus the
+            // scale DMA issued in step 0 for kt >= 1; kt = PD: the scale DMA
+            // and PD-1 steps' DMA; later steps: PD-1 steps' DMA
+            vm_wait_lgkm0<(PD - 1) * kDmaPerStep + kStores + kPrefetch>();
+            bare_barrier();
+            step(0, true);
 #pragma unroll
-            for (int kt = 0; kt < PD; ++kt) {
-                vm_wait_lgkm0<(PD - 1) * kDmaPerStep + kStores + kPrefetch>();
+            for (int kt = 1; kt < PD; ++kt) {
+                vm_wait_lgkm0<(PD - 1) * kDmaPerStep + kStores + kPrefetch + kSc>();
                 bare_barrier();
-                step(kt);
+                step(kt, false);
             }
-            for (int kt = PD; kt < nk; ++kt) {
+            if (nk > PD) {
+                vm_wait_lgkm0<(PD - 1) * kDmaPerStep + kSc>();
+                bare_barrier();
+                step(PD, false);
+            }
+            for (int kt = PD + 1; kt < nk; ++kt) {
                 vm_wait_lgkm0<(PD - 1) * kDmaPerStep>();
                 bare_barrier();
-                step(kt);
+                step(kt, false);
             }
         };
         auto dispatch = [&](auto self, auto nf_c) __attribute__((always_inline)) {
@@ -804,40 +955,79 @@ static hipError_t launch_cfg(int mode, bool outbf, const GemmArgs& a, int grid_x
 // pairs); dense modes the small one (grid_x = token tiles of
 // tiled_rows_dense() tokens).
 // Persistent routed launch: one workgroup per CU (at most), each XCD's 32
-// taking its run of items in turn.  Needs an even number of K steps, byte
-// offsets inside 32 bits and at most kPersistMaxItems items per workgroup.
+// taking its run of items in turn.  Needs whole K steps (at least NST - 1
+// per item; 4-bit: NST, so that an item's scale DMA, issued in its first
+// step, is older than the next item's first K step), byte offsets inside
+// 32 bits and at most kPersistMaxItems items per workgroup.
 #ifndef MOE_PERSIST_KS
 #define MOE_PERSIST_KS 64
 #endif
 constexpr int kPersistKS = MOE_PERSIST_KS;           // K per step of the persistent kernel
 constexpr int kPersistNST = kPersistKS == 64 ? 3 : 6;  // LDS stages: 144 KB either way
-static bool launch_persist(int mode, bool outbf, const GemmArgs& a, int max_tiles, hipStream_t s) {
+constexpr int kU4NST = 3;                            // 4-bit: 72 KB of stages + 64 KB of scales
+constexpr int kU4MaxGroupsTiled = 32;                // 4-bit rows: K up to 2048
+constexpr int kU4DownSmallGroups = 8;                // 4-bit down rows up to K = 512: smaller scale buffers
+
+static int persist_groups(int mode, bool u4, int N, int K, int max_tiles, int n_act_rows, int n_pairs, bool outbf) {
     using C = CfgLarge;
-    constexpr int KS = kPersistKS, NST = kPersistNST;
+    const int KS = u4 ? 64 : kPersistKS, NST = u4 ? kU4NST : kPersistNST;
     const int rows = mode == kRoutedGateUp ? C::BW / 2 : C::BW;
-    const long long max_items = (long long)max_tiles * ((a.N + rows - 1) / rows);
+    if (N <= 0 || K <= 0 || max_tiles <= 0) return 0;
+    const long long max_items = (long long)max_tiles * ((N + rows - 1) / rows);
     const long long per_xcd = (max_items + 7) / 8;
     const int nl = int(std::min<long long>(32, per_xcd));
-    // whole K steps, at least NST - 1 of them per item (the DMA runs that far ahead)
-    if (nl <= 0 || a.K % KS || a.K / KS < NST - 1 || (per_xcd + nl - 1) / nl > kPersistMaxItems) return false;
-    if ((unsigned long long)a.n_act_rows * a.K * 2 >= (1ull << 32) ||
-        (unsigned long long)rows * a.K * 2 >= (1ull << 32))
-        return false;
-    const dim3 g(unsigned(8 * nl)), b(C::THREADS);
+    if (nl <= 0 || K % KS || K / KS < (u4 ? NST : NST - 1) || (per_xcd + nl - 1) / nl > kPersistMaxItems) return 0;
+    if ((unsigned long long)n_act_rows * K * 2 >= (1ull << 32) || (unsigned long long)rows * K * 2 >= (1ull << 32))
+        return 0;
     // stores address the output with 32-bit offsets below the drop offset
-    if ((unsigned long long)a.n_pairs * a.N * (outbf || mode == kRoutedGateUp ? 2 : 4) >= (1ull << 31)) return false;
-    if (mode == kRoutedGateUp) gemm_routed_dma_kernel<kRoutedGateUp, true, C, KS, NST><<<g, b, 0, s>>>(a);
-    else if (outbf) gemm_routed_dma_kernel<kRoutedDown, true, C, KS, NST><<<g, b, 0, s>>>(a);
-    else gemm_routed_dma_kernel<kRoutedDown, false, C, KS, NST><<<g, b, 0, s>>>(a);
+    if ((unsigned long long)n_pairs * N * (outbf || mode == kRoutedGateUp ? 2 : 4) >= (1ull << 31)) return 0;
+    if (u4 && K / 64 > kU4MaxGroupsTiled) return 0;
+    return nl;
+}
+
+bool routed_tiled_u4_fits(int mode, int N, int K, int max_tiles, int n_act_rows, int n_pairs, bool outbf) {
+    return persist_groups(mode, true, N, K, max_tiles, n_act_rows, n_pairs, outbf) > 0;
+}
+
+static bool launch_persist(int mode, bool outbf, bool u4, const GemmArgs& a, int max_tiles, hipStream_t s) {
+    using C = CfgLarge;
+    const int nl = persist_groups(mode, u4, a.N, a.K, max_tiles, a.n_act_rows, a.n_pairs, outbf);
+    if (nl <= 0) return false;
+    const dim3 g(unsigned(8 * nl)), b(C::THREADS);
+    if (u4) {
+        using U = CfgU4;
+        static_assert(U::BW == C::BW && U::BT == C::BT && U::THREADS == C::THREADS, "same tile and grid");
+        constexpr int GU = kU4MaxGroupsTiled, GD = kU4DownSmallGroups;
+        if (mode == kRoutedGateUp) gemm_routed_dma_kernel<kRoutedGateUp, true, U, 64, kU4NST, GU><<<g, b, 0, s>>>(a);
+        else if (a.K / 64 <= GD) {
+            if (outbf) gemm_routed_dma_kernel<kRoutedDown, true, U, 64, kU4NST, GD><<<g, b, 0, s>>>(a);
+            else gemm_routed_dma_kernel<kRoutedDown, false, U, 64, kU4NST, GD><<<g, b, 0, s>>>(a);
+        } else {
+            if (outbf) gemm_routed_dma_kernel<kRoutedDown, true, U, 64, kU4NST, GU><<<g, b, 0, s>>>(a);
+            else gemm_routed_dma_kernel<kRoutedDown, false, U, 64, kU4NST, GU><<<g, b, 0, s>>>(a);
+        }
+        return true;
+    }
+    constexpr int KS = kPersistKS, NST = kPersistNST;
+    if (mode == kRoutedGateUp) gemm_routed_dma_kernel<kRoutedGateUp, true, C, KS, NST, 0><<<g, b, 0, s>>>(a);
+    else if (outbf) gemm_routed_dma_kernel<kRoutedDown, true, C, KS, NST, 0><<<g, b, 0, s>>>(a);
+    else gemm_routed_dma_kernel<kRoutedDown, false, C, KS, NST, 0><<<g, b, 0, s>>>(a);
     return true;
 }
 
 hipError_t launch_gemm_tiled(int mode, bool outbf, const GemmArgs& a, int grid_x, hipStream_t s) {
     if (grid_x <= 0) return hipSuccess;
-    if ((mode == kRoutedGateUp || mode == kRoutedDown) && launch_persist(mode, outbf, a, grid_x, s))
+    if ((mode == kRoutedGateUp || mode == kRoutedDown) && launch_persist(mode, outbf, false, a, grid_x, s))
         return hipGetLastError();
     if (mode == kRoutedGateUp || mode == kRoutedDown) return launch_cfg<CfgLarge>(mode, outbf, a, grid_x, s);
     return launch_cfg<CfgSmall>(mode, outbf, a, grid_x, s);
+}
+
+hipError_t launch_gemm_routed_u4(int mode, bool outbf, const GemmArgs& a, int max_tiles, hipStream_t s) {
+    if (max_tiles <= 0) return hipSuccess;
+    if (mode != kRoutedGateUp && mode != kRoutedDown) return hipErrorInvalidValue;
+    if (!launch_persist(mode, outbf, true, a, max_tiles, s)) return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 }  // namespace moe

@@ -86,6 +86,12 @@ hipError_t launch_gemm(int mode, int wkind, bool outbf, const GemmArgs& a, int g
 hipError_t launch_gemm_tiled(int mode, bool outbf, const GemmArgs& a, int grid_x, hipStream_t s);
 int tiled_rows();
 int tiled_rows_dense();
+// 4-bit affine group-64 banks on the persistent LDS-tiled kernel (routed
+// modes, tiles of tiled_rows() pairs): whether the shape fits it (K % 64 ==
+// 0, K <= 2048, at least 3 K steps, offsets inside 32 bits, the item table),
+// and the launch (hipErrorInvalidValue when it does not fit; nothing launched).
+bool routed_tiled_u4_fits(int mode, int N, int K, int max_tiles, int n_act_rows, int n_pairs, bool outbf);
+hipError_t launch_gemm_routed_u4(int mode, bool outbf, const GemmArgs& a, int max_tiles, hipStream_t s);
 
 // routing (parameter blocks in moe_select.h)
 struct SelParams;
