@@ -80,6 +80,14 @@ int routed_tf(const moe_config& c) { return routed_large(c) ? 4 : 1; }
 int routed_tile_rows(const moe_config& c) { return routed_tiled(c) ? moe::tiled_rows() : 16 * routed_tf(c); }
 int dense_tf(const moe_config& c) { return c.n_tokens >= 64 ? 4 : 1; }
 bool dense_tiled(const moe_config& c, moe_dtype d) { return c.n_tokens >= 128 && d == MOE_BF16; }
+// 4-bit shared expert from T = 128: its three matrices are dequantised to
+// bf16 into the workspace (6 MiB at Qwen3.6 shape, a few us) and it runs on
+// the LDS-tiled bf16 kernels.  The register-streaming 4-bit kernels re-read
+// each 64-token tile of activations for every 16 weight rows (Qwen3.6 4-bit,
+// K = 4, T = 4096: shared gate/up 92 us and down 212 us on the aux stream).
+bool shared_dequant(const moe_config& c) {
+    return c.expert_dtype == MOE_U4_AFFINE_G64 && c.d_ff_shared > 0 && dense_tiled(c, MOE_BF16);
+}
 // Small T*K: one stream; every GEMM workgroup finds its expert and pairs from
 // the routing ids itself (no permute launch) and the shared expert is an
 // extra work item of the routed launches.
@@ -119,7 +127,7 @@ int router_ksplit(const moe_config& c) {
 
 struct Layout {
     size_t chunk_base, logits, gate_logit, ids, wts, offsets, active, n_active, n_tiles, pairs, tiles, h, slots, hs, ys, xn,
-        total;
+        sw, total;
 };
 
 Layout layout(const moe_config& c) {
@@ -151,6 +159,7 @@ Layout layout(const moe_config& c) {
     L.hs = take(T * Fs * hb);
     L.ys = take(T * D * 4);
     L.xn = take(T * D * (c.act_dtype == MOE_F32 ? 4 : 2));  // normalised x (moe_layer_forward_norm)
+    L.sw = take(shared_dequant(c) ? 3 * Fs * D * 2 : 0);    // dequantised shared gate, up, down (bf16)
     L.total = o;
     return L;
 }
@@ -518,11 +527,24 @@ moe_status stage_shared(const moe_config& c, const Layout& L, void* ws, const vo
         gl = at<float>(ws, L.gate_logit);
     }
     void* hs = at<void>(ws, L.hs);
-    moe::GemmArgs a = gemm_args(w.shared_gate, &w.shared_up, c.d_ff_shared, c.d_model, 1);
+    moe_matrix sg = w.shared_gate, su = w.shared_up, sd = w.shared_down;
+    if (shared_dequant(c)) {
+        const int Fs = c.d_ff_shared, D = c.d_model;
+        uint16_t* base = at<uint16_t>(ws, L.sw);
+        const moe_matrix* src[3] = {&w.shared_gate, &w.shared_up, &w.shared_down};
+        moe_matrix* dst[3] = {&sg, &su, &sd};
+        for (int i = 0; i < 3; ++i) {
+            uint16_t* o = base + size_t(i) * Fs * D;
+            const int rows = i < 2 ? Fs : D, K = i < 2 ? D : Fs;
+            HIP_TRY(moe::launch_dequant_u4(src[i]->w, src[i]->scale, src[i]->min, rows, K, o, s));
+            *dst[i] = moe_matrix{o, nullptr, nullptr};
+        }
+    }
+    moe::GemmArgs a = gemm_args(sg, &su, c.d_ff_shared, c.d_model, 1);
     a.act = x; a.n_act_rows = T; a.n_rows = T; a.out = hs;
-    moe::GemmArgs d = gemm_args(w.shared_down, nullptr, c.d_model, c.d_ff_shared, 1);
+    moe::GemmArgs d = gemm_args(sd, nullptr, c.d_model, c.d_ff_shared, 1);
     d.act = hs; d.n_act_rows = T; d.n_rows = T; d.out = shared_out; d.row_scale = gl;
-    if (dense_tiled(c, c.expert_dtype)) {
+    if (dense_tiled(c, c.expert_dtype) || shared_dequant(c)) {
         const int g = (T + moe::tiled_rows_dense() - 1) / moe::tiled_rows_dense();
         HIP_TRY(moe::launch_gemm_tiled(moe::kDenseGateUp, true, a, g, s));
         HIP_TRY(moe::launch_gemm_tiled(moe::kDenseDown, false, d, g, s));

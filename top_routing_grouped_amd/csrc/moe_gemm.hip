@@ -766,6 +766,42 @@ static hipError_t dispatch_wk(const GemmArgs& a, int wkind, bool outbf, int grid
     return launch_cfg<MODE, kWF32, false>(a, grid_x, tf, s);
 }
 
+// 4-bit affine group-64 matrix [rows][K] -> bf16 [rows][K] (scale * q + min,
+// rounded to nearest even: the value every 4-bit GEMM here multiplies).  One
+// thread per 32 codes (one 16-byte load, four 16-byte stores); K % 64 == 0.
+__global__ __launch_bounds__(256) void dequant_u4_kernel(const uint8_t* __restrict__ codes,
+                                                         const uint16_t* __restrict__ scale,
+                                                         const uint16_t* __restrict__ mn, long long n_pieces, int K,
+                                                         uint16_t* __restrict__ out) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_pieces) return;
+    const long long e = i * 32;  // first element: row e / K, column e % K (a piece lies in one group)
+    const u32x4 c = *reinterpret_cast<const u32x4*>(codes + e / 2);
+    const float sc = bf16_to_f32(scale[e / 64]), m = bf16_to_f32(mn[e / 64]);
+    const uint32_t words[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t even, odd, packed[4];
+        nibble_bytes<false>(words[j], even, odd);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            packed[b] = pack_bf16x2(fmaf(sc, float((even >> (8 * b)) & 0xffu), m),
+                                    fmaf(sc, float((odd >> (8 * b)) & 0xffu), m));
+        *reinterpret_cast<u32x4*>(out + e + 8 * j) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    }
+}
+
+hipError_t launch_dequant_u4(const void* codes, const void* scale, const void* min, int rows, int K, void* out,
+                             hipStream_t s) {
+    if (rows <= 0 || K <= 0) return hipSuccess;
+    if (K % 64) return hipErrorInvalidValue;
+    const long long n = (long long)rows * K / 32;
+    dequant_u4_kernel<<<unsigned((n + 255) / 256), 256, 0, s>>>(
+        static_cast<const uint8_t*>(codes), static_cast<const uint16_t*>(scale), static_cast<const uint16_t*>(min), n,
+        K, static_cast<uint16_t*>(out));
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(int mode, int wkind, bool outbf, const GemmArgs& a, int grid_x, int tf, hipStream_t s) {
     if (grid_x <= 0) return hipSuccess;
     switch (mode) {

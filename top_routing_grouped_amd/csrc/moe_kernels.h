@@ -80,6 +80,9 @@ constexpr int kFusedSelMaxT = 8;
 constexpr int kU4MaxGroups = 64;
 
 hipError_t launch_gemm(int mode, int wkind, bool outbf, const GemmArgs& a, int grid_x, int tf, hipStream_t s);
+// 4-bit affine group-64 matrix [rows][K] (codes, scale, min) -> bf16 [rows][K]
+hipError_t launch_dequant_u4(const void* codes, const void* scale, const void* min, int rows, int K, void* out,
+                             hipStream_t s);
 // bf16 LDS-tiled variant; K % 64 == 0.  Routed modes: tiles of tiled_rows()
 // pairs (256 weight rows x 128 tokens per workgroup); dense modes: token
 // tiles of tiled_rows_dense() (128 x 128).
