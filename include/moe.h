@@ -149,8 +149,9 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids,
  * first n_active entries of active_experts are read) and the flat weights
  * [T*K] fp32.  Only active experts' weights are read, each once per tile of
  * up to 16 of its pairs (small T), 128 (bf16 weights, experts averaging >= 16
- * pairs; 4-bit weights averaging >= 16 pairs when d_model and d_ff are 256 ..
- * 2048) or 64 (other 4-bit and fp32 weights, >= 64 pairs).  4-bit codes are
+ * pairs; 4-bit weights averaging >= 64 pairs when d_model and d_ff are 256 ..
+ * 2048, 64 from 16 pairs) or 64 (other 4-bit and fp32 weights, >= 64
+ * pairs).  4-bit codes are
  * dequantised to bf16 (scale * q + min, rounded to nearest even) inside the
  * GEMM kernels.  The SwiGLU intermediate is rounded to bf16 for bf16/u4
  * weights and kept fp32 for fp32 weights. */

@@ -1,9 +1,9 @@
 """GPU parity of 4-bit affine group-64 layers on the persistent LDS-tiled routed
-GEMMs (codes and group scales staged in LDS, 128-token tiles), which take
-4-bit layers averaging at least 16 pairs per expert when both routed GEMMs
-fit them: every token's routing and layer output against the fp64 oracle
-(edge0 page, tier table: 4-bit affine, group 64; Treebeard page, "Routed
-expert computation").  The shapes cover the switch point, the smallest
+GEMMs (codes and group scales staged in LDS; 64-token tiles up to 64 pairs
+per expert, 128-token tiles from there), which take 4-bit layers averaging
+at least 16 pairs per expert when both routed GEMMs fit them: every token's
+routing and layer output against the fp64 oracle (edge0 page, tier table:
+4-bit affine, group 64; Treebeard page, "Routed expert computation").  The shapes cover the switch point, the smallest
 reduction the layer gives it (four K steps), rows past a partial row block,
 both scale-buffer sizes of the down projection, the largest gate/up
 reduction (32 groups), experts spanning many token tiles and skewed
@@ -35,10 +35,11 @@ def _tiled(spec):
             and 3 <= spec.d_model // 64 <= 32 and 3 <= spec.d_ff // 64 <= 32)
 
 
-@pytest.mark.parametrize("T", [127, 128, 700, 3000])
+@pytest.mark.parametrize("T", [127, 128, 300, 511, 512, 3000])
 def test_u4_tiled_switch_point(T):
     """E = 32, K = 4: T = 127 keeps the 16-token register tiles, T >= 128
-    takes the tiled kernel."""
+    takes the tiled kernel, with 64-token tiles below 64 pairs per expert
+    (T < 512) and 128-token tiles from there."""
     spec = spec_of("qwen_u4", n_tokens=T, d_model=256, n_experts=32, top_k=4, d_ff=256, d_ff_shared=256)
     assert _tiled(spec) == (T >= 128)
     _, flagged, err = _layer_vs_oracle(make_case(spec))
@@ -49,7 +50,7 @@ def test_u4_tiled_switch_point(T):
 @pytest.mark.parametrize("D,F,E,K,T", [
     (384, 384, 16, 4, 900),     # down: 1.5 row blocks of 256 (the second partial), 6 groups
     (2048, 1024, 16, 2, 512),   # gate/up 32 groups (the largest), down 16 groups (the larger scale buffer)
-    (512, 2048, 16, 2, 400),    # down 32 groups
+    (512, 2048, 16, 2, 400),    # down 32 groups (64-token tiles)
 ])
 def test_u4_tiled_shapes(D, F, E, K, T):
     spec = spec_of("qwen_u4", n_tokens=T, d_model=D, n_experts=E, top_k=K, d_ff=F, d_ff_shared=F)

@@ -56,28 +56,42 @@ int64_t max_tiles(int64_t n_pairs, int E, int tile_rows) {
     return (n_pairs + act * (tile_rows - 1)) / tile_rows;
 }
 // 4-bit banks averaging at least kU4TiledMinPairs pairs per expert use the
-// persistent LDS-tiled kernel (codes and group scales staged in LDS,
-// 128-token tiles) where both routed GEMMs fit it; fewer pairs keep the
-// register tiles (measured at Qwen3.6 shape, K = 4: 16 pairs per expert,
-// T = 1024, layer 328 -> 268 us on the tiled kernel; 8 pairs, T = 512,
-// 222 -> 238 us).
+// persistent LDS-tiled kernel (codes and group scales staged in LDS) where
+// both routed GEMMs fit it: 128-token tiles from kU4Bt128MinPairs pairs per
+// expert, 64-token tiles (a deeper ring) below; fewer pairs keep the
+// register tiles.  Measured at Qwen3.6 shape, K = 4 (pairs per expert:
+// layer us): register tiles 8: 212.6, 16: 328; 64-token tiles 1.6: 163.5
+// (register 136.7), 8: 221.4, 16: 234.4, 32: 264.0, 64: 404.2; 128-token
+// tiles 16: 251.6, 32: 281.9, 64: 349.5.
 #ifndef MOE_U4_TILED_MIN_PAIRS
 #define MOE_U4_TILED_MIN_PAIRS 16
 #endif
+#ifndef MOE_U4_BT128_MIN_PAIRS
+#define MOE_U4_BT128_MIN_PAIRS 64
+#endif
 constexpr int kU4TiledMinPairs = MOE_U4_TILED_MIN_PAIRS;
-bool routed_tiled_u4(const moe_config& c) {
-    if (c.expert_dtype != MOE_U4_AFFINE_G64) return false;
+constexpr int kU4Bt128MinPairs = MOE_U4_BT128_MIN_PAIRS;
+// token tile rows of the tiled 4-bit schedule, 0 when the layer does not take it
+int routed_u4_tile_rows(const moe_config& c) {
+    if (c.expert_dtype != MOE_U4_AFFINE_G64) return 0;
     const int64_t TK = (int64_t)c.n_tokens * c.top_k;
-    if (TK < (int64_t)kU4TiledMinPairs * c.n_experts || TK >= (int64_t(1) << 31)) return false;
-    const int mt = int(max_tiles(TK, c.n_experts, moe::tiled_rows()));
-    return moe::routed_tiled_u4_fits(moe::kRoutedGateUp, c.d_ff, c.d_model, mt, c.n_tokens, int(TK), true) &&
-           moe::routed_tiled_u4_fits(moe::kRoutedDown, c.d_model, c.d_ff, mt, int(TK), int(TK), false);
+    if (TK < (int64_t)kU4TiledMinPairs * c.n_experts || TK >= (int64_t(1) << 31)) return 0;
+    const int rows = TK >= (int64_t)kU4Bt128MinPairs * c.n_experts ? moe::tiled_rows() : moe::tiled_rows_u4_medium();
+    const int mt = int(max_tiles(TK, c.n_experts, rows));
+    const bool fits =
+        moe::routed_tiled_u4_fits(moe::kRoutedGateUp, rows, c.d_ff, c.d_model, mt, c.n_tokens, int(TK), true) &&
+        moe::routed_tiled_u4_fits(moe::kRoutedDown, rows, c.d_model, c.d_ff, mt, int(TK), int(TK), false);
+    return fits ? rows : 0;
 }
+bool routed_tiled_u4(const moe_config& c) { return routed_u4_tile_rows(c) > 0; }
 bool routed_tiled(const moe_config& c) {
     return (routed_large(c) && c.expert_dtype == MOE_BF16) || routed_tiled_u4(c);
 }
 int routed_tf(const moe_config& c) { return routed_large(c) ? 4 : 1; }
-int routed_tile_rows(const moe_config& c) { return routed_tiled(c) ? moe::tiled_rows() : 16 * routed_tf(c); }
+int routed_tile_rows(const moe_config& c) {
+    if (const int u = routed_u4_tile_rows(c)) return u;
+    return routed_tiled(c) ? moe::tiled_rows() : 16 * routed_tf(c);
+}
 int dense_tf(const moe_config& c) { return c.n_tokens >= 64 ? 4 : 1; }
 bool dense_tiled(const moe_config& c, moe_dtype d) { return c.n_tokens >= 128 && d == MOE_BF16; }
 // 4-bit shared expert from T = 128: its three matrices are dequantised to
@@ -336,7 +350,8 @@ moe_status stage_gateup(const moe_config& c, const Layout& L, void* ws, const vo
     a.tiles = tiles; a.n_tiles = n_tiles; a.pairs = pairs; a.n_pairs = TK; a.topk = K;
     a.out = at<void>(ws, L.h);
     if (routed_tiled_u4(c)) {
-        HIP_TRY(moe::launch_gemm_routed_u4(moe::kRoutedGateUp, true, a, int(max_tiles(TK, c.n_experts, routed_tile_rows(c))), s));
+        HIP_TRY(moe::launch_gemm_routed_u4(moe::kRoutedGateUp, true, routed_tile_rows(c), a,
+                                           int(max_tiles(TK, c.n_experts, routed_tile_rows(c))), s));
         return MOE_OK;
     }
     if (routed_tiled(c)) {
@@ -358,7 +373,8 @@ moe_status stage_down(const moe_config& c, const Layout& L, void* ws, const moe_
     d.tiles = tiles; d.n_tiles = n_tiles; d.pairs = pairs; d.n_pairs = TK; d.topk = K;
     d.out = slot_out; d.row_scale = wts;
     if (routed_tiled_u4(c)) {
-        HIP_TRY(moe::launch_gemm_routed_u4(moe::kRoutedDown, slot_bf16, d, int(max_tiles(TK, c.n_experts, routed_tile_rows(c))), s));
+        HIP_TRY(moe::launch_gemm_routed_u4(moe::kRoutedDown, slot_bf16, routed_tile_rows(c), d,
+                                           int(max_tiles(TK, c.n_experts, routed_tile_rows(c))), s));
         return MOE_OK;
     }
     if (routed_tiled(c)) {

@@ -64,6 +64,10 @@ using CfgLarge = Cfg<256, 128, 4, 2, 2, 1>;
 #define MOE_U4_WM 8
 #endif
 using CfgU4 = Cfg<256, 128, MOE_U4_WM, 8 / MOE_U4_WM, 2, 1>;
+// 4-bit experts with fewer pairs: 64-token tiles, whose smaller LDS stages
+// leave room for a deeper ring (the weights, a quarter of the bf16 bytes,
+// need more K steps in flight to keep enough bytes in flight)
+using CfgU4M = Cfg<256, 64, MOE_U4_WM, 8 / MOE_U4_WM, 2, 1>;
 // Dense products (shared expert, router logits): 128 x 128, 4 waves of
 // 64 x 64, one register stage ahead, 2 workgroups per CU (a dense T = 4096
 // product has too few 256 x 128 tiles to fill the chip).
@@ -965,12 +969,17 @@ static hipError_t launch_cfg(int mode, bool outbf, const GemmArgs& a, int grid_x
 constexpr int kPersistKS = MOE_PERSIST_KS;           // K per step of the persistent kernel
 constexpr int kPersistNST = kPersistKS == 64 ? 3 : 6;  // LDS stages: 144 KB either way
 constexpr int kU4NST = 3;                            // 4-bit: 72 KB of stages + 64 KB of scales
+#ifndef MOE_U4M_NST
+#define MOE_U4M_NST 4
+#endif
+constexpr int kU4MNST = MOE_U4M_NST;                 // 64-token tiles: 64 KB of stages + 64 KB of scales
 constexpr int kU4MaxGroupsTiled = 32;                // 4-bit rows: K up to 2048
 constexpr int kU4DownSmallGroups = 8;                // 4-bit down rows up to K = 512: smaller scale buffers
 
-static int persist_groups(int mode, bool u4, int N, int K, int max_tiles, int n_act_rows, int n_pairs, bool outbf) {
+static int persist_groups(int mode, bool u4, int N, int K, int max_tiles, int n_act_rows, int n_pairs, bool outbf,
+                          int nst) {
     using C = CfgLarge;
-    const int KS = u4 ? 64 : kPersistKS, NST = u4 ? kU4NST : kPersistNST;
+    const int KS = u4 ? 64 : kPersistKS, NST = nst;
     const int rows = mode == kRoutedGateUp ? C::BW / 2 : C::BW;
     if (N <= 0 || K <= 0 || max_tiles <= 0) return 0;
     const long long max_items = (long long)max_tiles * ((N + rows - 1) / rows);
@@ -985,27 +994,44 @@ static int persist_groups(int mode, bool u4, int N, int K, int max_tiles, int n_
     return nl;
 }
 
-bool routed_tiled_u4_fits(int mode, int N, int K, int max_tiles, int n_act_rows, int n_pairs, bool outbf) {
-    return persist_groups(mode, true, N, K, max_tiles, n_act_rows, n_pairs, outbf) > 0;
+int tiled_rows_u4_medium() { return CfgU4M::BT; }
+
+bool routed_tiled_u4_fits(int mode, int tile_rows, int N, int K, int max_tiles, int n_act_rows, int n_pairs,
+                          bool outbf) {
+    if (tile_rows != CfgU4::BT && tile_rows != CfgU4M::BT) return false;
+    const int nst = tile_rows == CfgU4::BT ? kU4NST : kU4MNST;
+    return persist_groups(mode, true, N, K, max_tiles, n_act_rows, n_pairs, outbf, nst) > 0;
 }
 
-static bool launch_persist(int mode, bool outbf, bool u4, const GemmArgs& a, int max_tiles, hipStream_t s) {
+template <class U, int NST>
+static void launch_u4(int mode, bool outbf, const GemmArgs& a, dim3 g, hipStream_t s) {
+    static_assert(U::BW == CfgLarge::BW && U::THREADS == CfgLarge::THREADS, "same weight rows and threads");
+    constexpr int GU = kU4MaxGroupsTiled, GD = kU4DownSmallGroups;
+    const dim3 b(U::THREADS);
+    if (mode == kRoutedGateUp) gemm_routed_dma_kernel<kRoutedGateUp, true, U, 64, NST, GU><<<g, b, 0, s>>>(a);
+    else if (a.K / 64 <= GD) {
+        if (outbf) gemm_routed_dma_kernel<kRoutedDown, true, U, 64, NST, GD><<<g, b, 0, s>>>(a);
+        else gemm_routed_dma_kernel<kRoutedDown, false, U, 64, NST, GD><<<g, b, 0, s>>>(a);
+    } else {
+        if (outbf) gemm_routed_dma_kernel<kRoutedDown, true, U, 64, NST, GU><<<g, b, 0, s>>>(a);
+        else gemm_routed_dma_kernel<kRoutedDown, false, U, 64, NST, GU><<<g, b, 0, s>>>(a);
+    }
+}
+
+// u4: 0 = bf16 weights, else the 4-bit token tile rows (CfgU4 or CfgU4M)
+static bool launch_persist(int mode, bool outbf, int u4, const GemmArgs& a, int max_tiles, hipStream_t s) {
     using C = CfgLarge;
-    const int nl = persist_groups(mode, u4, a.N, a.K, max_tiles, a.n_act_rows, a.n_pairs, outbf);
+    const int nst = u4 == 0 ? kPersistNST : u4 == CfgU4::BT ? kU4NST : kU4MNST;
+    if (u4 != 0 && u4 != CfgU4::BT && u4 != CfgU4M::BT) return false;
+    const int nl = persist_groups(mode, u4 != 0, a.N, a.K, max_tiles, a.n_act_rows, a.n_pairs, outbf, nst);
     if (nl <= 0) return false;
     const dim3 g(unsigned(8 * nl)), b(C::THREADS);
-    if (u4) {
-        using U = CfgU4;
-        static_assert(U::BW == C::BW && U::BT == C::BT && U::THREADS == C::THREADS, "same tile and grid");
-        constexpr int GU = kU4MaxGroupsTiled, GD = kU4DownSmallGroups;
-        if (mode == kRoutedGateUp) gemm_routed_dma_kernel<kRoutedGateUp, true, U, 64, kU4NST, GU><<<g, b, 0, s>>>(a);
-        else if (a.K / 64 <= GD) {
-            if (outbf) gemm_routed_dma_kernel<kRoutedDown, true, U, 64, kU4NST, GD><<<g, b, 0, s>>>(a);
-            else gemm_routed_dma_kernel<kRoutedDown, false, U, 64, kU4NST, GD><<<g, b, 0, s>>>(a);
-        } else {
-            if (outbf) gemm_routed_dma_kernel<kRoutedDown, true, U, 64, kU4NST, GU><<<g, b, 0, s>>>(a);
-            else gemm_routed_dma_kernel<kRoutedDown, false, U, 64, kU4NST, GU><<<g, b, 0, s>>>(a);
-        }
+    if (u4 == CfgU4::BT) {
+        launch_u4<CfgU4, kU4NST>(mode, outbf, a, g, s);
+        return true;
+    }
+    if (u4 == CfgU4M::BT) {
+        launch_u4<CfgU4M, kU4MNST>(mode, outbf, a, g, s);
         return true;
     }
     constexpr int KS = kPersistKS, NST = kPersistNST;
@@ -1017,16 +1043,17 @@ static bool launch_persist(int mode, bool outbf, bool u4, const GemmArgs& a, int
 
 hipError_t launch_gemm_tiled(int mode, bool outbf, const GemmArgs& a, int grid_x, hipStream_t s) {
     if (grid_x <= 0) return hipSuccess;
-    if ((mode == kRoutedGateUp || mode == kRoutedDown) && launch_persist(mode, outbf, false, a, grid_x, s))
+    if ((mode == kRoutedGateUp || mode == kRoutedDown) && launch_persist(mode, outbf, 0, a, grid_x, s))
         return hipGetLastError();
     if (mode == kRoutedGateUp || mode == kRoutedDown) return launch_cfg<CfgLarge>(mode, outbf, a, grid_x, s);
     return launch_cfg<CfgSmall>(mode, outbf, a, grid_x, s);
 }
 
-hipError_t launch_gemm_routed_u4(int mode, bool outbf, const GemmArgs& a, int max_tiles, hipStream_t s) {
+hipError_t launch_gemm_routed_u4(int mode, bool outbf, int tile_rows, const GemmArgs& a, int max_tiles,
+                                 hipStream_t s) {
     if (max_tiles <= 0) return hipSuccess;
     if (mode != kRoutedGateUp && mode != kRoutedDown) return hipErrorInvalidValue;
-    if (!launch_persist(mode, outbf, true, a, max_tiles, s)) return hipErrorInvalidValue;
+    if (!launch_persist(mode, outbf, tile_rows, a, max_tiles, s)) return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -90,11 +90,15 @@ hipError_t launch_gemm_tiled(int mode, bool outbf, const GemmArgs& a, int grid_x
 int tiled_rows();
 int tiled_rows_dense();
 // 4-bit affine group-64 banks on the persistent LDS-tiled kernel (routed
-// modes, tiles of tiled_rows() pairs): whether the shape fits it (K % 64 ==
-// 0, K <= 2048, at least 3 K steps, offsets inside 32 bits, the item table),
-// and the launch (hipErrorInvalidValue when it does not fit; nothing launched).
-bool routed_tiled_u4_fits(int mode, int N, int K, int max_tiles, int n_act_rows, int n_pairs, bool outbf);
-hipError_t launch_gemm_routed_u4(int mode, bool outbf, const GemmArgs& a, int max_tiles, hipStream_t s);
+// modes, tiles of tiled_rows() or tiled_rows_u4_medium() pairs): whether the
+// shape fits it (K % 64 == 0, K <= 2048, at least as many K steps as LDS
+// stages, offsets inside 32 bits, the item table), and the launch
+// (hipErrorInvalidValue when it does not fit; nothing launched).
+int tiled_rows_u4_medium();
+bool routed_tiled_u4_fits(int mode, int tile_rows, int N, int K, int max_tiles, int n_act_rows, int n_pairs,
+                          bool outbf);
+hipError_t launch_gemm_routed_u4(int mode, bool outbf, int tile_rows, const GemmArgs& a, int max_tiles,
+                                 hipStream_t s);
 
 // routing (parameter blocks in moe_select.h)
 struct SelParams;
