@@ -320,8 +320,10 @@ __device__ void fused_select(const GemmArgs& a, int32_t* ids_l) {
 // MODE: kRoutedGateUp | kRoutedDown | kDenseGateUp | kDenseDown | kDenseStore | kSmallGateUp | kSmallDown
 //       | kDenseStoreNorm
 // WK: weight kind; OUTBF: output stored as bf16 (else fp32)
-// TF: 16-token fragments per tile; WN x WKS waves = 4 (rows x K split)
-template <int MODE, int WK, bool OUTBF, int TF, int WN, int WKS>
+// TF: 16-token fragments per tile; WN x WKS waves = 4 (rows x K split);
+// RF: 16-row weight fragments per wave (4-bit routed tiles: each token chunk
+// a wave loads is used against RF row fragments)
+template <int MODE, int WK, bool OUTBF, int TF, int WN, int WKS, int RF = 1>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     constexpr bool F32 = (WK == kWF32);
     constexpr bool SMALL = (MODE == kSmallGateUp || MODE == kSmallDown);
@@ -335,6 +337,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     constexpr int BM = 16 * TF;
     constexpr int NM = DUAL ? 2 : 1;
     static_assert(!SMALL || TF == 1, "small-T tiles are 16 rows");
+    static_assert(RF == 1 || (ROUTED && WK == kWU4 && TF == 1 && WKS == 1), "row fragments: 4-bit routed tiles");
 
     // ---- tile: expert (bank) e, rows [begin, begin + count) or explicit rows (small T)
     __shared__ int srows_all[4][16];
@@ -385,7 +388,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     // dense store may split K over blockIdx.z (partial sums to separate planes)
     const int ksub = STORE ? K / max(a.ksplit, 1) : K;
     const int kbase = STORE ? int(blockIdx.z) * ksub : 0;
-    const int wrow0 = blockIdx.y * (16 * WN) + 16 * wn;
+    // rows wrow0 + 16 f + (0..15), f < RF (N is a multiple of 16 RF when RF > 1)
+    const int wrow0 = blockIdx.y * (16 * WN * RF) + 16 * RF * wn;
     const bool rows_ok = wrow0 < N;
 
     // ---- token rows of this lane (one per 16-token fragment)
@@ -413,11 +417,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         xrow[j] = p;
     }
 
-    f32x4 acc[NM][TF];
+    f32x4 acc[NM][RF][TF];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int j = 0; j < TF; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int f = 0; f < RF; ++f)
+#pragma unroll
+            for (int j = 0; j < TF; ++j) acc[m][f][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // routed down: each token column's pair id (its store row and routing
     // weight) is requested before the K loop, so it arrives during it
@@ -436,12 +442,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     // extra round trip before the K loop cost more than it saved there.
     constexpr bool U4S = (WK == kWU4) && DUAL;
     constexpr bool PIPE = (WK == kWBF16) && TF == 1 && !NORM;  // double-buffered K trips (below)
-    constexpr int kU4Stride = kU4MaxGroups + 1;  // words per row (odd: no bank conflicts)
-    __shared__ uint32_t u4_sm[U4S ? NM * 16 * WN * kU4Stride : 1];
+    // (RF > 1: reductions up to 2048, so that the staging of 128 rows stays 33 KB)
+    constexpr int kU4Groups = RF > 1 ? kU4MaxGroups / 2 : kU4MaxGroups;
+    constexpr int kU4Stride = kU4Groups + 1;  // words per row (odd: no bank conflicts)
+    __shared__ uint32_t u4_sm[U4S ? NM * 16 * WN * RF * kU4Stride : 1];
     if constexpr (U4S) {
-        constexpr int ROWS = 16 * WN;
+        constexpr int ROWS = 16 * WN * RF;
         const int g0 = kbase / 64, ng = ksub / 64, gpr = K / 64;  // groups: first, count, per row
-        if (ng > kU4MaxGroups) return;  // the host rejects such sizes; never index past the staging
+        if (ng > kU4Groups) return;  // the host rejects such sizes; never index past the staging
         const int row_base = int(blockIdx.y) * ROWS;
         const bool vec = (gpr % 8) == 0 && (g0 % 8) == 0 && (ng % 8) == 0 &&
                          ((reinterpret_cast<uintptr_t>(s0) | reinterpret_cast<uintptr_t>(m0) |
@@ -471,9 +479,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         }
         __syncthreads();
     }
-    // this lane's staged word for chunk base kc, matrix m
-    auto u4_word = [&](int m, int kc) __attribute__((always_inline)) {
-        return u4_sm[(m * 16 * WN + 16 * wn + r) * kU4Stride + (kc - kbase + q * WTraits<WK>::KL) / 64];
+    // this lane's staged word for chunk base kc, matrix m, row fragment f
+    auto u4_word = [&](int m, int kc, int f) __attribute__((always_inline)) {
+        return u4_sm[(m * 16 * WN * RF + 16 * RF * wn + 16 * f + r) * kU4Stride +
+                     (kc - kbase + q * WTraits<WK>::KL) / 64];
     };
 
     // folded RMS norm (router logits from the attention residual): the first
@@ -519,7 +528,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                 else
                     load_w<WK>(wa, w0, s0, m0, wrow, K, kbeg + c * SPAN, q);
                 load_x_norm(xb, static_cast<const float*>(xrow[0]), a.norm_w, x_inv, kbeg + c * SPAN, q, x_dst);
-                mma_chunk<F32>(acc[0][0], wa, xb);
+                mma_chunk<F32>(acc[0][0][0], wa, xb);
             }
         }
     } else if (rows_ok) {
@@ -528,20 +537,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         // without this a wave waits a full memory round trip per chunk.
         // (Measured at decode shapes: 4 chunks per trip halves occupancy for
         // no gain; the launch is bandwidth bound either way.)
-        constexpr int U = 2;
+        // (RF > 1: one chunk per trip, the same weight bytes in flight)
+        constexpr int U = RF > 1 ? 1 : 2;
         auto trip = [&](int c0, auto u_c) __attribute__((always_inline)) {
             constexpr int UU = decltype(u_c)::value;
-            Frag<F32> wa[UU][NM];
+            Frag<F32> wa[UU][NM][RF];
             Frag<F32> xb[UU][TF];
 #pragma unroll
             for (int i = 0; i < UU; ++i) {
                 const int kc = kbeg + (c0 + i) * SPAN;
-                if constexpr (U4S) {
-                    load_w_u4_staged(wa[i][0], w0, wrow, K, kc, q, u4_word(0, kc));
-                    load_w_u4_staged(wa[i][1], w1, wrow, K, kc, q, u4_word(1, kc));
-                } else {
-                    load_w<WK>(wa[i][0], w0, s0, m0, wrow, K, kc, q);
-                    if constexpr (DUAL) load_w<WK>(wa[i][1], w1, s1, m1, wrow, K, kc, q);
+#pragma unroll
+                for (int f = 0; f < RF; ++f) {
+                    if constexpr (U4S) {
+                        load_w_u4_staged(wa[i][0][f], w0, wrow + 16 * f, K, kc, q, u4_word(0, kc, f));
+                        load_w_u4_staged(wa[i][1][f], w1, wrow + 16 * f, K, kc, q, u4_word(1, kc, f));
+                    } else {
+                        load_w<WK>(wa[i][0][f], w0, s0, m0, wrow + 16 * f, K, kc, q);
+                        if constexpr (DUAL) load_w<WK>(wa[i][1][f], w1, s1, m1, wrow + 16 * f, K, kc, q);
+                    }
                 }
 #pragma unroll
                 for (int j = 0; j < TF; ++j) load_x<WK>(xb[i][j], xrow[j], kc, q);
@@ -551,7 +564,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
                 for (int m = 0; m < NM; ++m)
 #pragma unroll
-                    for (int j = 0; j < TF; ++j) mma_chunk<F32>(acc[m][j], wa[i][m], xb[i][j]);
+                    for (int f = 0; f < RF; ++f)
+#pragma unroll
+                        for (int j = 0; j < TF; ++j) mma_chunk<F32>(acc[m][f][j], wa[i][m][f], xb[i][j]);
         };
         int c = 0;
         if constexpr (PIPE) {
@@ -582,7 +597,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
                     for (int m = 0; m < NM; ++m)
 #pragma unroll
-                        for (int j = 0; j < TF; ++j) mma_chunk<F32>(acc[m][j], wb[B][i][m], xc[B][i][j]);
+                        for (int j = 0; j < TF; ++j) mma_chunk<F32>(acc[m][0][j], wb[B][i][m], xc[B][i][j]);
             };
             constexpr std::integral_constant<int, 0> I0{};
             constexpr std::integral_constant<int, 1> I1{};
@@ -619,7 +634,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
                 for (int j = 0; j < TF; ++j)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dst[((m * TF + j) * 4 + i) * 64 + lane] = acc[m][j][i];
+                    for (int i = 0; i < 4; ++i) dst[((m * TF + j) * 4 + i) * 64 + lane] = acc[m][0][j][i];
         }
         __syncthreads();
         if (wk == 0) {
@@ -631,7 +646,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
                     for (int j = 0; j < TF; ++j)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[m][j][i] += src[((m * TF + j) * 4 + i) * 64 + lane];
+                        for (int i = 0; i < 4; ++i) acc[m][0][j][i] += src[((m * TF + j) * 4 + i) * 64 + lane];
             }
         }
     }
@@ -640,65 +655,76 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     // returns: the compiler allocates 4-bit gate/up launches 118 registers
     // this way instead of 152, one more wave per SIMD.)
     if (!rows_ok || wk != 0) return;
-    const int f0 = wrow0 + 4 * q;
 #pragma unroll
-    for (int j = 0; j < TF; ++j) {
-        const int i = j * 16 + r;
-        if (i >= count) continue;
-        float v[4];
-        size_t dest;
-        if constexpr (DUAL) {
+    for (int rf = 0; rf < RF; ++rf) {
+        const int f0 = wrow0 + 16 * rf + 4 * q;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float g = acc[0][j][t];
-                v[t] = g / (1.0f + __expf(-g)) * acc[1][j][t];
-            }
-            if constexpr (MODE == kSmallGateUp)
-                dest = shared_item ? size_t(a.n_pairs + srows[i]) : size_t(srows[i]);
-            else
+        for (int j = 0; j < TF; ++j) {
+            const int i = j * 16 + r;
+            if (i >= count) continue;
+            float v[4];
+            size_t dest;
+            if constexpr (DUAL) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float g = acc[0][rf][j][t];
+                    v[t] = g / (1.0f + __expf(-g)) * acc[1][rf][j][t];
+                }
+                if constexpr (MODE == kSmallGateUp)
+                    dest = shared_item ? size_t(a.n_pairs + srows[i]) : size_t(srows[i]);
+                else
+                    dest = size_t(begin + i);
+            } else if constexpr (MODE == kRoutedDown) {
+                const int pair = down_pair[j];
+                if (pair < 0 || pair >= a.n_pairs) continue;
+                const float s = a.row_scale[pair];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = s * acc[0][rf][j][t];
+                dest = size_t(pair);
+            } else if constexpr (MODE == kSmallDown) {
+                // slot rows per token: K routed (+ the shared expert in slot K)
+                const int id = srows[i];
+                const int spt = a.topk + (a.has_shared ? 1 : 0);
+                float s;
+                if (shared_item) {
+                    s = a.gate_logit ? sigmoidf_(a.gate_logit[id]) : 1.0f;
+                    dest = size_t(id) * spt + a.topk;
+                } else {
+                    s = a.row_scale[id];
+                    dest = size_t(id / a.topk) * spt + id % a.topk;
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = s * acc[0][rf][j][t];
+            } else if constexpr (MODE == kDenseDown) {
+                const float s = a.row_scale ? sigmoidf_(a.row_scale[begin + i]) : 1.0f;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = s * acc[0][rf][j][t];
                 dest = size_t(begin + i);
-        } else if constexpr (MODE == kRoutedDown) {
-            const int pair = down_pair[j];
-            if (pair < 0 || pair >= a.n_pairs) continue;
-            const float s = a.row_scale[pair];
+            } else {  // kDenseStore
 #pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = s * acc[0][j][t];
-            dest = size_t(pair);
-        } else if constexpr (MODE == kSmallDown) {
-            // slot rows per token: K routed (+ the shared expert in slot K)
-            const int id = srows[i];
-            const int spt = a.topk + (a.has_shared ? 1 : 0);
-            float s;
-            if (shared_item) {
-                s = a.gate_logit ? sigmoidf_(a.gate_logit[id]) : 1.0f;
-                dest = size_t(id) * spt + a.topk;
-            } else {
-                s = a.row_scale[id];
-                dest = size_t(id / a.topk) * spt + id % a.topk;
+                for (int t = 0; t < 4; ++t) v[t] = acc[0][rf][j][t];
+                dest = size_t(blockIdx.z) * a.n_rows + begin + i;
             }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = s * acc[0][j][t];
-        } else if constexpr (MODE == kDenseDown) {
-            const float s = a.row_scale ? sigmoidf_(a.row_scale[begin + i]) : 1.0f;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = s * acc[0][j][t];
-            dest = size_t(begin + i);
-        } else {  // kDenseStore
-#pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = acc[0][j][t];
-            dest = size_t(blockIdx.z) * a.n_rows + begin + i;
-        }
-        if constexpr (OUTBF) {
-            uint2 pk = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + dest * out_ld + f0) = pk;
-        } else {
-            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + dest * out_ld + f0) =
-                make_float4(v[0], v[1], v[2], v[3]);
+            if constexpr (OUTBF) {
+                uint2 pk = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + dest * out_ld + f0) = pk;
+            } else {
+                *reinterpret_cast<float4*>(static_cast<float*>(a.out) + dest * out_ld + f0) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            }
         }
     }
 }
 
 // --------------------------------------------------------------- launchers
+// 4-bit routed 16-token tiles: weight row fragments per wave.  The down
+// projection (reduction d_ff) loads as many token bytes as weight bytes per
+// row fragment; two fragments per wave halve that (Qwen3.6 4-bit, K = 4,
+// T = 512: layer 212.6 -> 198 us; four: no further change).  The gate/up
+// keeps one: two measured 2-3 us slower (a wave per SIMD fewer).
+constexpr int kU4RowFragsGateUp = 1;
+constexpr int kU4RowFragsDown = 2;
+
 // K the waves of a small-T workgroup split: both the routed and the shared
 // item must divide evenly, so take the smaller of the two reduction lengths'
 // common divisibility (they are both multiples of the chunk span).
@@ -732,6 +758,16 @@ static hipError_t launch_cfg(const GemmArgs& a, int grid_x, int tf, hipStream_t 
         // T = 512 layer 252 -> 220 us, bf16 T = 256 386 -> 357 us).  Fewer
         // items (T <= 4) keep the 16-row tiles below: 64-row ones would leave
         // ~1 workgroup per CU.
+        if constexpr (WK == kWU4 && (MODE == kRoutedGateUp || MODE == kRoutedDown)) {
+            constexpr int RF = MODE == kRoutedGateUp ? kU4RowFragsGateUp : kU4RowFragsDown;
+            if (RF > 1 && nrows % (64 * RF) == 0 && kwg <= 64 * kU4MaxGroups / 2) {
+                // 4-bit routed tiles: each wave 16 * RF weight rows, so a
+                // token chunk is loaded once per that many rows
+                dim3 g(grid_x, nrows / (64 * RF), ks);
+                gemm_kernel<MODE, WK, OUTBF, 1, 4, 1, RF><<<g, 256, 0, s>>>(a);
+                return hipGetLastError();
+            }
+        }
         dim3 g(grid_x, (nrows + 63) / 64, ks);
         gemm_kernel<MODE, WK, OUTBF, 1, 4, 1><<<g, 256, 0, s>>>(a);
     } else if (tf == 1 || SMALL) {
