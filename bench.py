@@ -234,10 +234,13 @@ def single_layer_ms(insts, reps=10, flush_bytes=0):
     return sorted(times)[len(times) // 2]
 
 
-def time_stage(insts, stage, reps):
+def time_stage(insts, stage, reps, repeats=5, spread=None):
     """Average duration of one stage launch (or of a sequence of stage
     launches, given a tuple), re-launched `reps` times in one captured graph
-    over the instances' real routing; HIP events on the replay stream."""
+    over the instances' real routing; HIP events on the replay stream.  The
+    graph is replayed `repeats` times after a warm-up replay and the median
+    replay is returned (a list passed as `spread` receives every replay's
+    per-launch time)."""
     L = len(insts)
     stages = stage if isinstance(stage, tuple) else (stage,)
     cap = torch.cuda.Stream()
@@ -249,12 +252,17 @@ def time_stage(insts, stage, reps):
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / reps
+    per = []
+    for _ in range(max(1, repeats)):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        per.append(start.elapsed_time(end) / reps)
+    if spread is not None:
+        spread.extend(per)
+    return float(np.median(per))
 
 
 def source_hash():
@@ -417,7 +425,8 @@ def run_workload(name, T, L, steps, warmup, stage_reps):
     t = ms / 1e3
     # the routed gate/up launch the layer runs (selection folded in where the
     # layer folds it), re-launched back to back over the instances' routing
-    stage_ms = time_stage(insts, moe.STAGE_GATE_UP, stage_reps)
+    stage_spread = []
+    stage_ms = time_stage(insts, moe.STAGE_GATE_UP, stage_reps, spread=stage_spread)
     gu_bytes = float(np.mean([gateup_bytes(spec, a) for a in n_act]))
     gu_flops = gateup_flops(spec)
     gu_t = stage_ms / 1e3
@@ -429,7 +438,7 @@ def run_workload(name, T, L, steps, warmup, stage_reps):
         "mfma_ceiling": t_mfma / max(t_hbm, t_mfma),
         "n_active_mean": mean_act, "layer_bytes": byts, "layer_flops": flops,
         "layer_hbm_frac": byts / t / (HBM_PEAK_GBS * 1e9), "layer_mfma_frac": flops / t / (BF16_PEAK_TFLOPS * 1e12),
-        "gateup_ms": stage_ms, "gateup_bytes": gu_bytes, "gateup_flops": gu_flops,
+        "gateup_ms": stage_ms, "gateup_spread_ms": stage_spread, "gateup_bytes": gu_bytes, "gateup_flops": gu_flops,
         "gateup_gbs": gu_bytes / gu_t / 1e9, "gateup_tflops": gu_flops / gu_t / 1e12,
     }
     log(f"{name} T={T}: {ms * 1e3:.1f} us/layer, {T / t:,.0f} tok/s, n_active {mean_act:.1f}, "
@@ -748,7 +757,9 @@ def main():
                      "frac": round(dec["gateup_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": gu_traffic, "launch_us": round(dec["gateup_ms"] * 1e3, 3),
                      "launch_us_measured_as": f"{args.stage_reps} re-launches of the layer's gate/up launch in a "
-                                              "captured graph over the instances' routing, HIP events on its stream",
+                                              "captured graph over the instances' routing, HIP events on its stream; "
+                                              f"median of {len(dec['gateup_spread_ms'])} replays",
+                     "launch_us_replays": [round(v * 1e3, 2) for v in dec["gateup_spread_ms"]],
                      "algorithmic_bytes": round(dec["gateup_bytes"])},
     }
     line["hbm_reference"] = hbm_reference()
