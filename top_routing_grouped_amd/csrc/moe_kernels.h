@@ -112,9 +112,22 @@ hipError_t launch_route_select_gate(const SelParams& P, const GateParams& G, int
 hipError_t launch_route_permute(const SelParams& P, int32_t* ids, float* weights, const PermParams& Q,
                                 hipStream_t s);
 hipError_t launch_gate_logit(const void* x, bool x_f32, const void* wvec, int T, int D, float* out, hipStream_t s);
+// Selection that also counts each block's pairs per expert: block c takes
+// route_chunk_tokens(family) tokens (16 waves: two tokens per wave in the
+// softmax family, one in the group family) and writes counts[c][e] (how
+// many of its tokens' slots chose expert e), the first pass of
+// launch_permute_from_counts.  E <= 256.
+constexpr int kCountWaves = 16;
+inline int route_chunk_tokens(int family) { return family == 0 ? 2 * kCountWaves : kCountWaves; }
+hipError_t launch_route_select_counts(const SelParams& P, const GateParams& G, int32_t* ids, float* weights,
+                                      int32_t* counts, hipStream_t s);
 
 // permute (tiles may be null)
 hipError_t launch_permute(const PermParams& P, hipStream_t s);
+// The permute from per-chunk expert counts (chunk c = pairs c*chunk_pairs ..,
+// counts [n_chunks][E] in P.chunk_base, as launch_route_select_counts writes
+// them): one launch; E <= 256, chunk_pairs <= 1024.
+hipError_t launch_permute_from_counts(const PermParams& P, int n_chunks, int chunk_pairs, hipStream_t s);
 int id_bits_for(int E);
 int max_tiles_for(int n_pairs, int E, int tile_rows);
 hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* active, const int32_t* n_active, int E,

@@ -171,6 +171,107 @@ hipError_t launch_permute(const PermParams& P, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The permute from per-chunk expert counts that an earlier launch wrote
+// (the routing launch of many tokens counts each workgroup's pairs): one
+// launch.  Block b takes R = 1024 / chunk_pairs consecutive chunks (one pair
+// per thread).  Every block sums all chunk counts itself (threads over
+// experts x slices of chunks, each thread's counts loaded in round trips of
+// 16), so it knows every expert's offset and how many of the expert's pairs
+// lie in chunks before its own; block 0 also writes the offsets, the active
+// list and the tile list.  The scatter ranks pairs as permute_scatter_kernel
+// does (stable: ascending pair id inside each expert).
+constexpr int kCountsMaxE = 256;
+
+__global__ __launch_bounds__(kPermThreads) void permute_from_counts_kernel(PermParams P, int n_chunks,
+                                                                           int chunk_pairs) {
+    __shared__ int sh[32];
+    __shared__ int part_all[kPermThreads];
+    __shared__ int part_before[kPermThreads];
+    __shared__ int base_l[kCountsMaxE];
+    __shared__ uint16_t wcnt[kPermWaves * kCountsMaxE];
+    constexpr int G = 16;
+    const int E = P.E, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int R = kPermThreads / chunk_pairs;
+    const int cb = blockIdx.x * R;  // first chunk of this block
+    const int S = kPermThreads / E;
+    const int e = tid % E, sl = tid / E;
+    const bool act = sl < S;
+    const int per = (n_chunks + S - 1) / S;
+    const int c0 = act ? min(n_chunks, sl * per) : n_chunks, c1 = min(n_chunks, c0 + per);
+    int all = 0, before = 0;
+    for (int c = c0; c < c1; c += G) {
+        int v[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) v[i] = P.chunk_base[size_t(min(c + i, n_chunks - 1)) * E + e];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int n = c + i < c1 ? v[i] : 0;
+            all += n;
+            before += c + i < cb ? n : 0;
+        }
+    }
+    part_all[tid] = act ? all : 0;
+    part_before[tid] = act ? before : 0;
+    for (int i = tid; i < kPermWaves * E; i += kPermThreads) wcnt[i] = 0;
+    __syncthreads();
+    int total = 0, bef = 0;
+    if (tid < E) {
+        for (int s = 0; s < S; ++s) {
+            total += part_all[s * E + tid];
+            bef += part_before[s * E + tid];
+        }
+    }
+    int n_all, n_act, n_tiles;
+    const int off = block_exclusive_scan(total, &n_all, sh);
+    const int apos = block_exclusive_scan(total > 0 ? 1 : 0, &n_act, sh);
+    const int nt = (total + P.tile_rows - 1) / P.tile_rows;
+    const int tpos = block_exclusive_scan(P.tiles ? nt : 0, &n_tiles, sh);
+    if (tid < E) {
+        base_l[tid] = off + bef;
+        if (blockIdx.x == 0) {
+            P.offsets[tid] = off;
+            if (total > 0) {
+                P.active[apos] = tid;
+                if (P.tiles) write_tiles(P.tiles, tpos, tid, off, total, P.tile_rows, P.max_tiles);
+            }
+        }
+    }
+    if (blockIdx.x == 0 && tid == 0) {
+        P.offsets[E] = n_all;
+        *P.n_active = n_act;
+        if (P.n_tiles) *P.n_tiles = min(n_tiles, P.max_tiles);
+    }
+    __syncthreads();
+    const int p = cb * chunk_pairs + tid;
+    int ex = (tid < R * chunk_pairs && p < P.n_pairs) ? P.ids[p] : -1;
+    const bool valid = ex >= 0 && ex < E;
+    if (!valid) ex = 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < P.id_bits; ++b) {
+        const bool bit = (ex >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        peers &= bit ? bb : ~bb;
+    }
+    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(peers & lt);
+    if (valid && rank == 0) wcnt[wave * E + ex] = uint16_t(__popcll(peers));
+    __syncthreads();
+    if (valid) {
+        int bw = 0;
+        for (int w = 0; w < wave; ++w) bw += wcnt[w * E + ex];
+        P.sorted_pairs[base_l[ex] + bw + rank] = p;
+    }
+}
+
+hipError_t launch_permute_from_counts(const PermParams& P, int n_chunks, int chunk_pairs, hipStream_t s) {
+    if (P.E <= 0 || P.E > kCountsMaxE || chunk_pairs <= 0 || chunk_pairs > kPermThreads || n_chunks <= 0 ||
+        !P.chunk_base)
+        return hipErrorInvalidValue;
+    const int R = kPermThreads / chunk_pairs;
+    permute_from_counts_kernel<<<(n_chunks + R - 1) / R, kPermThreads, 0, s>>>(P, n_chunks, chunk_pairs);
+    return hipGetLastError();
+}
+
 // Tile list from given permute outputs (used when the caller supplies them).
 __global__ __launch_bounds__(kPermThreads) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                                    const int32_t* __restrict__ active,

@@ -22,43 +22,56 @@
 
 namespace moe {
 
-// One wave per token, blocks of 4 tokens; or (softmax family, PAIR) one wave
-// per two tokens, blocks of 8, whose selection chains interleave.
+// One wave per token, blocks of NW tokens; or (softmax family, PAIR) one wave
+// per two tokens, blocks of 2 NW, whose selection chains interleave.
 // Optionally also the shared-expert gate logit w_shared . x_t of the token
-// (Treebeard, "Shared expert computation").
-template <int NV, bool PAIR>
-__global__ __launch_bounds__(256) void route_select_kernel(SelParams P, GateParams G, int32_t* __restrict__ ids,
-                                                           float* __restrict__ wts) {
-    __shared__ float sel_s[4][64 * NV];
-    __shared__ float sig_s[4][64 * NV];
+// (Treebeard, "Shared expert computation"), and with `counts` the block's
+// pair histogram: counts[block][e] = how many of the block's tokens' slots
+// chose expert e (E <= 64 NV).
+template <int NV, bool PAIR, int NW>
+__global__ __launch_bounds__(NW * 64) void route_select_kernel(SelParams P, GateParams G, int32_t* __restrict__ ids,
+                                                               float* __restrict__ wts, int32_t* __restrict__ counts) {
+    __shared__ float sel_s[NW][64 * NV];
+    __shared__ float sig_s[NW][64 * NV];
+    __shared__ int hist[64 * NV];
     constexpr int B = PAIR ? 2 : 1;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t0 = blockIdx.x * 4 * B + wave;
-    if (t0 >= P.T) return;  // no block-wide barrier below
-    int id[B];
-    float w[B];
-    int tt[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) tt[b] = min(t0 + 4 * b, P.T - 1);  // a clamped second token repeats the last
-    if (PAIR || P.family == 0) {
-        select_softmax_lanes<NV, B>(P, tt, id, w);
-    } else {
-        select_token<NV>(P, t0, sel_s[wave], sig_s[wave], &id[0], &w[0]);
+    const int t0 = blockIdx.x * NW * B + wave;
+    if (counts) {
+        for (int e = threadIdx.x; e < P.E; e += NW * 64) hist[e] = 0;
+        __syncthreads();
     }
+    if (t0 < P.T) {  // wave-uniform; no block-wide barrier inside
+        int id[B];
+        float w[B];
+        int tt[B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-        const int t = t0 + 4 * b;
-        if (t >= P.T) break;
-        float gl = 0.f;
-        if (G.w) gl = wave_dot_row(G.x, G.w, t, G.D, G.x_f32 != 0);
-        if (lane < P.K) {
-            const size_t o = size_t(t) * P.K + lane;
-            ids[o] = id[b];
-            wts[o] = w[b];
-            if (P.ids2) P.ids2[o] = id[b];
-            if (P.wts2) P.wts2[o] = w[b];
+        for (int b = 0; b < B; ++b) tt[b] = min(t0 + NW * b, P.T - 1);  // a clamped second token repeats the last
+        if (PAIR || P.family == 0) {
+            select_softmax_lanes<NV, B>(P, tt, id, w);
+        } else {
+            select_token<NV>(P, t0, sel_s[wave], sig_s[wave], &id[0], &w[0]);
         }
-        if (G.w && lane == 0) G.out[t] = gl;
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int t = t0 + NW * b;
+            if (t >= P.T) break;
+            float gl = 0.f;
+            if (G.w) gl = wave_dot_row(G.x, G.w, t, G.D, G.x_f32 != 0);
+            if (lane < P.K) {
+                const size_t o = size_t(t) * P.K + lane;
+                ids[o] = id[b];
+                wts[o] = w[b];
+                if (P.ids2) P.ids2[o] = id[b];
+                if (P.wts2) P.wts2[o] = w[b];
+                if (counts) atomicAdd(&hist[id[b]], 1);
+            }
+            if (G.w && lane == 0) G.out[t] = gl;
+        }
+    }
+    if (counts) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < P.E; e += NW * 64) counts[size_t(blockIdx.x) * P.E + e] = hist[e];
     }
 }
 
@@ -96,9 +109,35 @@ template <int NV>
 static void launch_nv(const SelParams& P, const GateParams& G, int32_t* ids, float* wts, hipStream_t s) {
     // many tokens, softmax family: two tokens per wave
     if (P.family == 0 && P.T >= 1024 && NV <= 8)
-        route_select_kernel<NV, true><<<(P.T + 7) / 8, 256, 0, s>>>(P, G, ids, wts);
+        route_select_kernel<NV, true, 4><<<(P.T + 7) / 8, 256, 0, s>>>(P, G, ids, wts, nullptr);
     else
-        route_select_kernel<NV, false><<<(P.T + 3) / 4, 256, 0, s>>>(P, G, ids, wts);
+        route_select_kernel<NV, false, 4><<<(P.T + 3) / 4, 256, 0, s>>>(P, G, ids, wts, nullptr);
+}
+
+// With counts: blocks of kCountWaves waves, so a block's pairs are a chunk
+// of the permute from counts.
+
+template <int NV>
+static void launch_nv_counts(const SelParams& P, const GateParams& G, int32_t* ids, float* wts, int32_t* counts,
+                             hipStream_t s) {
+    const int ct = route_chunk_tokens(P.family);
+    if (P.family == 0)
+        route_select_kernel<NV, true, kCountWaves><<<(P.T + ct - 1) / ct, 64 * kCountWaves, 0, s>>>(P, G, ids, wts,
+                                                                                                  counts);
+    else
+        route_select_kernel<NV, false, kCountWaves><<<(P.T + ct - 1) / ct, 64 * kCountWaves, 0, s>>>(P, G, ids,
+                                                                                                   wts, counts);
+}
+
+hipError_t launch_route_select_counts(const SelParams& P, const GateParams& G, int32_t* ids, float* weights,
+                                      int32_t* counts, hipStream_t s) {
+    if (P.T <= 0) return hipSuccess;
+    if (!counts || P.E > 256) return hipErrorInvalidValue;
+    const int nv = (P.E + 63) / 64;
+    if (nv <= 1) launch_nv_counts<1>(P, G, ids, weights, counts, s);
+    else if (nv <= 2) launch_nv_counts<2>(P, G, ids, weights, counts, s);
+    else launch_nv_counts<4>(P, G, ids, weights, counts, s);
+    return hipGetLastError();
 }
 
 hipError_t launch_route_select_gate(const SelParams& P, const GateParams& G, int32_t* ids, float* weights,
