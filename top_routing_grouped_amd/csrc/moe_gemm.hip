@@ -185,6 +185,44 @@ __device__ __forceinline__ void load_x_norm(Frag<false>& f, const float* rowp, c
     }
 }
 
+// bf16 chunks loaded quad-wise: a 16-byte load by every lane reads 64
+// contiguous bytes of one row per four consecutive lanes (lane l: row
+// (l / 4) mod 16, 16-byte piece l mod 4 of the 64), the order in which the
+// vector memory path takes a full request per lane quad.  The MFMA order
+// (lane 16 q + r: row r, piece q) is restored at use time by a fixed lane
+// permutation (quad_order).  Both operands of a chunk take it, so the
+// products are the same.
+__device__ __forceinline__ void load_w_quad(Frag<false>& f, const uint16_t* w_rows, int K, int kc) {
+    const int lane = threadIdx.x & 63;
+    const uint16_t* p = w_rows + size_t((lane >> 2) & 15) * K + kc + (lane & 3) * 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.v[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(p + 32 * j));
+}
+__device__ __forceinline__ void load_x_quad(Frag<false>& f, const uint16_t* rowp, int kc) {
+    const int lane = threadIdx.x & 63;
+    if (rowp) {
+        const uint16_t* p = rowp + kc + (lane & 3) * 8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f.v[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(p + 32 * j));
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f.v[j] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+}
+__device__ __forceinline__ void quad_order(Frag<false>& f) {
+    const int lane = threadIdx.x & 63;
+    const int src = (4 * (lane & 15) + (lane >> 4)) << 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        u32x4 v = __builtin_bit_cast(u32x4, f.v[j]);
+        v.x = __builtin_amdgcn_ds_bpermute(src, int(v.x));
+        v.y = __builtin_amdgcn_ds_bpermute(src, int(v.y));
+        v.z = __builtin_amdgcn_ds_bpermute(src, int(v.z));
+        v.w = __builtin_amdgcn_ds_bpermute(src, int(v.w));
+        f.v[j] = __builtin_bit_cast(bf16x8, v);
+    }
+}
+
 template <bool F32>
 __device__ __forceinline__ void mma_chunk(f32x4& acc, const Frag<F32>& a, const Frag<F32>& b) {
 #pragma unroll
@@ -579,19 +617,51 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
             // -> 144 us, one wave per SIMD fewer.)
             Frag<false> wb[2][U][NM];
             Frag<false> xc[2][U][TF];
+            // gate/up launches load quad-wise (Qwen3.6 decode layer: T = 32 235.7
+            // -> 222.1 us, T = 1 28.9 -> 27.7, T = 8 unchanged); the down
+            // projections keep the MFMA order (their short reductions gained
+            // nothing and lost to the permutes: routed down at T = 64 82.6 ->
+            // 93.3 us)
+            constexpr bool QUAD = DUAL;
+            // quad-wise loads: the 16 weight rows of the wave's fragment from
+            // their first row, the token row of lane (l / 4) mod 16
+            const uint16_t* wq0 = static_cast<const uint16_t*>(w0) + (wrow - r) * size_t(K);
+            const uint16_t* wq1 = DUAL ? static_cast<const uint16_t*>(w1) + (wrow - r) * size_t(K) : nullptr;
+            const uint16_t* xq = nullptr;
+            if constexpr (QUAD) {
+                const uint64_t xp = reinterpret_cast<uint64_t>(xrow[0]);
+                const int src = ((lane >> 2) & 15) << 2;
+                const uint32_t lo = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(uint32_t(xp))));
+                const uint32_t hi = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(uint32_t(xp >> 32))));
+                xq = reinterpret_cast<const uint16_t*>((uint64_t(hi) << 32) | lo);
+            }
             auto issue = [&](auto b_c, int t) __attribute__((always_inline)) {
                 constexpr int B = decltype(b_c)::value;
 #pragma unroll
                 for (int i = 0; i < U; ++i) {
                     const int kc = kbeg + (t * U + i) * SPAN;
-                    load_w<WK>(wb[B][i][0], w0, s0, m0, wrow, K, kc, q);
-                    if constexpr (DUAL) load_w<WK>(wb[B][i][1], w1, s1, m1, wrow, K, kc, q);
+                    if constexpr (QUAD) {
+                        load_w_quad(wb[B][i][0], wq0, K, kc);
+                        if constexpr (DUAL) load_w_quad(wb[B][i][1], wq1, K, kc);
+                        load_x_quad(xc[B][i][0], xq, kc);
+                    } else {
+                        load_w<WK>(wb[B][i][0], w0, s0, m0, wrow, K, kc, q);
+                        if constexpr (DUAL) load_w<WK>(wb[B][i][1], w1, s1, m1, wrow, K, kc, q);
 #pragma unroll
-                    for (int j = 0; j < TF; ++j) load_x<WK>(xc[B][i][j], xrow[j], kc, q);
+                        for (int j = 0; j < TF; ++j) load_x<WK>(xc[B][i][j], xrow[j], kc, q);
+                    }
                 }
             };
             auto mmas = [&](auto b_c, int) __attribute__((always_inline)) {
                 constexpr int B = decltype(b_c)::value;
+                if constexpr (QUAD) {
+#pragma unroll
+                    for (int i = 0; i < U; ++i) {
+#pragma unroll
+                        for (int m = 0; m < NM; ++m) quad_order(wb[B][i][m]);
+                        quad_order(xc[B][i][0]);
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < U; ++i)
 #pragma unroll
