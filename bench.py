@@ -386,11 +386,13 @@ def stream_ops(src, dst, out):
 
 
 def hbm_reference(nbytes=1 << 30, reps=10):
-    """The chip's streaming rate through plain library kernels, as a reference
-    for the roofline fractions: a device-to-device copy of `nbytes` (reads and
+    """The chip's streaming rate, as a reference for the roofline fractions:
+    through torch's kernels a device-to-device copy of `nbytes` (reads and
     writes nbytes) and a read-only pass (a sum over `nbytes` of fp32), each
-    over distinct buffers larger than the 256 MB last-level cache, HIP events
-    around `reps` launches."""
+    over distinct buffers larger than the 256 MB last-level cache; and the
+    library's streaming read (moe_stream_read) of the same buffer and of a
+    128 MiB slice of it read again (served by the last-level cache); HIP
+    events around the launches."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     out = torch.empty((), dtype=torch.float32, device="cuda")
@@ -405,7 +407,22 @@ def hbm_reference(nbytes=1 << 30, reps=10):
         e.record()
         torch.cuda.synchronize()
         res[f"{name}_GBps"] = round(moved * reps / (s.elapsed_time(e) / 1e3) / 1e9, 1)
-    del src, dst
+    # the library's own streaming read (whole 128-byte lines per request, eight
+    # 16-byte loads per lane in flight): from HBM over the 1 GiB buffer, and
+    # from the last-level cache over a 128 MiB slice read again
+    sink = torch.empty(nbytes // 1024, dtype=torch.int32, device="cuda")
+    llc = src[: (128 << 20) // 4]
+    for name, buf, n in (("stream_read", src, reps), ("llc_read", llc, 4 * reps)):
+        moe.stream_read(buf, sink)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(n):
+            moe.stream_read(buf, sink)
+        e.record()
+        torch.cuda.synchronize()
+        res[f"{name}_GBps"] = round(buf.numel() * 4 * n / (s.elapsed_time(e) / 1e3) / 1e9, 1)
+    res["llc_bytes"] = 128 << 20
+    del src, dst, sink, llc
     torch.cuda.empty_cache()
     res["bytes"] = nbytes
     return res

@@ -289,6 +289,19 @@ typedef enum {
 moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, const void* x, moe_stage stage,
                            void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* Measurement aid, not part of the layer: one streaming read of `bytes`
+ * bytes of device memory at `buf`, the reference rate for the layer's
+ * HBM-bound kernels (a buffer larger than the 256 MB last-level cache is
+ * read from HBM; a smaller one read again comes from that cache).  Each
+ * 64 KB block is read by one wave in 16-byte loads whose requests cover
+ * whole 128-byte lines; the XOR of the 16-byte words lane l of block b read
+ * (the four 32-bit halves folded into one word) is written to
+ * sink[64 b + l], so the reads cannot be elided.
+ * buf: device pointer, 16-byte aligned; bytes: a non-zero multiple of
+ * 262144; sink: device pointer to sink_words >= bytes / 1024 uint32 words.
+ * MOE_ERR_INVALID_ARGUMENT (nothing launched) otherwise. */
+moe_status moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, moe_stream_t stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 

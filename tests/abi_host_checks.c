@@ -148,6 +148,15 @@ int main(void) {
 
     /* ---- an unknown stage and status */
     CHECK(moe_layer_stage(&c, &w, fake, (moe_stage)99, ws, need, NULL), MOE_ERR_INVALID_ARGUMENT);
+    /* streaming read: NULL buffers, misalignment, sizes off the 256 KiB grid, a short sink */
+    uint32_t* sink = (uint32_t*)(((uintptr_t)1 << 20) + 64);
+    CHECK(moe_stream_read(NULL, 1 << 18, sink, 256, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_stream_read(fake, 1 << 18, NULL, 256, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_stream_read((const void*)(((uintptr_t)1 << 20) + 8), 1 << 18, sink, 256, NULL),
+          MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_stream_read(fake, 0, sink, 256, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_stream_read(fake, (1 << 18) + 1024, sink, 1 << 20, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_stream_read(fake, 1 << 18, sink, 255, NULL), MOE_ERR_INVALID_ARGUMENT);
     const int codes[] = {MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP,
                          99, -3};
     for (int i = 0; i < 7; ++i) {

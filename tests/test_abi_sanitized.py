@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PKG = os.path.join(ROOT, "top_routing_grouped_amd")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 KERNEL_OBJS = ["moe_gemm.hip", "moe_gemm_tiled.hip", "moe_route.hip", "moe_permute.hip", "moe_down_combine.hip",
-               "moe_norm.hip"]
+               "moe_norm.hip", "moe_stream.hip"]
 
 
 def _kernel_objects():

@@ -28,7 +28,7 @@ DEVICE = ["-x", "hip", f"--offload-arch={ARCH}",
           "-fno-gpu-flush-denormals-to-zero"]
 
 SOURCES = ["moe_gemm.hip", "moe_gemm_tiled.hip", "moe_route.hip", "moe_permute.hip", "moe_down_combine.hip",
-           "moe_norm.hip", "moe_api.cpp"]
+           "moe_norm.hip", "moe_stream.hip", "moe_api.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -928,6 +928,20 @@ moe_status moe_layer_forward_norm(const moe_config* cfg, const moe_weights* weig
     return layer_forward_impl(c, weights, x, residual, out, topk_ids_out, topk_weights_out, ws, stream, aux_stream);
 }
 
+moe_status moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, moe_stream_t stream) {
+    g_err[0] = 0;
+    if (!buf || !sink) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL buffer or sink");
+    if (reinterpret_cast<uintptr_t>(buf) % 16) return fail(MOE_ERR_INVALID_ARGUMENT, "buf must be 16-byte aligned");
+    if (bytes == 0 || bytes % (size_t(1) << 18))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "bytes (%zu) must be a non-zero multiple of 262144", bytes);
+    if (sink_words < moe::stream_read_sink_words(bytes))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "sink holds %zu words, %zu needed", sink_words,
+                    moe::stream_read_sink_words(bytes));
+    (void)hipGetLastError();
+    HIP_TRY(moe::launch_stream_read(buf, bytes, sink, stream));
+    return MOE_OK;
+}
+
 moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, const void* x, moe_stage stage,
                            void* ws, size_t ws_bytes, moe_stream_t stream) {
     g_err[0] = 0;

@@ -163,6 +163,11 @@ hipError_t launch_combine(const void* slots, bool slots_bf16, const float* share
                           float* out, int T, int K, int D, hipStream_t s);
 // small T: the slot rows hold K routed slots + the shared expert (K+1 per token)
 
+// Streaming read of `bytes` (a multiple of 256 KiB) at buf; one XOR word per
+// lane of each 64 KB block into sink (stream_read_sink_words(bytes) words).
+size_t stream_read_sink_words(size_t bytes);
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
+
 // x[t, :] = r[t, :] / sqrt(mean(r[t, :]^2) + eps) * w (w may be NULL: ones);
 // x bf16 (out_bf16) or fp32.  D % 4 == 0; r, w, x 16-byte aligned.
 hipError_t launch_rms_norm(const float* r, const float* w, float eps, int T, int D, void* x, bool out_bf16,
