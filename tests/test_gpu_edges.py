@@ -141,3 +141,32 @@ def test_layer_schedule_boundaries(dtype, T):
     z, rt = case.oracle_route()
     check_route(case, ids, wts, z, rt)
     check_layer(case, out, ids)
+
+
+# The permute that runs from the selection launch's per-block pair counts
+# (from 4096 pairs, E <= 256; blocks of 32 tokens in the softmax family, 16
+# in the group family): expert counts whose thread slices divide unevenly,
+# a last chunk of a few tokens, several chunks per permute block, and one
+# chunk per block (32 tokens x K = 32 = 1024 pairs).
+COUNTS_CASES = [
+    ("qwen_decode", 1030, dict(n_experts=16, top_k=4)),  # 33 chunks, the last of 6 tokens; 64 slices of experts
+    ("qwen_decode", 517, dict(n_experts=48, top_k=8, d_ff_shared=0)),  # 4 chunks per block, 5 blocks
+    ("qwen_decode", 130, dict(n_experts=256, top_k=32)),  # one chunk per block
+    ("sigmoid_group", 600, dict(n_experts=64, n_group=8, topk_group=4, top_k=8)),  # 16-token chunks
+    ("qwen_u4", 1100, dict(n_experts=80, top_k=4)),  # 4-bit experts on the same permute
+]
+
+
+@pytest.mark.parametrize("base,T,kw", COUNTS_CASES)
+def test_layer_permute_from_block_counts(base, T, kw):
+    dims = dict(SMALL_DIMS)
+    dims.update(kw)
+    spec = spec_of(base, n_tokens=T, **dims)
+    assert T * spec.top_k >= 4096 and spec.n_experts <= 256
+    case = make_case(spec, cache_key=("counts", base, T))
+    out, ids, wts = run_layer(case)
+    z, rt = case.oracle_route()
+    flagged, _ = check_route(case, ids, wts, z, rt)
+    err = check_layer(case, out, ids)
+    assert err <= TOL[spec.expert_dtype]
+    print(f"{base} T={T} {kw}: {flagged} near-tie tokens, y_moe normwise error {err:.2e}")
