@@ -51,25 +51,33 @@ __device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float acc)
 
 // 4-bit weights: piece j of lane s covers reduction elements 256 j + 32 s ..
 // +31 (16 bytes of codes, inside one group of 64); the same 32 h elements are
-// 4 loads of 16 bytes.  Each weight is dequantised to bf16 (w = scale * q +
-// min, rounded to nearest even, as in the MFMA path) and dotted with h in
-// pairs.
+// 4 loads of 16 bytes.  With w = scale * q + min (edge0, tier table: 4-bit
+// affine, group 64),
+//   sum_k w_k h_k = scale * sum_k (128 + q_k) h_k + (min - 128 scale) * sum_k h_k,
+// and 128 + q is a bf16 number whose bits are 0x4300 | q (exponent 2^7, the
+// code in the low mantissa bits), so a pair of codes becomes a bf16 pair with
+// one byte permute and one and-or, and both sums are v_dot2 over bf16 pairs:
+// no per-weight conversion, fma or rounding of w (about half the VALU work of
+// dequantising every weight to bf16 first).
 __device__ __forceinline__ float dot_u4_piece(const u32x4& c, float s, float m, const u32x4 (&h)[4], float acc) {
+    constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 pair (1, 1)
     const uint32_t words[4] = {c.x, c.y, c.z, c.w};
+    float pv = 0.f, ph = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        uint32_t even, odd;
-        nibble_bytes<kU4OpaqueReg>(words[i], even, odd);
+        const uint32_t w = words[i], w4 = w >> 4;
         const uint32_t h0 = h[i].x, h1 = h[i].y, h2 = h[i].z, h3 = h[i].w;
         const uint32_t hp[4] = {h0, h1, h2, h3};
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const uint32_t wp = pack_bf16x2(fmaf(s, float((even >> (8 * b)) & 0xffu), m),
-                                            fmaf(s, float((odd >> (8 * b)) & 0xffu), m));
-            acc = dot2(wp, hp[b], acc);
+            // byte b of w holds codes 2b (low nibble) and 2b+1 (high nibble):
+            // bytes 0 and 2 of the permute take byte b of w and of w >> 4
+            const uint32_t v = (__builtin_amdgcn_perm(w4, w, 0x0c040c00u + 0x00010001u * b) & 0x000f000fu) | 0x43004300u;
+            pv = dot2(v, hp[b], pv);
+            ph = dot2(kOnes, hp[b], ph);
         }
     }
-    return acc;
+    return fmaf(s, pv, fmaf(m - 128.f * s, ph, acc));
 }
 
 template <class F, int... I>
