@@ -422,7 +422,21 @@ def hbm_reference(nbytes=1 << 30, reps=10):
         torch.cuda.synchronize()
         res[f"{name}_GBps"] = round(buf.numel() * 4 * n / (s.elapsed_time(e) / 1e3) / 1e9, 1)
     res["llc_bytes"] = 128 << 20
-    del src, dst, sink, llc
+    # one launch per 256 MiB slice, the slices in turn (each read from HBM): a
+    # read of about the decode gate/up's bytes, its launch ramp and tail included
+    q = (256 << 20) // 4
+    slices = [src[i * q:(i + 1) * q] for i in range(src.numel() // q)]
+    if slices:
+        moe.stream_read(slices[-1], sink)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 4 * reps
+        s.record()
+        for i in range(n):
+            moe.stream_read(slices[i % len(slices)], sink)
+        e.record()
+        torch.cuda.synchronize()
+        res["stream_read_256MiB_GBps"] = round((256 << 20) * n / (s.elapsed_time(e) / 1e3) / 1e9, 1)
+    del src, dst, sink, llc, slices
     torch.cuda.empty_cache()
     res["bytes"] = nbytes
     return res
