@@ -30,6 +30,21 @@ namespace moe {
 
 constexpr float kClamp = 0x1p-14f;  // smallest normal fp16
 
+// Softmax-family routing weight of slot `lane` < K, whose logit z the lane
+// holds (slot 0 holds the largest logit m):
+//   alpha_k = p_k / max(sum_{j in I} p_j, 2^-14),  p = softmax(z) over all E.
+// The full softmax denominator cancels, and the floor cannot bind: the K
+// largest of E probabilities sum to at least K / E >= 2^-10 (the library
+// accepts E <= 1024).  So alpha_k is
+// exp(z_k - m) / sum_{j in I} exp(z_j - m): K exponentials, one wave sum,
+// no pass over all E experts.
+__device__ __forceinline__ float softmax_topk_weight(float z, int K) {
+    const int lane = threadIdx.x & 63;
+    const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), 0));
+    const float e = lane < K ? __expf(z - m) : 0.f;
+    return e / wave_sum_dpp(e);
+}
+
 // Orders LDS accesses of one wave (lanes of a wave exchange data through LDS).
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -123,15 +138,6 @@ __device__ __forceinline__ void select_from_logits(const SelParams& P, float (&v
     uint32_t taken = 0;
     int my_id = 0;
     if (P.family == 0) {
-        float m = v[0];
-#pragma unroll
-        for (int j = 1; j < NV; ++j) m = fmaxf(m, v[j]);
-        m = wave_max_dpp(m);
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < NV; ++j)
-            if (lane + 64 * j < E) s += __expf(v[j] - m);
-        s = wave_sum_dpp(s);
         float my_z = -INFINITY;
         for (int k = 0; k < K; ++k) {
             uint64_t best = 0;
@@ -151,10 +157,8 @@ __device__ __forceinline__ void select_from_logits(const SelParams& P, float (&v
                 my_z = key_score(best);
             }
         }
-        const float p = lane < K ? __expf(my_z - m) / s : 0.f;
-        const float denom = fmaxf(wave_sum_dpp(p), kClamp);
         *id_out = my_id;
-        *w_out = p / denom;
+        *w_out = softmax_topk_weight(my_z, K);
         return;
     }
     // sigmoid group top-k
@@ -267,21 +271,11 @@ __device__ __forceinline__ void select_softmax_lanes(const SelParams& P, const i
 #pragma unroll
             for (int j = 0; j < NV; ++j) v[b][j] = valid ? v[b][j] : 0.f;
     }
-    float m[B], ssum[B];
     uint32_t key[B][NV], taken[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-        float lm = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < NV; ++j) lm = valid ? fmaxf(lm, v[b][j]) : lm;
-        m[b] = wave_max_dpp(lm);
-        float ls = 0.f;
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            ls += valid ? __expf(v[b][j] - m[b]) : 0.f;
-            key[b][j] = valid ? orderable(v[b][j]) : 0u;  // any real score orders above 0
-        }
-        ssum[b] = wave_sum_dpp(ls);
+        for (int j = 0; j < NV; ++j) key[b][j] = valid ? orderable(v[b][j]) : 0u;  // any real score orders above 0
         taken[b] = 0;
     }
     int my_id[B];
@@ -319,10 +313,8 @@ __device__ __forceinline__ void select_softmax_lanes(const SelParams& P, const i
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-        const float p = lane < K ? __expf(from_orderable(my_key[b]) - m[b]) / ssum[b] : 0.f;
-        const float denom = fmaxf(wave_sum_dpp(p), kClamp);
         id[b] = my_id[b];
-        w[b] = p / denom;
+        w[b] = softmax_topk_weight(from_orderable(my_key[b]), K);
     }
 }
 
