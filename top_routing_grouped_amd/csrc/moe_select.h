@@ -271,40 +271,54 @@ __device__ __forceinline__ void select_softmax_lanes(const SelParams& P, const i
 #pragma unroll
             for (int j = 0; j < NV; ++j) v[b][j] = valid ? v[b][j] : 0.f;
     }
-    uint32_t key[B][NV], taken[B];
+    // each lane's keys sorted once, descending, by adjacent swaps on a
+    // strictly greater key (stable: equal keys keep the lower expert first);
+    // a round then offers the lane's head, and the winning lane shifts its
+    // list (no rescan of the lane's keys per round)
+    uint32_t sk[B][NV];
+    int sj[B][NV];
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
+    for (int b = 0; b < B; ++b)
 #pragma unroll
-        for (int j = 0; j < NV; ++j) key[b][j] = valid ? orderable(v[b][j]) : 0u;  // any real score orders above 0
-        taken[b] = 0;
-    }
+        for (int j = 0; j < NV; ++j) {
+            sk[b][j] = valid ? orderable(v[b][j]) : 0u;  // any real score orders above 0
+            sj[b][j] = j;
+        }
+#pragma unroll
+    for (int pass = 0; pass < NV - 1; ++pass)
+#pragma unroll
+        for (int i = 0; i < NV - 1 - pass; ++i)
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const bool sw = sk[b][i + 1] > sk[b][i];
+                const uint32_t ka = sk[b][i], kb = sk[b][i + 1];
+                const int ja = sj[b][i], jb = sj[b][i + 1];
+                sk[b][i] = sw ? kb : ka;
+                sk[b][i + 1] = sw ? ka : kb;
+                sj[b][i] = sw ? jb : ja;
+                sj[b][i + 1] = sw ? ja : jb;
+            }
     int my_id[B];
     uint32_t my_key[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) { my_id[b] = 0; my_key[b] = 0; }
     for (int k = 0; k < K; ++k) {
-        uint32_t best[B];
-        int bj[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            best[b] = 0;
-            bj[b] = 0;
-#pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                const bool ok = !((taken[b] >> j) & 1u) && key[b][j] > best[b];
-                best[b] = ok ? key[b][j] : best[b];
-                bj[b] = ok ? j : bj[b];
-            }
-        }
         uint32_t mx[B];
 #pragma unroll
-        for (int b = 0; b < B; ++b) mx[b] = wave_max_u32_dpp(best[b]);
+        for (int b = 0; b < B; ++b) mx[b] = wave_max_u32_dpp(sk[b][0]);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            const uint64_t ball = __ballot(best[b] == mx[b]);
+            const uint64_t ball = __ballot(sk[b][0] == mx[b]);
             const int wl = __ffsll((unsigned long long)ball) - 1;
-            const int wj = __builtin_amdgcn_readlane(bj[b], wl);
-            if (lane == wl) taken[b] |= 1u << wj;
+            const int wj = __builtin_amdgcn_readlane(sj[b][0], wl);
+            if (lane == wl) {
+#pragma unroll
+                for (int i = 0; i + 1 < NV; ++i) {
+                    sk[b][i] = sk[b][i + 1];
+                    sj[b][i] = sj[b][i + 1];
+                }
+                sk[b][NV - 1] = 0u;
+            }
             if (lane == k) {
                 my_id[b] = NV * wl + wj;
                 my_key[b] = mx[b];
