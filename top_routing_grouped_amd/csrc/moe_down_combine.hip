@@ -11,9 +11,10 @@
 // once from HBM) and sums a token's units (its K routed pairs in ascending
 // k, then the shared expert) in a fixed order: no slot buffer, no second
 // launch, no atomics.  With about one token per selected expert a unit is a
-// matrix-vector product, done with v_dot2 on the VALU: lane (r, s) holds
-// feature d0 + r and the 8-element K blocks s, s + 8, s + 16, ... of it, so a
-// 16-byte load instruction reads R whole 128-byte lines.  The waves split the
+// matrix-vector product, done with v_dot2 on the VALU: with L = 64 / R lanes
+// per feature, lane (r, s) holds feature d0 + r and the 8-element K blocks
+// s, s + L, s + 2L, ... of it (bf16), so a 16-byte load instruction reads
+// whole 128-byte lines (R = 8 or 4).  The waves split the
 // list of units evenly; a wave's partial sum for a token goes to LDS when the
 // token changes and the workgroup adds the waves' partials in wave order.
 // The loads of the next one or two units are in flight per wave while a unit
@@ -31,8 +32,14 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kDcR = 8;             // output features per workgroup
-constexpr int kDcLanes = 64 / kDcR;  // lanes per feature
+constexpr int kDcR = 8;  // output features per workgroup
+// bf16 banks with d_ff 512 and at least 64 units (8 per wave): 4 features per
+// workgroup, twice the workgroups, half the units walked by each wave in
+// turn (Qwen3.6 decode down + combine: T = 32 78.6 -> 77.2 us, T = 8 22.3
+// -> 21.8 us; T = 1, with 9 units, 5.4 -> 5.6 us, so it keeps 8; 4-bit
+// banks measured no faster with 4: T = 64 53.2 -> 55.3 us)
+constexpr int kDcR4 = 4;
+constexpr int kDcNarrowUnits = 64;
 constexpr int kDcWaves = 8;
 constexpr int kDcMaxT = 64;
 // Fourth word of a raw (stride 0, byte-addressed) buffer resource on gfx9:
@@ -90,16 +97,18 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// J: 16-byte weight loads per lane per unit (bf16: F = 64 J; U4: F = 256 J);
-// NB: units whose loads are in flight per wave
-template <int J, bool U4, int NB>
+// R: output features per workgroup, L = 64 / R lanes per feature; J: 16-byte
+// weight loads per lane per unit (bf16: F = 8 L J; U4: F = 32 L J); NB: units
+// whose loads are in flight per wave
+template <int J, bool U4, int NB, int R = kDcR>
 __global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombineArgs a) {
-    __shared__ float part[kDcWaves][kDcMaxT][kDcR];
+    constexpr int L = 64 / R;  // lanes per feature
+    __shared__ float part[kDcWaves][kDcMaxT][R];
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
-    const int r = lane / kDcLanes, s = lane % kDcLanes;
-    const int d0 = blockIdx.x * kDcR;
+    const int r = lane / L, s = lane % L;
+    const int d0 = blockIdx.x * R;
     const int T = a.T, K = a.K, S = a.has_shared ? 1 : 0, KS = K + S, TK = T * K;
-    for (int i = tid; i < kDcWaves * kDcMaxT * kDcR; i += kDcWaves * 64) (&part[0][0][0])[i] = 0.f;
+    for (int i = tid; i < kDcWaves * kDcMaxT * R; i += kDcWaves * 64) (&part[0][0][0])[i] = 0.f;
 
     // the wave's units ub .. ue-1 (at most 64): lane l holds unit ub + l's
     // expert (-1: the shared expert) and scale, read back with readlane
@@ -123,7 +132,7 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombine
     const uint16_t* wb = static_cast<const uint16_t*>(a.w);
     const uint16_t* wsb = static_cast<const uint16_t*>(a.ws);
     const uint16_t* hb = static_cast<const uint16_t*>(a.h);
-    const int F = U4 ? 256 * J : 64 * J;
+    const int F = U4 ? 32 * L * J : 8 * L * J;
 
     // unit u: token u / KS, slot u % KS (slot K: the shared expert).  Buffer
     // loads: the unit's row-slice and h row are scalar bases, a lane's byte
@@ -144,18 +153,18 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombine
         const uint16_t* srow = static_cast<const uint16_t*>(e >= 0 ? a.w_scale : a.ws_scale) + rowi * (F / 64);
         const uint16_t* mrow = static_cast<const uint16_t*>(e >= 0 ? a.w_min : a.ws_min) + rowi * (F / 64);
         const size_t hrow = k < K ? size_t(t) * K + k : size_t(TK) + t;
-        const auto rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(crow), 0, kDcR * F / 2, kRsrcWord3);
-        const auto rsc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(srow), 0, kDcR * F / 32, kRsrcWord3);
-        const auto rmn = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(mrow), 0, kDcR * F / 32, kRsrcWord3);
+        const auto rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(crow), 0, R * F / 2, kRsrcWord3);
+        const auto rsc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(srow), 0, R * F / 32, kRsrcWord3);
+        const auto rmn = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(mrow), 0, R * F / 32, kRsrcWord3);
         const auto rh = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(hb + hrow * a.h_ld), 0, F * 2, kRsrcWord3);
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            cr[j] = __builtin_amdgcn_raw_buffer_load_b128(rc, c_off + 128 * j, 0, 0);
-            const uint32_t sv = __builtin_amdgcn_raw_buffer_load_b16(rsc, g_off + 8 * j, 0, 0);
-            const uint32_t mv = __builtin_amdgcn_raw_buffer_load_b16(rmn, g_off + 8 * j, 0, 0);
+            cr[j] = __builtin_amdgcn_raw_buffer_load_b128(rc, c_off + 16 * L * j, 0, 0);
+            const uint32_t sv = __builtin_amdgcn_raw_buffer_load_b16(rsc, g_off + L * j, 0, 0);
+            const uint32_t mv = __builtin_amdgcn_raw_buffer_load_b16(rmn, g_off + L * j, 0, 0);
             sm[j] = sv | (mv << 16);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) hr[j][i] = __builtin_amdgcn_raw_buffer_load_b128(rh, hq_off + 512 * j + 16 * i, 0, 0);
+            for (int i = 0; i < 4; ++i) hr[j][i] = __builtin_amdgcn_raw_buffer_load_b128(rh, hq_off + 64 * L * j + 16 * i, 0, 0);
         }
     };
     auto load = [&](int u, u32x4 (&wr)[J], u32x4 (&hr)[J]) __attribute__((always_inline)) {
@@ -163,12 +172,12 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombine
         const int e = __builtin_amdgcn_readlane(u_e, u - ub);
         const uint16_t* wrow = e >= 0 ? wb + (size_t(e) * a.D + d0) * F : wsb + size_t(d0) * F;
         const size_t hrow = k < K ? size_t(t) * K + k : size_t(TK) + t;
-        const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wrow), 0, kDcR * F * 2, kRsrcWord3);
+        const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wrow), 0, R * F * 2, kRsrcWord3);
         const auto rh = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(hb + hrow * a.h_ld), 0, F * 2, kRsrcWord3);
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            wr[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off + 128 * j, 0, 0);
-            hr[j] = __builtin_amdgcn_raw_buffer_load_b128(rh, h_off + 128 * j, 0, 0);
+            wr[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off + 16 * L * j, 0, 0);
+            hr[j] = __builtin_amdgcn_raw_buffer_load_b128(rh, h_off + 16 * L * j, 0, 0);
         }
     };
     auto unit_scale = [&](int u) __attribute__((always_inline)) {
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombine
     auto flush = [&]() __attribute__((always_inline)) {
         float v = acc;
 #pragma unroll
-        for (int m = 1; m < kDcLanes; m <<= 1) v += __shfl_xor(v, m, 64);
+        for (int m = 1; m < L; m <<= 1) v += __shfl_xor(v, m, 64);
         if (s == 0) part[wave][cur_t][r] = v;
         acc = 0.f;
     };
@@ -254,8 +263,8 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_kernel(DownCombine
     __syncthreads();
 
     // waves' partials in wave order, then the residual
-    for (int i = tid; i < T * kDcR; i += kDcWaves * 64) {
-        const int t = i / kDcR, rr = i % kDcR;
+    for (int i = tid; i < T * R; i += kDcWaves * 64) {
+        const int t = i / R, rr = i % R;
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < kDcWaves; ++w) v += part[w][t][rr];
@@ -307,10 +316,14 @@ hipError_t launch_down_combine(const DownCombineArgs& a, hipStream_t s) {
         }
         return hipGetLastError();
     }
+    const int units = a.T * (a.K + (a.has_shared ? 1 : 0));
     switch (a.F / 64) {
         case 2: down_combine_kernel<2, false, 2><<<g, b, 0, s>>>(a); break;
         case 4: down_combine_kernel<4, false, 2><<<g, b, 0, s>>>(a); break;
-        case 8: down_combine_kernel<8, false, 2><<<g, b, 0, s>>>(a); break;
+        case 8:
+            if (units >= kDcNarrowUnits) down_combine_kernel<4, false, 2, kDcR4><<<dim3(unsigned(a.D / kDcR4)), b, 0, s>>>(a);
+            else down_combine_kernel<8, false, 2><<<g, b, 0, s>>>(a);
+            break;
         case 12: down_combine_kernel<12, false, 2><<<g, b, 0, s>>>(a); break;
         default: down_combine_kernel<16, false, 2><<<g, b, 0, s>>>(a); break;
     }
