@@ -72,6 +72,9 @@ struct GemmArgs {
     const float* norm_w;      // [K] or null (ones)
     float norm_eps;
     void* norm_x;             // [n_rows][K] bf16
+    // LDS-tiled dense modes: work items in token-tile-major order (row block
+    // fastest), so each XCD reads its own slice of the activation rows
+    int tile_major;
 };
 // Largest T for which the small-T gate/up launch does the selection itself.
 constexpr int kFusedSelMaxT = 8;
