@@ -215,14 +215,17 @@ def time_layer(insts, steps, warmup, protocol_chains=20):
 def single_layer_ms(insts, reps=10, flush_bytes=0):
     """Latency of one layer launched alone (its single-layer graph) after the
     GPU has drained: median over `reps` instances.  With flush_bytes, a buffer
-    of that size is written first (it evicts the last-level cache, leaves its
-    lines dirty, and replaces the TLB entries of the weights)."""
+    of that size (never written, so none of its lines is dirty) is read first:
+    it evicts the layer's data from the last-level cache and replaces the TLB
+    entries of the weights.  (A flush that writes the buffer leaves the cache
+    full of dirty lines, and the layer then pays for writing them back: 142
+    against 90 us at decode T = 8.)"""
     flush = torch.empty(max(flush_bytes, 4) // 4, dtype=torch.float32, device="cuda")
     times = []
     for i in range(reps):
         inst = insts[i % len(insts)]
         if flush_bytes:
-            flush.fill_(float(i))
+            flush.amax()
         torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
