@@ -389,7 +389,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         const int32_t* ids = a.ids;
         if constexpr (MODE == kSmallGateUp) {
             __shared__ int32_t ids_l[kFusedSelMaxT * 64];
-            if (a.fused_sel) {
+            // the shared expert's rows need no routing: of its workgroups only
+            // the first (which writes the routing outputs and gate logits)
+            // selects, and the others start streaming the shared weights
+            // while the routed workgroups select
+            const bool first = blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0;
+            if (a.fused_sel && (item >= 0 || first)) {
                 fused_select(a, ids_l);
                 ids = ids_l;
             }
