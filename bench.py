@@ -445,6 +445,34 @@ def hbm_reference(nbytes=1 << 30, reps=10):
     return res
 
 
+MFMA_SHAPES = ((0, "16x16x32_bf16", 2 * 16 * 16 * 32), (1, "32x32x16_bf16", 2 * 32 * 32 * 16))
+
+
+def mfma_reference(reps=5):
+    """The chip's bf16 MFMA issue rate, as a reference for the MFMA fractions:
+    the library's issue-rate loop (moe_mfma_rate: 8 independent accumulator
+    chains per wave, back-to-back MFMAs) for the 16x16x32 shape the grouped
+    GEMMs use and for 32x32x16, with one wave on each SIMD (256 workgroups of
+    4 waves) and two; about a millisecond per launch, HIP events around
+    `reps` launches after a warm-up one."""
+    res = {}
+    for shape, name, flops in MFMA_SHAPES:
+        iters = 20000 if shape == 0 else 10000
+        for wgs, label in ((256, "1_wave_per_simd"), (512, "2_waves_per_simd")):
+            sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+            moe.mfma_rate(shape, wgs, iters, sink)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                moe.mfma_rate(shape, wgs, iters, sink)
+            e.record()
+            torch.cuda.synchronize()
+            total = wgs * 4 * iters * 8 * flops * reps
+            res[f"mfma_{name}_{label}_TFLOPs"] = round(total / (s.elapsed_time(e) / 1e3) / 1e12, 1)
+    res["peak_TFLOPs"] = BF16_PEAK_TFLOPS
+    return res
+
+
 def run_workload(name, T, L, steps, warmup, stage_reps):
     spec = WORKLOADS[name].with_tokens(T)
     insts = build_instances(spec, L, f"{name} T={T}")
@@ -797,6 +825,7 @@ def main():
                      "algorithmic_bytes": round(dec["gateup_bytes"])},
     }
     line["hbm_reference"] = hbm_reference()
+    line["mfma_reference"] = mfma_reference()
     if not args.no_chain:
         line["chained_decode"] = chained_decode(args, dec["ms_per_step"] * 1e3)
     if not args.no_cpu_baseline:

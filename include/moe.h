@@ -302,6 +302,22 @@ moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, co
  * MOE_ERR_INVALID_ARGUMENT (nothing launched) otherwise. */
 moe_status moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, moe_stream_t stream);
 
+/* Measurement aid, not part of the layer: the bf16 MFMA issue rate of this
+ * chip, the reference for the MFMA-bound side of the grouped GEMMs.  Launches
+ * `workgroups` workgroups of 4 waves (256 of them put one wave on each SIMD
+ * of the 256 compute units, 512 two); every wave runs 8 independent
+ * accumulator chains of `iterations` back-to-back MFMAs of one shape
+ * (shape 0: v_mfma_f32_16x16x32_bf16, 2*16*16*32 flops; 1:
+ * v_mfma_f32_32x32x16_bf16, 2*32*32*16 flops) on operands equal to 1.0, and
+ * each lane writes the sum of its accumulators to sink[256 w + t] (w the
+ * workgroup, t the thread): iterations * 8 * 4 * 32 for shape 0 and
+ * iterations * 8 * 16 * 16 for shape 1.  The caller times the launch.
+ * shape: 0 or 1; workgroups: 1 .. 65536; iterations: 1 .. 2^20; sink: device
+ * pointer to sink_words >= 256 * workgroups floats.
+ * MOE_ERR_INVALID_ARGUMENT (nothing launched) otherwise. */
+moe_status moe_mfma_rate(int32_t shape, int32_t workgroups, int32_t iterations, float* sink, size_t sink_words,
+                         moe_stream_t stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 

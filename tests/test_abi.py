@@ -161,6 +161,22 @@ def test_rms_norm_argument_errors_without_launch():
                                     ws, 16, None, None) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_mfma_rate_argument_errors_without_launch():
+    """The MFMA issue-rate aid rejects shapes, sizes and sinks off its grid
+    before any launch (the sink pointer is never dereferenced)."""
+    L = moe.lib()
+    E = moe.MOE_ERR_INVALID_ARGUMENT
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.moe_mfma_rate(2, 1, 1, fake, 256, None) == E
+    assert L.moe_mfma_rate(-1, 1, 1, fake, 256, None) == E
+    assert L.moe_mfma_rate(0, 0, 1, fake, 256, None) == E
+    assert L.moe_mfma_rate(0, 65537, 1, fake, 65537 * 256, None) == E
+    assert L.moe_mfma_rate(1, 1, 0, fake, 256, None) == E
+    assert L.moe_mfma_rate(1, 1, (1 << 20) + 1, fake, 256, None) == E
+    assert L.moe_mfma_rate(0, 2, 1, fake, 511, None) == E
+    assert L.moe_mfma_rate(0, 1, 1, None, 256, None) == E
+
+
 def test_noalloc_entry_host_checks_without_launch():
     """The allocation-free layer entry rejects bad arguments and layers whose
     scratch need exceeds its 32 MiB array before any HIP call."""

@@ -1,6 +1,8 @@
-"""GPU test of moe_stream_read, the streaming-read measurement aid: the sink
-words are the XOR of what each lane read, checked against the same fold of
-the buffer on the host (every byte of the buffer read once, in place)."""
+"""GPU tests of the measurement aids.  moe_stream_read: the sink words are the
+XOR of what each lane read, checked against the same fold of the buffer on
+the host (every byte of the buffer read once, in place).  moe_mfma_rate: with
+every operand 1.0, each MFMA adds its reduction length to every accumulator
+element, so each lane's sum has a closed form (exact in fp32 at these sizes)."""
 import numpy as np
 import pytest
 import torch
@@ -29,3 +31,12 @@ def test_stream_read_rejects_sizes_off_the_grid():
     sink = torch.zeros(64, dtype=torch.int32, device="cuda")
     with pytest.raises(moe.MoeError):
         moe.stream_read(buf, sink)
+
+
+@pytest.mark.parametrize("shape,per_iter", [(0, 8 * 4 * 32), (1, 8 * 16 * 16)])
+@pytest.mark.parametrize("workgroups,iterations", [(1, 1), (3, 7), (512, 40)])
+def test_mfma_rate_sums_every_mfma(shape, per_iter, workgroups, iterations):
+    sink = torch.full((workgroups * 256,), -1.0, dtype=torch.float32, device="cuda")
+    moe.mfma_rate(shape, workgroups, iterations, sink)
+    torch.cuda.synchronize()
+    assert torch.all(sink == float(per_iter * iterations)).item()

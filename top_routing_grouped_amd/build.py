@@ -27,13 +27,19 @@ DEVICE = ["-x", "hip", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-flush-denormals-to-zero"]
 
+# Per-source device options.  The MFMA issue-rate loop keeps its accumulators
+# in ordinary VGPRs: with the default accumulator-register form the compiler
+# copies some 16x16 accumulators between register files on every iteration,
+# and the loop then times those copies instead of the matrix cores.
+EXTRA_DEVICE = {"moe_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 SOURCES = ["moe_gemm.hip", "moe_gemm_tiled.hip", "moe_route.hip", "moe_permute.hip", "moe_down_combine.hip",
            "moe_norm.hip", "moe_stream.hip", "moe_api.cpp"]
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *DEVICE, *EXTRA_DEVICE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

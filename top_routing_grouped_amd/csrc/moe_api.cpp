@@ -942,6 +942,22 @@ moe_status moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t
     return MOE_OK;
 }
 
+moe_status moe_mfma_rate(int32_t shape, int32_t workgroups, int32_t iterations, float* sink, size_t sink_words,
+                         moe_stream_t stream) {
+    g_err[0] = 0;
+    if (shape != 0 && shape != 1) return fail(MOE_ERR_INVALID_ARGUMENT, "shape %d is not 0 or 1", int(shape));
+    if (workgroups < 1 || workgroups > 65536)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "workgroups %d outside 1 .. 65536", int(workgroups));
+    if (iterations < 1 || iterations > (1 << 20))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "iterations %d outside 1 .. 2^20", int(iterations));
+    if (!sink) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL sink");
+    if (sink_words < size_t(workgroups) * 256)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "sink holds %zu floats, %zu needed", sink_words, size_t(workgroups) * 256);
+    (void)hipGetLastError();
+    HIP_TRY(moe::launch_mfma_rate(shape, workgroups, iterations, sink, stream));
+    return MOE_OK;
+}
+
 moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, const void* x, moe_stage stage,
                            void* ws, size_t ws_bytes, moe_stream_t stream) {
     g_err[0] = 0;

@@ -170,6 +170,11 @@ hipError_t launch_combine(const void* slots, bool slots_bf16, const float* share
 // lane of each 64 KB block into sink (stream_read_sink_words(bytes) words).
 size_t stream_read_sink_words(size_t bytes);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
+// MFMA issue-rate loop (shape 0: 16x16x32 bf16, 1: 32x32x16 bf16): workgroups
+// of 4 waves, `iterations` rounds of mfma_rate_chains() MFMAs per wave, one
+// float per lane into sink (workgroups * 256 floats).
+int mfma_rate_chains();
+hipError_t launch_mfma_rate(int shape, int workgroups, int iterations, float* sink, hipStream_t s);
 
 // x[t, :] = r[t, :] / sqrt(mean(r[t, :]^2) + eps) * w (w may be NULL: ones);
 // x bf16 (out_bf16) or fp32.  D % 4 == 0; r, w, x 16-byte aligned.

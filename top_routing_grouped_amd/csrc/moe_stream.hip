@@ -1,4 +1,6 @@
-// Streaming read of device memory, a measurement aid for the layer's
+// Measurement aids beside the layer.
+//
+// Streaming read of device memory, the reference for the layer's
 // HBM-bound kernels: the rate at which this chip delivers a plain read
 // stream (from HBM for a buffer larger than the 256 MB last-level cache,
 // from that cache for a smaller one read again), against which the
@@ -8,6 +10,7 @@
 // bytes at 16 l of each KB, so every request is whole 128-byte lines), eight
 // requests in flight per lane, and folds what it read with XOR into one
 // word per lane, which is stored so the loads cannot be elided.
+#include "moe_device.h"
 #include "moe_kernels.h"
 
 namespace moe {
@@ -39,6 +42,59 @@ hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hip
     const size_t waves = bytes / kBlock;
     if (waves == 0 || waves % 4) return hipErrorInvalidValue;
     stream_read_kernel<<<dim3(unsigned(waves / 4)), dim3(256), 0, s>>>(static_cast<const uint8_t*>(buf), sink);
+    return hipGetLastError();
+}
+
+// MFMA issue rate, the reference for the MFMA-bound side of the grouped
+// GEMMs: every wave runs kChains independent accumulator chains of the
+// layer's bf16 MFMA shapes back to back (16x16x32, as the kernels use, or
+// 32x32x16), with every operand element equal to `one` (1.0 from the host, a
+// kernel argument, so no chain can be folded at compile time).  Each lane
+// then stores the sum of its accumulator elements: iterations * kChains *
+// (elements per lane) * (reduction per MFMA) when one is 1.
+namespace {
+constexpr int kChains = 8;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+}  // namespace
+
+template <int SHAPE>
+__global__ __launch_bounds__(256) void mfma_rate_kernel(float one, int iterations, float* __restrict__ sink) {
+    const __bf16 v = __bf16(one);
+    const bf16x8 a = {v, v, v, v, v, v, v, v};
+    float total = 0.f;
+    if constexpr (SHAPE == 0) {
+        f32x4 acc[kChains];
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int it = 0; it < iterations; ++it)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, acc[c], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) total += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+    } else {
+        f32x16 acc[kChains];
+#pragma unroll
+        for (int c = 0; c < kChains; ++c)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+        for (int it = 0; it < iterations; ++it)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, acc[c], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < kChains; ++c)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) total += acc[c][e];
+    }
+    sink[size_t(blockIdx.x) * 256 + threadIdx.x] = total;
+}
+
+int mfma_rate_chains() { return kChains; }
+
+hipError_t launch_mfma_rate(int shape, int workgroups, int iterations, float* sink, hipStream_t s) {
+    if (shape == 0)
+        mfma_rate_kernel<0><<<dim3(unsigned(workgroups)), dim3(256), 0, s>>>(1.0f, iterations, sink);
+    else
+        mfma_rate_kernel<1><<<dim3(unsigned(workgroups)), dim3(256), 0, s>>>(1.0f, iterations, sink);
     return hipGetLastError();
 }
 

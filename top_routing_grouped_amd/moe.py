@@ -31,7 +31,7 @@ _FAM = {"softmax": SOFTMAX_TOPK, "sigmoid_group": SIGMOID_GROUP_TOPK}
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_experts", "moe_shared_expert",
            "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_layer_forward_direct",
            "moe_rms_norm", "moe_layer_forward_norm",
-           "moe_layer_stage", "moe_stream_read", "moe_status_string", "moe_last_error")
+           "moe_layer_stage", "moe_stream_read", "moe_mfma_rate", "moe_status_string", "moe_last_error")
 STAGE_ROUTER_LOGITS, STAGE_GATE_UP, STAGE_DOWN, STAGE_GATE_UP_DIRECT, STAGE_DOWN_GROUPED, STAGE_DOWN_DIRECT = range(6)
 
 
@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
             "moe_layer_forward_norm": [cfg, wts, P, ctypes.c_float, P, P, P, P, P, P, S, P, P],
             "moe_layer_stage": [cfg, wts, P, I32, P, S, P],
             "moe_stream_read": [P, S, P, S, P],
+            "moe_mfma_rate": [I32, I32, I32, P, S, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -222,6 +223,14 @@ def stream_read(buf, sink, stream=None):
     sink: a uint32 device tensor of at least buf.nbytes / 1024 elements)."""
     _check(lib().moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), sink.numel(),
                                  _stream(stream)), "moe_stream_read")
+
+
+def mfma_rate(shape: int, workgroups: int, iterations: int, sink, stream=None):
+    """One launch of the MFMA issue-rate loop (measurement aid; shape 0:
+    16x16x32 bf16, 1: 32x32x16 bf16; sink: a float32 device tensor of at
+    least 256 * workgroups elements)."""
+    _check(lib().moe_mfma_rate(shape, workgroups, iterations, _ptr(sink), sink.numel(), _stream(stream)),
+           "moe_mfma_rate")
 
 
 def layer_stage(cfg, wstruct: MoeWeights, x, stage: int, ws, stream=None):
