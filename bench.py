@@ -269,11 +269,18 @@ def time_stage(insts, stage, reps, repeats=5, spread=None):
 
 
 def source_hash():
+    """Hash of what the library's machine code is built from: the HIP and C++
+    sources, the public header and the build options."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "top_routing_grouped_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    pkg = os.path.join(ROOT, "top_routing_grouped_amd")
+    csrc = os.path.join(pkg, "csrc")
+    inc = os.path.join(ROOT, "include")
+    files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))]
+    files += [os.path.join(inc, f) for f in sorted(os.listdir(inc))]
+    files.append(os.path.join(pkg, "build.py"))
+    for p in files:
+        with open(p, "rb") as fh:
+            h.update(os.path.relpath(p, ROOT).encode() + fh.read())
     return h.hexdigest()[:16]
 
 
