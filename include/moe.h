@@ -312,7 +312,9 @@ moe_status moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t
  * each lane writes the sum of its accumulators to sink[256 w + t] (w the
  * workgroup, t the thread): iterations * 8 * 4 * 32 for shape 0 and
  * iterations * 8 * 16 * 16 for shape 1.  The caller times the launch.
- * shape: 0 or 1; workgroups: 1 .. 65536; iterations: 1 .. 2^20; sink: device
+ * Every partial sum is a multiple of 16 below 2^27, so the stated value is
+ * exact in fp32 for every allowed count.
+ * shape: 0 or 1; workgroups: 1 .. 65536; iterations: 1 .. 65536; sink: device
  * pointer to sink_words >= 256 * workgroups floats.
  * MOE_ERR_INVALID_ARGUMENT (nothing launched) otherwise. */
 moe_status moe_mfma_rate(int32_t shape, int32_t workgroups, int32_t iterations, float* sink, size_t sink_words,

@@ -172,7 +172,7 @@ def test_mfma_rate_argument_errors_without_launch():
     assert L.moe_mfma_rate(0, 0, 1, fake, 256, None) == E
     assert L.moe_mfma_rate(0, 65537, 1, fake, 65537 * 256, None) == E
     assert L.moe_mfma_rate(1, 1, 0, fake, 256, None) == E
-    assert L.moe_mfma_rate(1, 1, (1 << 20) + 1, fake, 256, None) == E
+    assert L.moe_mfma_rate(1, 1, (1 << 16) + 1, fake, 256, None) == E
     assert L.moe_mfma_rate(0, 2, 1, fake, 511, None) == E
     assert L.moe_mfma_rate(0, 1, 1, None, 256, None) == E
 

@@ -34,7 +34,7 @@ def test_stream_read_rejects_sizes_off_the_grid():
 
 
 @pytest.mark.parametrize("shape,per_iter", [(0, 8 * 4 * 32), (1, 8 * 16 * 16)])
-@pytest.mark.parametrize("workgroups,iterations", [(1, 1), (3, 7), (512, 40)])
+@pytest.mark.parametrize("workgroups,iterations", [(1, 1), (3, 7), (512, 40), (2, 65535), (1, 65536)])
 def test_mfma_rate_sums_every_mfma(shape, per_iter, workgroups, iterations):
     sink = torch.full((workgroups * 256,), -1.0, dtype=torch.float32, device="cuda")
     moe.mfma_rate(shape, workgroups, iterations, sink)

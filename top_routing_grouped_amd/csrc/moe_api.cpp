@@ -948,8 +948,10 @@ moe_status moe_mfma_rate(int32_t shape, int32_t workgroups, int32_t iterations, 
     if (shape != 0 && shape != 1) return fail(MOE_ERR_INVALID_ARGUMENT, "shape %d is not 0 or 1", int(shape));
     if (workgroups < 1 || workgroups > 65536)
         return fail(MOE_ERR_INVALID_ARGUMENT, "workgroups %d outside 1 .. 65536", int(workgroups));
-    if (iterations < 1 || iterations > (1 << 20))
-        return fail(MOE_ERR_INVALID_ARGUMENT, "iterations %d outside 1 .. 2^20", int(iterations));
+    // at most 2^16 rounds: every accumulator and partial sum of a lane stays
+    // an exact fp32 integer, so the sink holds the stated value
+    if (iterations < 1 || iterations > (1 << 16))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "iterations %d outside 1 .. 65536", int(iterations));
     if (!sink) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL sink");
     if (sink_words < size_t(workgroups) * 256)
         return fail(MOE_ERR_INVALID_ARGUMENT, "sink holds %zu floats, %zu needed", sink_words, size_t(workgroups) * 256);
