@@ -480,6 +480,38 @@ def mfma_reference(reps=5):
     return res
 
 
+L2_PATTERNS = ((0, "row_segments"), (1, "mfma_operand_order"), (2, "row_quads"))
+SHADER_CLOCK_GHZ = 2.4  # MI355X peak engine clock
+
+
+def l2_read_reference(reps=5, iterations=32):
+    """Vector-memory read rate from the L2 for the three lane-to-address
+    patterns of the library's L2 read loop (moe_l2_read_rate: 16-byte loads,
+    each wave 64 KB of 4 KB rows per pass, a 1 MiB set every XCD's L2 holds):
+    eight consecutive lanes per 128-byte line, the 16x16x32 MFMA operand
+    order, and four consecutive lanes per 64-byte segment; 4 and 16 waves per
+    compute unit (256 and 1024 workgroups).  Bytes per clock per compute unit
+    at the peak engine clock, HIP events around `reps` launches after a
+    warm-up one."""
+    buf = torch.zeros(1 << 18, dtype=torch.int32, device="cuda")
+    res = {}
+    for wgs, label in ((256, "4_waves_per_cu"), (1024, "16_waves_per_cu")):
+        sink = torch.empty(wgs * 256, dtype=torch.int32, device="cuda")
+        for pattern, name in L2_PATTERNS:
+            moe.l2_read_rate(pattern, wgs, iterations, buf, sink)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                moe.l2_read_rate(pattern, wgs, iterations, buf, sink)
+            e.record()
+            torch.cuda.synchronize()
+            nbytes = wgs * 4 * 65536 * iterations * reps
+            per_s = nbytes / (s.elapsed_time(e) / 1e3)
+            res[f"{name}_{label}_B_per_clk_per_CU"] = round(per_s / (SHADER_CLOCK_GHZ * 1e9 * 256), 1)
+    res["clock_GHz"] = SHADER_CLOCK_GHZ
+    return res
+
+
 def run_workload(name, T, L, steps, warmup, stage_reps):
     spec = WORKLOADS[name].with_tokens(T)
     insts = build_instances(spec, L, f"{name} T={T}")
@@ -833,6 +865,7 @@ def main():
     }
     line["hbm_reference"] = hbm_reference()
     line["mfma_reference"] = mfma_reference()
+    line["l2_read_reference"] = l2_read_reference()
     if not args.no_chain:
         line["chained_decode"] = chained_decode(args, dec["ms_per_step"] * 1e3)
     if not args.no_cpu_baseline:

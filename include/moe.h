@@ -320,6 +320,32 @@ moe_status moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t
 moe_status moe_mfma_rate(int32_t shape, int32_t workgroups, int32_t iterations, float* sink, size_t sink_words,
                          moe_stream_t stream);
 
+/* Measurement aid, not part of the layer: the vector-memory read rate from
+ * the L2 for three ways of mapping lanes to addresses, the reference for the
+ * load layouts of the register-streaming GEMMs.  Launches `workgroups`
+ * workgroups of 4 waves; every wave reads a 64 KB region laid out as 16 rows
+ * of 4096 bytes, `iterations` passes of 64 load instructions (16 bytes per
+ * lane each, issued in groups of eight):
+ *   pattern 0: instruction c reads bytes 1024 c .. 1024 c + 1023 of the
+ *     region, lane l the 16 at 1024 c + 16 l;
+ *   pattern 1: instruction c reads bytes 64 c .. 64 c + 63 of every row,
+ *     lane l row l % 16 at 64 c + 16 (l / 16) (the lane order of a 16x16x32
+ *     MFMA operand fragment);
+ *   pattern 2: the same bytes as pattern 1, lane l row l / 4 at
+ *     64 c + 16 (l % 4).
+ * Workgroup w's wave v reads region 4 ((w / 256) % 4) + v of buf (1 MiB: 16
+ * regions), starting each pass at chunk (8 w) % 64.  Each lane adds the
+ * 32-bit words it read, modulo 2^32, into sink[256 w + 64 v + l]:
+ * `iterations` times the sum of the words of its 64 chunks.  The caller
+ * times the launch; 1 MiB fits every XCD's L2 (4 MB), so after the first
+ * pass the loads are served from there.
+ * pattern: 0, 1 or 2; workgroups: 1 .. 65536; iterations: 1 .. 65536; buf:
+ * device pointer, 16-byte aligned, buf_bytes >= 1048576; sink: device
+ * pointer to sink_words >= 256 * workgroups uint32 words.
+ * MOE_ERR_INVALID_ARGUMENT (nothing launched) otherwise. */
+moe_status moe_l2_read_rate(int32_t pattern, int32_t workgroups, int32_t iterations, const void* buf,
+                            size_t buf_bytes, uint32_t* sink, size_t sink_words, moe_stream_t stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 

@@ -177,6 +177,26 @@ def test_mfma_rate_argument_errors_without_launch():
     assert L.moe_mfma_rate(0, 1, 1, None, 256, None) == E
 
 
+def test_l2_read_rate_argument_errors_without_launch():
+    """The L2 read-rate aid rejects patterns, sizes, buffers and sinks off its
+    grid before any launch (the pointers are never dereferenced)."""
+    L = moe.lib()
+    E = moe.MOE_ERR_INVALID_ARGUMENT
+    buf, sink = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 24)
+    MiB = 1 << 20
+    assert L.moe_l2_read_rate(3, 1, 1, buf, MiB, sink, 256, None) == E
+    assert L.moe_l2_read_rate(-1, 1, 1, buf, MiB, sink, 256, None) == E
+    assert L.moe_l2_read_rate(0, 0, 1, buf, MiB, sink, 256, None) == E
+    assert L.moe_l2_read_rate(0, 65537, 1, buf, MiB, sink, 65537 * 256, None) == E
+    assert L.moe_l2_read_rate(1, 1, 0, buf, MiB, sink, 256, None) == E
+    assert L.moe_l2_read_rate(1, 1, (1 << 16) + 1, buf, MiB, sink, 256, None) == E
+    assert L.moe_l2_read_rate(2, 1, 1, None, MiB, sink, 256, None) == E
+    assert L.moe_l2_read_rate(2, 1, 1, ctypes.c_void_p((1 << 20) + 8), MiB, sink, 256, None) == E
+    assert L.moe_l2_read_rate(0, 1, 1, buf, MiB - 16, sink, 256, None) == E
+    assert L.moe_l2_read_rate(0, 1, 1, buf, MiB, None, 256, None) == E
+    assert L.moe_l2_read_rate(0, 2, 1, buf, MiB, sink, 511, None) == E
+
+
 def test_noalloc_entry_host_checks_without_launch():
     """The allocation-free layer entry rejects bad arguments and layers whose
     scratch need exceeds its 32 MiB array before any HIP call."""

@@ -960,6 +960,26 @@ moe_status moe_mfma_rate(int32_t shape, int32_t workgroups, int32_t iterations, 
     return MOE_OK;
 }
 
+moe_status moe_l2_read_rate(int32_t pattern, int32_t workgroups, int32_t iterations, const void* buf,
+                            size_t buf_bytes, uint32_t* sink, size_t sink_words, moe_stream_t stream) {
+    g_err[0] = 0;
+    if (pattern < 0 || pattern > 2) return fail(MOE_ERR_INVALID_ARGUMENT, "pattern %d is not 0, 1 or 2", int(pattern));
+    if (workgroups < 1 || workgroups > 65536)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "workgroups %d outside 1 .. 65536", int(workgroups));
+    if (iterations < 1 || iterations > (1 << 16))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "iterations %d outside 1 .. 65536", int(iterations));
+    if (!buf || reinterpret_cast<uintptr_t>(buf) % 16)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "buf must be a 16-byte aligned device pointer");
+    if (buf_bytes < moe::l2_read_buffer_bytes())
+        return fail(MOE_ERR_INVALID_ARGUMENT, "buf holds %zu bytes, %zu needed", buf_bytes, moe::l2_read_buffer_bytes());
+    if (!sink) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL sink");
+    if (sink_words < size_t(workgroups) * 256)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "sink holds %zu words, %zu needed", sink_words, size_t(workgroups) * 256);
+    (void)hipGetLastError();
+    HIP_TRY(moe::launch_l2_read(pattern, workgroups, iterations, buf, sink, stream));
+    return MOE_OK;
+}
+
 moe_status moe_layer_stage(const moe_config* cfg, const moe_weights* weights, const void* x, moe_stage stage,
                            void* ws, size_t ws_bytes, moe_stream_t stream) {
     g_err[0] = 0;

@@ -175,6 +175,13 @@ hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hip
 // float per lane into sink (workgroups * 256 floats).
 int mfma_rate_chains();
 hipError_t launch_mfma_rate(int shape, int workgroups, int iterations, float* sink, hipStream_t s);
+// L2 read rate by lane pattern (0 row segments, 1 MFMA operand order, 2 row
+// quads): workgroups of 4 waves, each wave `iterations` passes over a 64 KB
+// region of a buffer of l2_read_buffer_bytes(); one word per lane into sink
+// (workgroups * 256 words).
+size_t l2_read_buffer_bytes();
+hipError_t launch_l2_read(int pattern, int workgroups, int iterations, const void* buf, uint32_t* sink,
+                          hipStream_t s);
 
 // x[t, :] = r[t, :] / sqrt(mean(r[t, :]^2) + eps) * w (w may be NULL: ones);
 // x bf16 (out_bf16) or fp32.  D % 4 == 0; r, w, x 16-byte aligned.

@@ -90,6 +90,69 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(float one, int iteration
 
 int mfma_rate_chains() { return kChains; }
 
+// Vector-memory read rate from the L2 by lane pattern, the reference for how a
+// kernel maps lanes to addresses.  Every wave reads a 64 KB region laid out
+// as 16 rows of 4 KB (the rows of a bf16 matrix with 2048 columns), 64 load
+// instructions of 16 bytes per lane per pass, issued in groups of eight:
+//   pattern 0, row segments: instruction c reads the 1 KB at 1024 c, lane l
+//     the 16 bytes at 16 l (eight consecutive lanes per 128-byte line);
+//   pattern 1, MFMA operand order: instruction c reads 64 bytes of each row,
+//     lane l row l mod 16 at byte 64 c + 16 (l / 16) (the lanes of one
+//     64-byte segment are 16 apart), the order in which a 16x16x32 operand
+//     fragment sits in the lanes;
+//   pattern 2, row quads: the same 16 x 64 bytes per instruction, lane l row
+//     l / 4 at byte 64 c + 16 (l mod 4) (four consecutive lanes per segment).
+// A workgroup's four waves read four regions of one 256 KB set, set
+// (workgroup / 256) mod 4 of a 1 MiB buffer: after the first pass every XCD's
+// L2 (4 MB) holds what its compute units read, which their 32 KB L1s cannot.
+// Each workgroup starts its passes at its own chunk (so the workgroups that
+// share a compute unit do not read the same lines in step), and each lane
+// adds the 32-bit words it read (mod 2^32) into the word it stores.
+namespace {
+constexpr int kL2Row = 4096;
+constexpr int kL2Region = 16 * kL2Row;  // bytes per wave
+constexpr int kL2Set = 4 * kL2Region;   // bytes per workgroup
+}  // namespace
+
+template <int PATTERN>
+__global__ __launch_bounds__(256) void l2_read_kernel(const uint8_t* __restrict__ buf, int iterations,
+                                                      uint32_t* __restrict__ sink) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const uint8_t* region = buf + size_t((blockIdx.x >> 8) & 3) * kL2Set + size_t(wv) * kL2Region;
+    uint32_t lane_off;
+    if constexpr (PATTERN == 0) lane_off = 16 * lane;
+    else if constexpr (PATTERN == 1) lane_off = (lane & 15) * kL2Row + 16 * (lane >> 4);
+    else lane_off = (lane >> 2) * kL2Row + 16 * (lane & 3);
+    constexpr uint32_t kStep = PATTERN == 0 ? 1024 : 64;
+    const int c0 = int(blockIdx.x * 8u) & 63;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int it = 0; it < iterations; ++it) {
+        uint32_t off = lane_off;
+        asm volatile("" : "+v"(off));  // a new pass: the loads cannot be hoisted out of it
+        for (int i = 0; i < 64; i += kInFlight) {
+            u32x4 v[kInFlight];
+#pragma unroll
+            for (int u = 0; u < kInFlight; ++u)
+                v[u] = *reinterpret_cast<const u32x4*>(region + off + kStep * uint32_t((c0 + i + u) & 63));
+#pragma unroll
+            for (int u = 0; u < kInFlight; ++u) acc += v[u];
+        }
+    }
+    sink[(size_t(blockIdx.x) * 4 + wv) * 64 + lane] = acc.x + acc.y + acc.z + acc.w;
+}
+
+size_t l2_read_buffer_bytes() { return size_t(4) * kL2Set; }
+
+hipError_t launch_l2_read(int pattern, int workgroups, int iterations, const void* buf, uint32_t* sink,
+                          hipStream_t s) {
+    const uint8_t* b = static_cast<const uint8_t*>(buf);
+    const dim3 g{unsigned(workgroups)}, t{256u};
+    if (pattern == 0) l2_read_kernel<0><<<g, t, 0, s>>>(b, iterations, sink);
+    else if (pattern == 1) l2_read_kernel<1><<<g, t, 0, s>>>(b, iterations, sink);
+    else l2_read_kernel<2><<<g, t, 0, s>>>(b, iterations, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_mfma_rate(int shape, int workgroups, int iterations, float* sink, hipStream_t s) {
     if (shape == 0)
         mfma_rate_kernel<0><<<dim3(unsigned(workgroups)), dim3(256), 0, s>>>(1.0f, iterations, sink);

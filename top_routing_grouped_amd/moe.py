@@ -31,7 +31,7 @@ _FAM = {"softmax": SOFTMAX_TOPK, "sigmoid_group": SIGMOID_GROUP_TOPK}
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_experts", "moe_shared_expert",
            "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_layer_forward_direct",
            "moe_rms_norm", "moe_layer_forward_norm",
-           "moe_layer_stage", "moe_stream_read", "moe_mfma_rate", "moe_status_string", "moe_last_error")
+           "moe_layer_stage", "moe_stream_read", "moe_mfma_rate", "moe_l2_read_rate", "moe_status_string", "moe_last_error")
 STAGE_ROUTER_LOGITS, STAGE_GATE_UP, STAGE_DOWN, STAGE_GATE_UP_DIRECT, STAGE_DOWN_GROUPED, STAGE_DOWN_DIRECT = range(6)
 
 
@@ -87,6 +87,7 @@ def lib() -> ctypes.CDLL:
             "moe_layer_stage": [cfg, wts, P, I32, P, S, P],
             "moe_stream_read": [P, S, P, S, P],
             "moe_mfma_rate": [I32, I32, I32, P, S, P],
+            "moe_l2_read_rate": [I32, I32, I32, P, S, P, S, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -231,6 +232,15 @@ def mfma_rate(shape: int, workgroups: int, iterations: int, sink, stream=None):
     least 256 * workgroups elements)."""
     _check(lib().moe_mfma_rate(shape, workgroups, iterations, _ptr(sink), sink.numel(), _stream(stream)),
            "moe_mfma_rate")
+
+
+def l2_read_rate(pattern: int, workgroups: int, iterations: int, buf, sink, stream=None):
+    """One launch of the L2 read-rate loop (measurement aid; pattern 0: row
+    segments, 1: MFMA operand order, 2: row quads; buf: a device tensor of at
+    least 1 MiB; sink: an int32 device tensor of at least 256 * workgroups
+    elements)."""
+    _check(lib().moe_l2_read_rate(pattern, workgroups, iterations, _ptr(buf), buf.numel() * buf.element_size(),
+                                  _ptr(sink), sink.numel(), _stream(stream)), "moe_l2_read_rate")
 
 
 def layer_stage(cfg, wstruct: MoeWeights, x, stage: int, ws, stream=None):
