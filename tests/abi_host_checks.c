@@ -157,6 +157,24 @@ int main(void) {
     CHECK(moe_stream_read(fake, 0, sink, 256, NULL), MOE_ERR_INVALID_ARGUMENT);
     CHECK(moe_stream_read(fake, (1 << 18) + 1024, sink, 1 << 20, NULL), MOE_ERR_INVALID_ARGUMENT);
     CHECK(moe_stream_read(fake, 1 << 18, sink, 255, NULL), MOE_ERR_INVALID_ARGUMENT);
+    /* MFMA issue-rate loop: shapes, counts and sinks off its grid */
+    float* fsink = (float*)(((uintptr_t)1 << 20) + 64);
+    CHECK(moe_mfma_rate(2, 1, 1, fsink, 256, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_mfma_rate(0, 0, 1, fsink, 256, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_mfma_rate(0, 1, 0, fsink, 256, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_mfma_rate(1, 1, (1 << 16) + 1, fsink, 256, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_mfma_rate(0, 2, 1, fsink, 511, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_mfma_rate(0, 1, 1, NULL, 256, NULL), MOE_ERR_INVALID_ARGUMENT);
+    /* L2 read-rate loop: patterns, counts, buffers and sinks off its grid */
+    CHECK(moe_l2_read_rate(3, 1, 1, fake, 1 << 20, sink, 256, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_l2_read_rate(0, 65537, 1, fake, 1 << 20, sink, (size_t)65537 * 256, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_l2_read_rate(1, 1, (1 << 16) + 1, fake, 1 << 20, sink, 256, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_l2_read_rate(2, 1, 1, NULL, 1 << 20, sink, 256, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_l2_read_rate(2, 1, 1, (const void*)(((uintptr_t)1 << 20) + 8), 1 << 20, sink, 256, NULL),
+          MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_l2_read_rate(0, 1, 1, fake, (1 << 20) - 16, sink, 256, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_l2_read_rate(0, 1, 1, fake, 1 << 20, NULL, 256, NULL), MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_l2_read_rate(0, 2, 1, fake, 1 << 20, sink, 511, NULL), MOE_ERR_INVALID_ARGUMENT);
     const int codes[] = {MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP,
                          99, -3};
     for (int i = 0; i < 7; ++i) {
